@@ -1,0 +1,220 @@
+"""The oracle: TEST INFRASTRUCTURE ONLY.
+
+A plain CPU statement of the single-GPU MoE FFN layer (moe_oracle.c), loaded
+through ctypes.  Only the tests, the smoke check and the CPU-baseline leg of the
+benchmark may import this package; the product path never does.  It shares no
+code with the HIP library.  Arrays in, arrays out (numpy); bf16 tensors are
+passed as their raw uint16 bit patterns.
+
+See moe_oracle.c for the pages and sections each function follows.
+"""
+import ctypes as C
+import os
+
+import numpy as np
+
+from . import build as _build
+
+SOFTMAX, SIGMOID, SQRTSOFTPLUS = 0, 1, 2
+LEARNED, HASH = 0, 1
+F32, BF16 = 0, 1
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = _build.LIB
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+            _build.build()
+        L = C.CDLL(path)
+        P, I, F = C.c_void_p, C.c_int, C.c_float
+        L.oracle_affinity.argtypes = [F, I]
+        L.oracle_affinity.restype = F
+        L.oracle_route.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P]
+        L.oracle_hash_route.argtypes = [I, I, I, I, P, P, P, I, P, P]
+        L.oracle_permute.argtypes = [I, I, I, P, P, P, P, P, P, P]
+        L.oracle_combine.argtypes = [I, I, P, P, P, P]
+        L.oracle_combine.restype = None
+        L.oracle_expert_ffn.argtypes = [I, I, P, P, P, I, P]
+        L.oracle_expert_ffn.restype = None
+        L.oracle_logits.argtypes = [I, P, I, I, P, P, I, P, P]
+        L.oracle_logits.restype = None
+        L.oracle_layer.argtypes = [I, P, I, I, I, I, I, I, I, I, I, I, I,
+                                   P, P, P, P, P, P, I, P, P, P, P, P, P, P, P]
+        L.oracle_num_threads.argtypes = []
+        for name in ("oracle_route", "oracle_hash_route", "oracle_permute",
+                     "oracle_layer", "oracle_num_threads"):
+            getattr(L, name).restype = I
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _tensor(a):
+    """float32 array -> (array, F32); uint16 (bf16 bits) -> (array, BF16)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a, F32
+    if a.dtype == np.uint16:
+        return a, BF16
+    raise TypeError("oracle tensors are float32 or uint16 bf16 bit patterns, got %s" % a.dtype)
+
+
+def affinity(l, scoring):
+    """Affinity of one float logit (float arithmetic, C library exp/log1p/sqrt)."""
+    return lib().oracle_affinity(float(l), int(scoring))
+
+
+def route(logits, k, scoring, bias=None, n_group=1, topk_group=1, group_topk=0):
+    """Learned routing from given float logits [T, E] -> (ids [T,k] int32,
+    gates [T,k] float32, margin [T] float32)."""
+    lg = _c(logits, np.float32)
+    T, E = lg.shape
+    ids = np.zeros((T, k), np.int32)
+    gates = np.zeros((T, k), np.float32)
+    margin = np.zeros(T, np.float32)
+    b = None if bias is None else _c(bias, np.float32)
+    rc = lib().oracle_route(T, E, k, scoring, n_group, topk_group, group_topk,
+                            _p(lg), _p(b), _p(ids), _p(gates), _p(margin))
+    if rc:
+        raise ValueError("oracle_route rejected its arguments")
+    return ids, gates, margin
+
+
+def hash_route(logits, token_ids, tid2eid, scoring):
+    lg = _c(logits, np.float32)
+    T, E = lg.shape
+    tab = _c(tid2eid, np.int32)
+    vocab, k = tab.shape
+    tok = _c(token_ids, np.int32)
+    ids = np.zeros((T, k), np.int32)
+    gates = np.zeros((T, k), np.float32)
+    rc = lib().oracle_hash_route(T, E, k, scoring, _p(lg), _p(tok), _p(tab), vocab,
+                                 _p(ids), _p(gates))
+    if rc:
+        raise ValueError("oracle_hash_route rejected its arguments")
+    return ids, gates
+
+
+def permute(ids, gates, E):
+    """Expert-major dispatch -> dict(counts, offsets, sorted_token_ids,
+    sorted_weights, dispatch_index)."""
+    ids = _c(ids, np.int32)
+    gates = _c(gates, np.float32)
+    T, k = ids.shape
+    out = dict(counts=np.zeros(E, np.int32), offsets=np.zeros(E + 1, np.int32),
+               sorted_token_ids=np.zeros(T * k, np.int32),
+               sorted_weights=np.zeros(T * k, np.float32),
+               dispatch_index=np.zeros((T, k), np.int32))
+    rc = lib().oracle_permute(T, k, E, _p(ids), _p(gates), _p(out["counts"]),
+                              _p(out["offsets"]), _p(out["sorted_token_ids"]),
+                              _p(out["sorted_weights"]), _p(out["dispatch_index"]))
+    if rc:
+        raise ValueError("oracle_permute: an id lies outside [0, E)")
+    return out
+
+
+def combine(expert_out, token_of_row, weight_of_row, T, out=None):
+    """index_add_-style combine of dispatch rows into T output rows (double)."""
+    eo = _c(expert_out, np.float64)
+    P, d = eo.shape
+    tok = _c(token_of_row, np.int32)
+    w = _c(weight_of_row, np.float32)
+    o = np.zeros((T, d), np.float64) if out is None else _c(out, np.float64).copy()
+    lib().oracle_combine(P, d, _p(eo), _p(tok), _p(w), _p(o))
+    return o
+
+
+def expert_ffn(x, w13_e, w2_e):
+    """One SwiGLU expert on one row x [d] (double result)."""
+    w13_e, dt = _tensor(w13_e)
+    w2_e, dt2 = _tensor(w2_e)
+    assert dt == dt2
+    d_ff2, d = w13_e.shape
+    xx = _c(x, np.float64)
+    y = np.zeros(d, np.float64)
+    lib().oracle_expert_ffn(d, d_ff2 // 2, _p(xx), _p(w13_e), _p(w2_e), dt, _p(y))
+    return y
+
+
+def logits(hidden, w_router, rows=None, logit_offset=None):
+    h, dt = _tensor(hidden)
+    w, dt2 = _tensor(w_router)
+    assert dt == dt2
+    T, d = h.shape
+    E = w.shape[0]
+    r = np.arange(T, dtype=np.int32) if rows is None else _c(rows, np.int32)
+    out = np.zeros((len(r), E), np.float64)
+    off = None if logit_offset is None else _c(logit_offset, np.float32)
+    lib().oracle_logits(len(r), _p(r), d, E, _p(h), _p(w), dt, _p(off), _p(out))
+    return out
+
+
+def layer(hidden, w_router, w13, w2, k, scoring, rows=None, bias=None,
+          logit_offset=None, n_group=1, topk_group=1, group_topk=0,
+          w13_shared=None, w2_shared=None, route_mode=LEARNED, token_ids=None,
+          tid2eid=None):
+    """The whole layer for the listed token rows.
+
+    w13 / w2 are either stacked arrays [E, ...] or sequences of per-expert arrays
+    (None for experts no listed token selects).  Returns dict(out [n, d] double,
+    ids [n, k], gates [n, k], margin [n])."""
+    h, dt = _tensor(hidden)
+    wr, _ = _tensor(w_router)
+    T, d = h.shape
+    E = wr.shape[0]
+    keep = []
+
+    def ptrs(ws):
+        arr = (C.c_void_p * E)()
+        for e in range(E):
+            w = ws[e]
+            if w is None:
+                arr[e] = None
+            else:
+                w, dte = _tensor(w)
+                assert dte == dt
+                keep.append(w)
+                arr[e] = w.ctypes.data
+        return arr
+
+    p13, p2 = ptrs(w13), ptrs(w2)
+    first = next(w for w in w13 if w is not None)
+    d_ff = np.asarray(first).shape[0] // 2
+    n_shared = 0 if w13_shared is None else 1
+    s13 = s2 = None
+    if n_shared:
+        s13, _ = _tensor(w13_shared)
+        s2, _ = _tensor(w2_shared)
+    r = np.arange(T, dtype=np.int32) if rows is None else _c(rows, np.int32)
+    n = len(r)
+    out = np.zeros((n, d), np.float64)
+    ids = np.zeros((n, k), np.int32)
+    gates = np.zeros((n, k), np.float32)
+    margin = np.zeros(n, np.float32)
+    b = None if bias is None else _c(bias, np.float32)
+    off = None if logit_offset is None else _c(logit_offset, np.float32)
+    tok = None if token_ids is None else _c(token_ids, np.int32)
+    tab = None if tid2eid is None else _c(tid2eid, np.int32)
+    vocab = 0 if tab is None else tab.shape[0]
+    rc = lib().oracle_layer(n, _p(r), d, E, k, d_ff, n_shared, dt, scoring, route_mode,
+                            n_group, topk_group, group_topk, _p(h), _p(wr), _p(b), _p(off),
+                            _p(tok), _p(tab), vocab,
+                            C.cast(p13, C.c_void_p), C.cast(p2, C.c_void_p),
+                            _p(s13), _p(s2), _p(out), _p(ids), _p(gates), _p(margin))
+    if rc:
+        raise ValueError("oracle_layer rejected its arguments (missing expert weights?)")
+    return dict(out=out, ids=ids, gates=gates, margin=margin)
+
+
+def num_threads():
+    return lib().oracle_num_threads()

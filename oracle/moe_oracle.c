@@ -1,0 +1,444 @@
+/*
+ * moe_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow CPU statement of the single-GPU Mixture-of-Experts FFN layer.
+ * Only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark load this library.  The product path never links, imports or calls
+ * it, and it shares no code, header, table or helper with the HIP library.
+ *
+ * Sources (web pages, by title and section):
+ *  [P1] "DeepSeek-V4 MoE: Token 从路由到专家计算，再回到原位置" (akiyangdev llm-inference-notes),
+ *       sections 二 (Router, TopK, HashTopK) and 四 (Dispatch, expert FFN, Combine).
+ *  [P2] "MoE 架构与路由策略" (t6page DeepSeek-V4 notes), equation dsv4-moe-softplus,
+ *       the aux-loss-free section, the V3 node-limited routing section and the
+ *       hash routing section.
+ *  [P3] "MoE 的算量与通信" (arganzheng, moe-compute-and-communication), chapter 二.1-二.3
+ *       (SwiGLU FFN, router, top-k renormalisation, weighted sum plus shared experts),
+ *       chapter 五.3 (group choice by the sum of each group's top Kr/M scores),
+ *       chapter 七.3 (bias used for selection only).
+ *  [P4] "Mixture of Experts: Router, Token Dispatch, Grouped GEMM" (111qqz), sections
+ *       Router (worked example), Expert (SwiGLU), Token Dispatch, Token Combine.
+ *
+ * Precision.
+ *  - Expert FFNs, logits and the combine are evaluated in double precision from
+ *    the inputs as given (bf16 -> double is exact).
+ *  - Routing decisions (which experts a token selects) are taken in float, the
+ *    precision the GPU kernels decide in: logits are rounded to float, affinities
+ *    come from the C library's expf/log1pf/sqrtf, and the selection key is the
+ *    float sum score + bias.  Gates are then formed in double from those floats.
+ *
+ * Readings where the pages are silent (each is also listed in the design notes):
+ *  - w13 rows [0, d_ff) are the gate projection W1 (the SiLU input), rows
+ *    [d_ff, 2 d_ff) the up projection W3; weights are stored [out, in].
+ *  - top-k order: descending key, equal keys go to the lower expert index; the
+ *    same rule orders groups.
+ *  - softmax routing selects on the raw logits and forms the gates as a softmax
+ *    over the selected logits (equal to softmax over all experts followed by
+ *    renormalisation over the selected ones).
+ *  - sigmoid / sqrt(softplus): gates are the unbiased scores of the selected
+ *    experts divided by their sum; if that sum is 0 every gate is 1/k.
+ *  - the group stage scores a group by the float sum, in descending order, of its
+ *    top `group_topk` biased keys.
+ *  - hash routing takes the ids from tid2eid in stored order; its gates are the
+ *    affinities of the token's logits at those ids, renormalised (bias unused).
+ *  - shared experts are added with weight 1; no routed scaling factor.
+ *
+ * Pins: the tests check this file against the pages' worked examples (router
+ * example, two-token toy, dispatch/combine toy, EP4 per-expert counts), closed
+ * forms of the affinities, invariants of routing and permutation, a dense SwiGLU
+ * FFN for E = 1, k = 1, and a dense masked evaluation of every expert on tiny
+ * inputs.  The group stage has no printed example: it is pinned only by its
+ * invariants and by an independent array formulation in the tests.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_SOFTMAX 0
+#define ORACLE_SIGMOID 1
+#define ORACLE_SQRTSOFTPLUS 2
+
+/* element i of a tensor stored as float (dtype 0) or bfloat16 (dtype 1) */
+static double elem(const void *p, size_t i, int dtype)
+{
+    if (dtype == 0)
+        return (double)((const float *)p)[i];
+    uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* ---------------------------------------------------------------------------
+ * Affinity functions, in float.  [P2] equation dsv4-moe-softplus gives
+ * Sigmoid(x) = 1 / (1 + e^-x) and sqrt(Softplus(x)) = sqrt(ln(1 + e^x));
+ * ln(1 + e^x) is evaluated as max(x, 0) + log1p(e^-|x|), which is the same
+ * number without overflow for large x.
+ * ------------------------------------------------------------------------- */
+float oracle_affinity(float l, int scoring)
+{
+    if (scoring == ORACLE_SIGMOID)
+        return 1.0f / (1.0f + expf(-l));
+    if (scoring == ORACLE_SQRTSOFTPLUS)
+        return sqrtf(fmaxf(l, 0.0f) + log1pf(expf(-fabsf(l))));
+    return l; /* softmax: selection is on the logit itself */
+}
+
+/* index of the best candidate (largest key, lowest index on equal keys) among
+   those with ok[i] != 0; -1 if none is left */
+static int best_of(int n, const float *key, const unsigned char *ok)
+{
+    int b = -1;
+    for (int i = 0; i < n; ++i)
+        if (ok[i] && (b < 0 || key[i] > key[b]))
+            b = i;
+    return b;
+}
+
+/* gates over the selected experts, in double ([P3] 二.2 renormalisation; [P4]
+   Router: softmax over the selected logits) */
+static void form_gates(int k, const int32_t *sel, const float *logit_row,
+                       const float *score_row, int scoring, float *gates)
+{
+    double g[64];
+    double sum = 0.0;
+    if (scoring == ORACLE_SOFTMAX) {
+        double lmax = -INFINITY;
+        for (int j = 0; j < k; ++j)
+            if ((double)logit_row[sel[j]] > lmax)
+                lmax = (double)logit_row[sel[j]];
+        for (int j = 0; j < k; ++j) {
+            g[j] = exp((double)logit_row[sel[j]] - lmax);
+            sum += g[j];
+        }
+    } else {
+        for (int j = 0; j < k; ++j) {
+            g[j] = (double)score_row[sel[j]];
+            sum += g[j];
+        }
+    }
+    for (int j = 0; j < k; ++j)
+        gates[j] = (sum > 0.0) ? (float)(g[j] / sum) : (float)(1.0 / k);
+}
+
+/* ---------------------------------------------------------------------------
+ * Learned routing for one token.  Returns 0, or -1 on bad arguments.
+ *  key_i = affinity_i + bias_i  ([P3] 七.3: the bias only decides who is chosen)
+ *  optional group stage ([P2] V3 node-limited routing, [P3] 五.3): experts form
+ *  n_group contiguous groups; a group scores the sum of its top group_topk keys;
+ *  the topk_group best groups stay eligible.
+ *  top-k by key among eligible experts ([P3] 二.2, [P4] Router).
+ *  margin: the smallest gap between consecutive sorted values that decide the
+ *  result (keys 1..k+1 among eligible experts, and group scores around the
+ *  topk_group cut); tests use it to excuse near-ties.
+ * ------------------------------------------------------------------------- */
+static int route_one(int E, int k, int scoring, int n_group, int topk_group,
+                     int group_topk, const float *l, const float *bias,
+                     int32_t *ids, float *gates, float *margin)
+{
+    float *s = malloc(sizeof(float) * E);
+    float *key = malloc(sizeof(float) * E);
+    unsigned char *ok = malloc(E);
+    float m = INFINITY;
+    if (!s || !key || !ok)
+        return -1;
+    for (int i = 0; i < E; ++i) {
+        s[i] = oracle_affinity(l[i], scoring);
+        key[i] = bias ? s[i] + bias[i] : s[i];
+        ok[i] = 1;
+    }
+    if (n_group > 1) {
+        int G = E / n_group;
+        float *gs = malloc(sizeof(float) * n_group);
+        unsigned char *gok = malloc(n_group);
+        unsigned char *tmp = malloc(G);
+        for (int g = 0; g < n_group; ++g) {
+            /* sum of this group's group_topk largest keys, largest first */
+            memset(tmp, 1, G);
+            float acc = 0.0f;
+            for (int r = 0; r < group_topk; ++r) {
+                int b = best_of(G, key + g * G, tmp);
+                acc = (r == 0) ? key[g * G + b] : acc + key[g * G + b];
+                tmp[b] = 0;
+            }
+            gs[g] = acc;
+            gok[g] = 1;
+        }
+        unsigned char *keep = calloc(n_group, 1);
+        float prev = 0.0f;
+        for (int r = 0; r < topk_group + 1 && r < n_group; ++r) {
+            int b = best_of(n_group, gs, gok);
+            /* only the cut between kept and dropped groups decides the result */
+            if (r == topk_group && prev - gs[b] < m)
+                m = prev - gs[b];
+            prev = gs[b];
+            gok[b] = 0;
+            if (r < topk_group)
+                keep[b] = 1;
+        }
+        for (int i = 0; i < E; ++i)
+            ok[i] = keep[i / G];
+        free(gs);
+        free(gok);
+        free(tmp);
+        free(keep);
+    }
+    float prev = 0.0f;
+    for (int r = 0; r < k + 1; ++r) {
+        int b = best_of(E, key, ok);
+        if (b < 0) {
+            if (r < k) { /* fewer eligible experts than k */
+                free(s); free(key); free(ok);
+                return -1;
+            }
+            break;
+        }
+        if (r > 0 && prev - key[b] < m)
+            m = prev - key[b];
+        prev = key[b];
+        ok[b] = 0;
+        if (r < k)
+            ids[r] = b;
+    }
+    form_gates(k, ids, l, s, scoring, gates);
+    if (margin)
+        *margin = m;
+    free(s);
+    free(key);
+    free(ok);
+    return 0;
+}
+
+int oracle_route(int T, int E, int k, int scoring, int n_group, int topk_group,
+                 int group_topk, const float *logits, const float *bias,
+                 int32_t *ids, float *gates, float *margin)
+{
+    if (T < 0 || E < 1 || k < 1 || k > E || k > 64)
+        return -1;
+    if (n_group > 1 && (E % n_group || topk_group < 1 || topk_group > n_group ||
+                        group_topk < 1 || group_topk > E / n_group))
+        return -1;
+    for (int t = 0; t < T; ++t)
+        if (route_one(E, k, scoring, n_group, topk_group, group_topk,
+                      logits + (size_t)t * E, bias, ids + (size_t)t * k,
+                      gates + (size_t)t * k, margin ? margin + t : NULL))
+            return -1;
+    return 0;
+}
+
+/* Hash routing ([P1] 二 HashTopK; [P2] hash routing): ids come from the
+   token-id table; gates are the token's affinities at those ids, renormalised. */
+int oracle_hash_route(int T, int E, int k, int scoring, const float *logits,
+                      const int32_t *token_ids, const int32_t *tid2eid, int vocab,
+                      int32_t *ids, float *gates)
+{
+    float *s = malloc(sizeof(float) * E);
+    if (!s || k > 64)
+        return -1;
+    for (int t = 0; t < T; ++t) {
+        const float *l = logits + (size_t)t * E;
+        int tok = token_ids[t];
+        if (tok < 0 || tok >= vocab) {
+            free(s);
+            return -1;
+        }
+        for (int j = 0; j < k; ++j) {
+            int e = tid2eid[(size_t)tok * k + j];
+            if (e < 0 || e >= E) {
+                free(s);
+                return -1;
+            }
+            ids[(size_t)t * k + j] = e;
+        }
+        for (int i = 0; i < E; ++i)
+            s[i] = oracle_affinity(l[i], scoring);
+        form_gates(k, ids + (size_t)t * k, l, s, scoring, gates + (size_t)t * k);
+    }
+    free(s);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Token dispatch ([P4] Token Dispatch): the T*k (token, slot) pairs reordered
+ * expert-major, tokens ascending inside each expert.  Written as the plain
+ * definition: walk the experts in order and, for each, the pairs in token order.
+ * dispatch_index[t*k + j] is the row that pair (t, j) lands on.
+ * ------------------------------------------------------------------------- */
+int oracle_permute(int T, int k, int E, const int32_t *ids, const float *gates,
+                   int32_t *counts, int32_t *offsets, int32_t *sorted_tok,
+                   float *sorted_w, int32_t *dispatch_index)
+{
+    int r = 0;
+    for (int e = 0; e < E; ++e) {
+        offsets[e] = r;
+        counts[e] = 0;
+        for (int t = 0; t < T; ++t)
+            for (int j = 0; j < k; ++j)
+                if (ids[(size_t)t * k + j] == e) {
+                    sorted_tok[r] = t;
+                    sorted_w[r] = gates[(size_t)t * k + j];
+                    dispatch_index[(size_t)t * k + j] = r;
+                    ++counts[e];
+                    ++r;
+                }
+    }
+    offsets[E] = r;
+    return (r == T * k) ? 0 : -1; /* every pair must name an expert in [0, E) */
+}
+
+/* ---------------------------------------------------------------------------
+ * Combine ([P4] Token Combine, index_add_): for every dispatch row r,
+ * out[token_of_row[r]] += weight[r] * expert_out[r]; then the shared rows.
+ * out must hold zeros (or the value to add onto) on entry.
+ * ------------------------------------------------------------------------- */
+void oracle_combine(int P, int d, const double *expert_out, const int32_t *token_of_row,
+                    const float *weight_of_row, double *out)
+{
+    for (int r = 0; r < P; ++r) {
+        double w = (double)weight_of_row[r];
+        double *o = out + (size_t)token_of_row[r] * d;
+        const double *x = expert_out + (size_t)r * d;
+        for (int i = 0; i < d; ++i)
+            o[i] += w * x[i];
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * One SwiGLU expert ([P3] 二.1; [P1] 四; [P4] Expert):
+ *   y = W2 (SiLU(W1 x) (.) W3 x),  SiLU(z) = z / (1 + e^-z)
+ * with W1 = w13[0:d_ff], W3 = w13[d_ff:2 d_ff] (each [d_ff, d]) and W2 = w2 [d, d_ff].
+ * ------------------------------------------------------------------------- */
+void oracle_expert_ffn(int d, int d_ff, const double *x, const void *w13,
+                       const void *w2, int dtype, double *y)
+{
+    double *h = malloc(sizeof(double) * d_ff);
+    for (int f = 0; f < d_ff; ++f) {
+        double g = 0.0, u = 0.0;
+        for (int i = 0; i < d; ++i) {
+            g += elem(w13, (size_t)f * d + i, dtype) * x[i];
+            u += elem(w13, (size_t)(d_ff + f) * d + i, dtype) * x[i];
+        }
+        h[f] = g / (1.0 + exp(-g)) * u;
+    }
+    for (int o = 0; o < d; ++o) {
+        double acc = 0.0;
+        for (int f = 0; f < d_ff; ++f)
+            acc += elem(w2, (size_t)o * d_ff + f, dtype) * h[f];
+        y[o] = acc;
+    }
+    free(h);
+}
+
+/* router logits ([P3] 二.2: l = W_r x, W_r is [E, d]) for the listed tokens, in
+   double, plus an optional per-expert offset added to every token's logits */
+void oracle_logits(int n, const int32_t *rows, int d, int E, const void *hidden,
+                   const void *w_router, int dtype, const float *logit_offset,
+                   double *logits)
+{
+    for (int q = 0; q < n; ++q) {
+        size_t t = (size_t)rows[q];
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int i = 0; i < d; ++i)
+                acc += elem(w_router, (size_t)e * d + i, dtype) * elem(hidden, t * d + i, dtype);
+            if (logit_offset)
+                acc += (double)logit_offset[e];
+            logits[(size_t)q * E + e] = acc;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * The whole layer for a list of tokens ([P3] 二.2 and 二.3):
+ *   y_t = sum_j g[t,j] * FFN_{ids[t,j]}(x_t) + sum_s FFN^shared_s(x_t)
+ * Each listed token is routed from its own logits (rounded to float) and its
+ * output row is written in double.  w13[e] / w2[e] point at expert e's weights
+ * (only the experts the listed tokens select need to be non-NULL); route_mode
+ * 0 = learned, 1 = hash.  ids/gates/margin may be NULL.
+ * Returns 0, or -1 on bad arguments or a needed expert without weights.
+ * ------------------------------------------------------------------------- */
+int oracle_layer(int n, const int32_t *rows, int d, int E, int k, int d_ff,
+                 int n_shared, int dtype, int scoring, int route_mode, int n_group,
+                 int topk_group, int group_topk, const void *hidden,
+                 const void *w_router, const float *bias, const float *logit_offset,
+                 const int32_t *token_ids, const int32_t *tid2eid, int vocab,
+                 const void *const *w13, const void *const *w2,
+                 const void *w13_shared, const void *w2_shared, double *out,
+                 int32_t *ids_out, float *gates_out, float *margin_out)
+{
+    int bad = 0;
+    if (k < 1 || k > 64 || k > E || n_shared < 0 || n_shared > 1)
+        return -1;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int q = 0; q < n; ++q) {
+        int32_t ids[64];
+        float gates[64], margin = INFINITY;
+        double *lg = malloc(sizeof(double) * E);
+        float *lf = malloc(sizeof(float) * E);
+        double *x = malloc(sizeof(double) * d);
+        double *y = malloc(sizeof(double) * d);
+        double *o = out + (size_t)q * d;
+        size_t t = (size_t)rows[q];
+        oracle_logits(1, rows + q, d, E, hidden, w_router, dtype, logit_offset, lg);
+        for (int e = 0; e < E; ++e)
+            lf[e] = (float)lg[e];
+        int rc;
+        if (route_mode == 1)
+            rc = oracle_hash_route(1, E, k, scoring, lf, token_ids + t, tid2eid,
+                                   vocab, ids, gates);
+        else
+            rc = route_one(E, k, scoring, n_group, topk_group, group_topk, lf,
+                           bias, ids, gates, &margin);
+        for (int i = 0; i < d; ++i) {
+            x[i] = elem(hidden, t * d + i, dtype);
+            o[i] = 0.0;
+        }
+        for (int j = 0; !rc && j < k; ++j) {
+            if (!w13[ids[j]] || !w2[ids[j]]) {
+                rc = -1;
+                break;
+            }
+            oracle_expert_ffn(d, d_ff, x, w13[ids[j]], w2[ids[j]], dtype, y);
+            for (int i = 0; i < d; ++i)
+                o[i] += (double)gates[j] * y[i];
+        }
+        if (!rc && n_shared == 1) {
+            oracle_expert_ffn(d, d_ff, x, w13_shared, w2_shared, dtype, y);
+            for (int i = 0; i < d; ++i)
+                o[i] += y[i];
+        }
+        if (rc)
+            bad = 1;
+        for (int j = 0; j < k; ++j) {
+            if (ids_out)
+                ids_out[(size_t)q * k + j] = rc ? -1 : ids[j];
+            if (gates_out)
+                gates_out[(size_t)q * k + j] = rc ? 0.0f : gates[j];
+        }
+        if (margin_out)
+            margin_out[q] = margin;
+        free(lg);
+        free(lf);
+        free(x);
+        free(y);
+    }
+    return bad ? -1 : 0;
+}
+
+/* number of OpenMP threads the layer loop runs on (reported with timings) */
+int oracle_num_threads(void)
+{
+    int n = 1;
+#ifdef _OPENMP
+#pragma omp parallel
+    {
+#pragma omp single
+        n = omp_get_num_threads();
+    }
+#endif
+    return n;
+}

@@ -1,0 +1,379 @@
+"""Pins for the CPU oracle, against what the pages and the mathematics fix.
+
+Every check here runs on the CPU.  Worked examples come from tests/golden/
+(each file names its page and section); the rest are closed forms, invariants,
+an independent array formulation of the routing rules, and dense evaluation of
+every expert masked by the gates (textbook SwiGLU through torch, float64).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle as O
+
+
+# ----------------------------------------------------------------------------
+# independent references (torch / numpy library routines, float64)
+# ----------------------------------------------------------------------------
+def dense_swiglu(x, w13_e, w2_e):
+    """Textbook SwiGLU FFN: W2 (SiLU(W1 x) * W3 x), float64 torch."""
+    x = torch.as_tensor(x, dtype=torch.float64)
+    w13_e = torch.as_tensor(w13_e, dtype=torch.float64)
+    w2_e = torch.as_tensor(w2_e, dtype=torch.float64)
+    f = w13_e.shape[0] // 2
+    return (F.silu(x @ w13_e[:f].T) * (x @ w13_e[f:].T)) @ w2_e.T
+
+
+def np_affinity(l, scoring):
+    l = np.asarray(l, np.float32)
+    if scoring == O.SIGMOID:
+        return (1.0 / (1.0 + np.exp(-l.astype(np.float64)))).astype(np.float32)
+    if scoring == O.SQRTSOFTPLUS:
+        return np.sqrt(np.logaddexp(0.0, l.astype(np.float64))).astype(np.float32)
+    return l
+
+
+def np_route(logits, k, scoring, bias=None, n_group=1, topk_group=1, group_topk=0):
+    """Array formulation of the routing rules with stable argsorts: returns the
+    ids [T,k] and float64 gates [T,k]."""
+    s = np_affinity(logits, scoring)
+    key = s + (np.zeros(s.shape[1], np.float32) if bias is None else np.asarray(bias, np.float32))
+    T, E = key.shape
+    ids = np.zeros((T, k), np.int64)
+    gates = np.zeros((T, k))
+    for t in range(T):
+        kk = key[t].copy()
+        if n_group > 1:
+            G = E // n_group
+            grp = kk.reshape(n_group, G)
+            top = -np.sort(-grp, axis=1)[:, :group_topk]
+            gscore = top[:, 0].copy()
+            for r in range(1, group_topk):
+                gscore = (gscore + top[:, r]).astype(np.float32)
+            keep = np.argsort(-gscore, kind="stable")[:topk_group]
+            mask = np.zeros(n_group, bool)
+            mask[keep] = True
+            kk = np.where(np.repeat(mask, G), kk, -np.inf)
+        sel = np.argsort(-kk, kind="stable")[:k]
+        ids[t] = sel
+        if scoring == O.SOFTMAX:
+            p = torch.softmax(torch.as_tensor(logits[t], dtype=torch.float64), 0).numpy()
+            g = p[sel]
+        else:
+            g = s[t, sel].astype(np.float64)
+        gates[t] = g / g.sum()
+    return ids, gates
+
+
+def random_layer(rng, T, d, E, d_ff, dtype=np.float32):
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wr = (rng.standard_normal((E, d)) / math.sqrt(d)).astype(np.float32)
+    w13 = (rng.standard_normal((E, 2 * d_ff, d)) / math.sqrt(d)).astype(np.float32)
+    w2 = (rng.standard_normal((E, d, d_ff)) / math.sqrt(d_ff)).astype(np.float32)
+    return x, wr, w13, w2
+
+
+# ----------------------------------------------------------------------------
+# worked examples
+# ----------------------------------------------------------------------------
+def test_router_worked_example(golden):
+    g = golden("router_worked_example.json")
+    ids, gates, _ = O.route(np.array([g["scores"]], np.float32), g["k"], O.SOFTMAX)
+    assert ids[0].tolist() == g["expected_ids"]
+    half_unit = 0.5 * 10 ** -g["printed_decimals"]
+    assert np.all(np.abs(gates[0] - np.array(g["expected_weights_printed"])) <= half_unit)
+    assert abs(gates[0].sum() - 1.0) < 1e-6
+
+
+def _constant_rows(expert_of_row, token_of_row, d=4):
+    # expert output of dispatch row r: the constant 10*expert + token, so the
+    # combined value of a token is an exact linear form of its (expert, weight) pairs
+    return np.array([[10.0 * e + t] * d for e, t in zip(expert_of_row, token_of_row)])
+
+
+def test_two_token_toy(golden):
+    g = golden("two_token_toy.json")
+    ids = np.array(g["ids"], np.int32)
+    w = np.array(g["weights"], np.float32)
+    p = O.permute(ids, w, g["E"])
+    assert p["counts"].tolist() == g["expected_rows_per_expert"]
+    expert_of_row = np.repeat(np.arange(g["E"]), p["counts"])
+    eo = _constant_rows(expert_of_row, p["sorted_token_ids"])
+    y = O.combine(eo, p["sorted_token_ids"], p["sorted_weights"], T=2)
+    want_A = sum(wt * (10.0 * e + 0) for e, wt in g["expected_combine"]["A"])
+    assert y[0] == pytest.approx([want_A] * 4, rel=1e-6)
+    # token B by the same rule: 0.4 E5(x_B) + 0.6 E1(x_B)
+    assert y[1] == pytest.approx([0.4 * 51 + 0.6 * 11] * 4, rel=1e-6)
+
+
+def test_dispatch_combine_toy(golden):
+    g = golden("dispatch_combine_toy.json")
+    ids = np.array(g["ids"], np.int32)
+    w = np.array(g["weights"], np.float32)
+    p = O.permute(ids, w, g["E"])
+    assert p["sorted_token_ids"].tolist() == g["expected_permuted_token_ids"]
+    assert p["counts"].tolist() == g["expected_tokens_per_expert"]
+    assert np.array_equal(p["sorted_weights"], np.array(g["expected_position_weights"], np.float32))
+    assert p["offsets"].tolist() == [0, 3, 5, 8]
+    expert_of_row = np.repeat(np.arange(g["E"]), p["counts"])
+    eo = _constant_rows(expert_of_row, p["sorted_token_ids"])
+    y = O.combine(eo, p["sorted_token_ids"], p["sorted_weights"], T=4)
+    for t, terms in g["expected_combine"].items():
+        t = int(t)
+        want = sum(wt * (10.0 * e + t) for e, wt in terms)
+        assert y[t] == pytest.approx([want] * 4, rel=1e-6)
+
+
+def test_ep4_counts(golden):
+    g = golden("ep4_counts.json")
+    ids = np.array(g["ids"], np.int32)
+    p = O.permute(ids, np.ones(ids.shape, np.float32), g["E"])
+    assert p["counts"].tolist() == g["expected_rows_per_expert"]
+    m = np.zeros((4, 4), int)
+    for e in range(g["E"]):
+        for r in range(p["offsets"][e], p["offsets"][e + 1]):
+            m[g["token_rank"][p["sorted_token_ids"][r]], g["expert_rank"][e]] += 1
+    assert m.tolist() == g["expected_dispatch_matrix"]
+    assert m.sum(axis=0).tolist() == g["expected_received"]
+    assert m.sum() == g["expected_total"] == len(g["ids"]) * g["k"]
+
+
+def test_expected_active_experts(golden):
+    """Top-k of iid logits is a uniform k-subset, so the mean number of distinct
+    experts over B tokens follows the page's formula and table."""
+    g = golden("expected_active_experts.json")
+    rng = np.random.default_rng(7)
+    for tab in g["tables"]:
+        E, k = tab["E"], tab["k"]
+        for B, want in zip(tab["B"], tab["expected"]):
+            formula = E * (1 - (1 - k / E) ** B)
+            assert round(formula, 1) == pytest.approx(want, abs=0.051)
+            if B > 64:
+                continue
+            trials = 300
+            lg = rng.standard_normal((trials * B, E)).astype(np.float32)
+            ids, _, _ = O.route(lg, k, O.SOFTMAX)
+            act = [len(np.unique(ids[i * B:(i + 1) * B])) for i in range(trials)]
+            assert np.mean(act) == pytest.approx(formula, abs=max(0.6, 0.01 * formula))
+
+
+# ----------------------------------------------------------------------------
+# affinities: closed forms
+# ----------------------------------------------------------------------------
+def test_affinity_closed_forms():
+    assert O.affinity(0.0, O.SIGMOID) == 0.5
+    assert O.affinity(0.0, O.SQRTSOFTPLUS) == pytest.approx(math.sqrt(math.log(2.0)), rel=2e-7)
+    # sqrt(softplus) grows like sqrt(x) for large x, and never saturates
+    assert O.affinity(100.0, O.SQRTSOFTPLUS) == pytest.approx(10.0, rel=1e-7)
+    assert O.affinity(1e4, O.SQRTSOFTPLUS) == pytest.approx(100.0, rel=1e-7)
+    # sigmoid saturates to 1; softplus(-x) ~ e^-x
+    assert O.affinity(40.0, O.SIGMOID) == 1.0
+    assert O.affinity(-30.0, O.SQRTSOFTPLUS) == pytest.approx(math.exp(-15.0), rel=1e-5)
+    for x in np.linspace(-30, 30, 601):
+        xf = float(np.float32(x))
+        sig = 1.0 / (1.0 + math.exp(-xf))
+        ssp = math.sqrt(math.log1p(math.exp(xf)) if xf < 30 else xf + math.log1p(math.exp(-xf)))
+        assert O.affinity(xf, O.SIGMOID) == pytest.approx(sig, rel=3e-7, abs=1e-30)
+        assert O.affinity(xf, O.SQRTSOFTPLUS) == pytest.approx(ssp, rel=3e-7, abs=1e-30)
+    assert O.affinity(1.5, O.SOFTMAX) == 1.5
+
+
+# ----------------------------------------------------------------------------
+# routing: invariants and an independent formulation
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("scoring", [O.SOFTMAX, O.SIGMOID, O.SQRTSOFTPLUS])
+def test_softmax_and_scores_match_array_formulation(scoring):
+    rng = np.random.default_rng(11 + scoring)
+    T, E, k = 300, 64, 6
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (0.01 * rng.standard_normal(E)).astype(np.float32) if scoring else None
+    ids, gates, margin = O.route(lg, k, scoring, bias=bias)
+    rid, rg = np_route(lg, k, scoring, bias=bias)
+    ok = margin > 1e-6
+    assert ok.mean() > 0.95
+    assert np.array_equal(ids[ok], rid[ok])
+    assert np.allclose(gates[ok], rg[ok], atol=1e-6)
+    assert np.allclose(gates.sum(1), 1.0, atol=1e-6)
+    assert (gates >= 0).all()
+
+
+def test_group_routing_matches_array_formulation():
+    rng = np.random.default_rng(5)
+    T, E, k = 400, 256, 8
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (0.01 * rng.standard_normal(E)).astype(np.float32)
+    ids, gates, margin = O.route(lg, k, O.SIGMOID, bias=bias, n_group=8, topk_group=4, group_topk=2)
+    rid, rg = np_route(lg, k, O.SIGMOID, bias=bias, n_group=8, topk_group=4, group_topk=2)
+    ok = margin > 1e-6
+    assert ok.mean() > 0.9
+    assert np.array_equal(ids[ok], rid[ok])
+    assert np.allclose(gates[ok], rg[ok], atol=1e-6)
+    # selected experts span at most topk_group groups
+    assert max(len(np.unique(r // 32)) for r in ids) <= 4
+    # grouping actually binds on some tokens (otherwise the stage is untested)
+    flat, _, _ = O.route(lg, k, O.SIGMOID, bias=bias)
+    assert (np.sort(flat, 1) != np.sort(ids, 1)).any(axis=1).sum() > 10
+
+
+def test_group_routing_reductions():
+    rng = np.random.default_rng(6)
+    lg = rng.standard_normal((200, 64)).astype(np.float32)
+    a, ga, _ = O.route(lg, 4, O.SIGMOID, n_group=1)
+    b, gb, _ = O.route(lg, 4, O.SIGMOID, n_group=8, topk_group=8, group_topk=2)
+    assert np.array_equal(a, b) and np.array_equal(ga, gb)      # all groups kept
+    c, _, _ = O.route(lg, 4, O.SOFTMAX)                            # sigmoid is monotone
+    assert np.array_equal(a, c)
+    # the bias moves selection only: a uniform shift keeps ids and gates
+    d1, gd1, m1 = O.route(lg, 4, O.SIGMOID, bias=np.full(64, 0.25, np.float32))
+    ok = m1 > 1e-6
+    assert np.array_equal(d1[ok], a[ok]) and np.allclose(gd1[ok], ga[ok], atol=0)
+
+
+def test_bias_changes_selection_not_weights():
+    lg = np.array([[0.0, 0.1, 0.2, 0.3]], np.float32)
+    ids, g, _ = O.route(lg, 2, O.SIGMOID)
+    assert ids[0].tolist() == [3, 2]
+    ids2, g2, _ = O.route(lg, 2, O.SIGMOID, bias=np.array([1.0, 0, 0, 0], np.float32))
+    assert ids2[0].tolist() == [0, 3]
+    s = 1 / (1 + np.exp(-np.float64([0.0, 0.3])))
+    assert g2[0] == pytest.approx(s / s.sum(), abs=1e-7)
+
+
+def test_tie_break_lower_index_and_zero_denominator():
+    ids, g, m = O.route(np.zeros((1, 5), np.float32), 3, O.SOFTMAX)
+    assert ids[0].tolist() == [0, 1, 2] and m[0] == 0.0
+    assert g[0] == pytest.approx([1 / 3] * 3)
+    # sqrt(softplus(-200)) underflows to 0 in float: gates fall back to 1/k
+    ids, g, _ = O.route(np.full((1, 6), -200.0, np.float32), 2, O.SQRTSOFTPLUS)
+    assert g[0].tolist() == [0.5, 0.5]
+
+
+def test_hash_route():
+    rng = np.random.default_rng(3)
+    V, E, k, T = 50, 16, 4, 30
+    tab = np.stack([rng.permutation(E)[:k] for _ in range(V)]).astype(np.int32)
+    tok = rng.integers(0, V, T).astype(np.int32)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    ids, g = O.hash_route(lg, tok, tab, O.SQRTSOFTPLUS)
+    assert np.array_equal(ids, tab[tok])
+    s = np.sqrt(np.logaddexp(0, lg.astype(np.float64)))
+    want = np.take_along_axis(s, ids, 1)
+    assert np.allclose(g, want / want.sum(1, keepdims=True), atol=1e-6)
+
+
+# ----------------------------------------------------------------------------
+# permutation invariants
+# ----------------------------------------------------------------------------
+def test_permutation_invariants():
+    rng = np.random.default_rng(9)
+    T, E, k = 777, 37, 5
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    p = O.permute(ids, w, E)
+    assert p["counts"].sum() == T * k and p["offsets"][-1] == T * k
+    assert np.array_equal(np.sort(p["dispatch_index"].ravel()), np.arange(T * k))
+    tt = np.repeat(np.arange(T), k)
+    assert np.array_equal(p["sorted_token_ids"][p["dispatch_index"].ravel()], tt)
+    assert np.array_equal(p["sorted_weights"][p["dispatch_index"].ravel()], w.ravel())
+    for e in range(E):
+        seg = p["sorted_token_ids"][p["offsets"][e]:p["offsets"][e + 1]]
+        assert np.all(np.diff(seg) > 0)
+        assert np.all((ids[seg] == e).any(axis=1))
+    with pytest.raises(ValueError):
+        O.permute(np.array([[0, E]], np.int32), np.ones((1, 2), np.float32), E)
+
+
+# ----------------------------------------------------------------------------
+# expert FFN and the whole layer
+# ----------------------------------------------------------------------------
+def test_single_expert_is_dense_swiglu():
+    rng = np.random.default_rng(1)
+    x, wr, w13, w2 = random_layer(rng, 6, 24, 1, 40)
+    for scoring in (O.SOFTMAX, O.SIGMOID, O.SQRTSOFTPLUS):
+        r = O.layer(x, wr, w13, w2, k=1, scoring=scoring)
+        want = dense_swiglu(x, w13[0], w2[0]).numpy()
+        assert np.allclose(r["out"], want, rtol=1e-12, atol=1e-12)
+        assert (r["gates"] == 1.0).all()
+
+
+def test_expert_ffn_matches_dense():
+    rng = np.random.default_rng(2)
+    x, _, w13, w2 = random_layer(rng, 1, 16, 1, 24)
+    y = O.expert_ffn(x[0], w13[0], w2[0])
+    assert np.allclose(y, dense_swiglu(x[0], w13[0], w2[0]).numpy(), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("case", [
+    dict(scoring=O.SOFTMAX, k=2),
+    dict(scoring=O.SIGMOID, k=3, bias=True, n_group=3, topk_group=2, group_topk=2, shared=True),
+    dict(scoring=O.SQRTSOFTPLUS, k=2, bias=True, shared=True),
+    dict(scoring=O.SQRTSOFTPLUS, k=2, offset=True),
+])
+def test_layer_equals_dense_masked_evaluation(case):
+    """Every expert evaluated densely, weighted by a gate vector that is zero off
+    the top-k (independent routing via stable argsort), plus the shared expert."""
+    rng = np.random.default_rng(4)
+    T, d, E, d_ff = 7, 16, 6, 12
+    x, wr, w13, w2 = random_layer(rng, T, d, E, d_ff)
+    bias = (0.05 * rng.standard_normal(E)).astype(np.float32) if case.get("bias") else None
+    off = (-1.1 * np.log(rng.permutation(E) + 1.0)).astype(np.float32) if case.get("offset") else None
+    s13 = s2 = None
+    if case.get("shared"):
+        _, _, s13, s2 = random_layer(rng, 1, d, 1, d_ff)
+        s13, s2 = s13[0], s2[0]
+    grp = dict(n_group=case.get("n_group", 1), topk_group=case.get("topk_group", 1),
+               group_topk=case.get("group_topk", 0))
+    r = O.layer(x, wr, w13, w2, k=case["k"], scoring=case["scoring"], bias=bias,
+                logit_offset=off, w13_shared=s13, w2_shared=s2, **grp)
+    lg = (torch.as_tensor(x, dtype=torch.float64) @ torch.as_tensor(wr, dtype=torch.float64).T).numpy()
+    if off is not None:
+        lg = lg + off
+    rid, rg = np_route(lg.astype(np.float32), case["k"], case["scoring"], bias=bias, **grp)
+    gate = np.zeros((T, E))
+    np.put_along_axis(gate, rid, rg, 1)
+    dense = np.stack([dense_swiglu(x, w13[e], w2[e]).numpy() for e in range(E)], 1)  # [T,E,d]
+    want = np.einsum("te,ted->td", gate, dense)
+    if s13 is not None:
+        want += dense_swiglu(x, s13, s2).numpy()
+    assert (r["margin"] > 1e-5).all()
+    assert np.array_equal(r["ids"], rid)
+    assert np.allclose(r["out"], want, rtol=1e-6, atol=1e-6 * np.abs(want).max())
+
+
+def test_shared_expert_adds_a_dense_ffn():
+    rng = np.random.default_rng(8)
+    x, wr, w13, w2 = random_layer(rng, 5, 16, 4, 8)
+    _, _, s13, s2 = random_layer(rng, 1, 16, 1, 8)
+    a = O.layer(x, wr, w13, w2, k=2, scoring=O.SIGMOID)["out"]
+    b = O.layer(x, wr, w13, w2, k=2, scoring=O.SIGMOID, w13_shared=s13[0], w2_shared=s2[0])["out"]
+    assert np.allclose(b - a, dense_swiglu(x, s13[0], s2[0]).numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_bf16_inputs_are_used_exactly():
+    rng = np.random.default_rng(12)
+    x, wr, w13, w2 = random_layer(rng, 4, 16, 4, 8)
+    to_bits = lambda a: torch.as_tensor(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    to_f32 = lambda a: torch.as_tensor(a).to(torch.bfloat16).to(torch.float32).numpy()
+    a = O.layer(to_bits(x), to_bits(wr), to_bits(w13), to_bits(w2), k=2, scoring=O.SOFTMAX)
+    b = O.layer(to_f32(x), to_f32(wr), to_f32(w13), to_f32(w2), k=2, scoring=O.SOFTMAX)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["ids"], b["ids"])
+
+
+def test_logits_and_sampled_rows():
+    rng = np.random.default_rng(13)
+    x, wr, w13, w2 = random_layer(rng, 9, 16, 5, 8)
+    lg = O.logits(x, wr)
+    assert np.allclose(lg, x.astype(np.float64) @ wr.astype(np.float64).T, rtol=1e-12, atol=1e-12)
+    full = O.layer(x, wr, w13, w2, k=2, scoring=O.SOFTMAX)
+    rows = np.array([8, 2, 5], np.int32)
+    part = O.layer(x, wr, w13, w2, k=2, scoring=O.SOFTMAX, rows=rows)
+    assert np.array_equal(part["out"], full["out"][rows])
+    # experts no listed token selects may be absent
+    need = set(part["ids"].ravel().tolist())
+    w13s = [w13[e] if e in need else None for e in range(5)]
+    w2s = [w2[e] if e in need else None for e in range(5)]
+    again = O.layer(x, wr, w13s, w2s, k=2, scoring=O.SOFTMAX, rows=rows)
+    assert np.array_equal(again["out"], part["out"])
