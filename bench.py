@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark: one MoE FFN layer step on one MI355X.
+
+A step is one moe_forward call (router GEMM, scores + top-k, permutation,
+grouped SwiGLU GEMM 1, grouped GEMM 2, combine) over one batch of synthetic
+inputs already resident in HBM.  Prints ONE JSON line with tokens/s, the
+roofline of the dominant kernel (grouped GEMM 1 + SwiGLU), and the CPU oracle
+timed on a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + grouped-GEMM % bf16 MFMA peak (prefill), % HBM BW (decode)"
+DEFAULT_WORKLOAD = "mixtral_prefill"  # T=4096, d=4096, E=8, top-2, d_ff=14336, bf16
+
+# MI355X published peaks
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--all", action="store_true", help="also time the other workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def accounting(lc, counts):
+    """Algorithmic work of the grouped expert GEMMs from the realised routing.
+    Units: one dispatch row = one (token, expert) pair, shared expert included.
+      GEMM 1 (+SwiGLU): 4*d*d_ff FLOPs per row; bytes = w13 of every expert with
+      rows (2*d_ff*d elements) + gathered rows read (d) + H written (d_ff) per row
+      GEMM 2: 2*d*d_ff FLOPs per row; bytes = w2 of active experts + H read + Y written
+    Layer FLOPs per row: 6*d*d_ff (the SwiGLU count)."""
+    import numpy as np
+    es = 4 if lc.dtype == "f32" else 2
+    d, F, T, k, S = lc.d, lc.d_ff, lc.T, lc.k, lc.n_shared
+    active = int((np.asarray(counts) > 0).sum()) + S
+    rows = T * k + S * T
+    routed_rows = T * k
+    routed_active = int((np.asarray(counts) > 0).sum())
+    up_flops = 4 * d * F * rows
+    up_bytes = (active * 2 * F * d + rows * d + rows * F) * es
+    up_routed_flops = 4 * d * F * routed_rows
+    up_routed_bytes = (routed_active * 2 * F * d + routed_rows * d + routed_rows * F) * es
+    layer_flops = 6 * d * F * rows + 2 * T * d * lc.E
+    layer_bytes = (active * 3 * F * d + 2 * T * d + 2 * rows * F) * es + T * lc.E * 4
+    return dict(active_experts=active, rows=rows, up_flops=up_flops, up_bytes=up_bytes,
+                up_routed_flops=up_routed_flops, up_routed_bytes=up_routed_bytes,
+                layer_flops=layer_flops, layer_bytes=layer_bytes)
+
+
+def time_gpu(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        fn()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return ev0.elapsed_time(ev1) / steps, wall
+
+
+def run_workload(name, steps, warmup, with_cpu, cpu_seconds):
+    import numpy as np
+    import torch
+
+    import mixture_experts_ffn_sqrt_amd as moe
+    from mixture_experts_ffn_sqrt_amd.synth import CONFIGS, make_inputs
+
+    lc = CONFIGS[name]
+    stream = torch.cuda.current_stream()
+    inp = make_inputs(lc, "cuda")
+    c = moe.make_config(T=lc.T, d=lc.d, E=lc.E, k=lc.k, d_ff=lc.d_ff, n_shared=lc.n_shared,
+                        dtype=lc.dtype, scoring=lc.scoring, n_group=lc.n_group,
+                        topk_group=lc.topk_group, group_topk=lc.group_topk)
+    layer = moe.MoELayer(c, inp)
+    print("[bench] %s: inputs ready, workspace %.1f MB" % (name, layer.workspace.numel() / 1e6),
+          file=sys.stderr, flush=True)
+
+    ms_step, wall = time_gpu(layer.forward, steps, warmup, stream)
+    print("[bench] %s: %.3f ms/step" % (name, ms_step), file=sys.stderr, flush=True)
+
+    # staged pieces on the same stream: routing decision of the last step
+    ids = layer.ids
+    counts = np.bincount(ids.cpu().numpy().ravel(), minlength=lc.E)
+    acct = accounting(lc, counts)
+    T, k, E = lc.T, lc.k, lc.E
+    ws = layer.workspace
+    perm = dict(counts=torch.empty(E, dtype=torch.int32, device="cuda"),
+                offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+                tok=torch.empty(T * k, dtype=torch.int32, device="cuda"),
+                w=torch.empty(T * k, dtype=torch.float32, device="cuda"),
+                disp=torch.empty((T, k), dtype=torch.int32, device="cuda"))
+    moe.moe_permute(c, ids, layer.gates, perm["counts"], perm["offsets"], perm["tok"], perm["w"],
+                    perm["disp"], ws)
+    H = torch.empty((T * k, lc.d_ff), dtype=lc.torch_dtype, device="cuda")
+    Y = torch.empty((T * k, lc.d), dtype=lc.torch_dtype, device="cuda")
+
+    def up():
+        moe.moe_expert_up(c, inp["hidden"], perm["tok"], perm["offsets"], inp["w13"], H, ws)
+
+    def down():
+        moe.moe_expert_down(c, H, perm["offsets"], inp["w2"], Y, ws)
+
+    ms_up, _ = time_gpu(up, steps, warmup, stream)
+    ms_down, _ = time_gpu(down, steps, warmup, stream)
+
+    decode = acct["rows"] / max(acct["active_experts"], 1) < 48
+    if decode:
+        ach = acct["up_routed_bytes"] / (ms_up * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(ach / PEAK_HBM_GBS, 4), traffic=None)
+    else:
+        ach = acct["up_routed_flops"] / (ms_up * 1e-3) / 1e12
+        peak = PEAK_TFLOPS[lc.dtype]
+        roof = dict(bound="mfma", achieved=round(ach, 1), peak=peak, unit="TFLOP/s",
+                    frac=round(ach / peak, 4), traffic=None)
+    roof["kernel"] = "grouped_gemm_kernel (GEMM 1 + SwiGLU, routed rows)"
+    roof["kernel_ms"] = round(ms_up, 4)
+    gemm_tflops = 6 * lc.d * lc.d_ff * T * k / ((ms_up + ms_down) * 1e-3) / 1e12
+    res = dict(
+        workload=name, ms_per_step=ms_step, tokens_per_s=T / (ms_step * 1e-3), wall_s=wall,
+        roofline=roof,
+        grouped_gemm=dict(ms_up=round(ms_up, 4), ms_down=round(ms_down, 4),
+                          tflops=round(gemm_tflops, 1),
+                          frac_bf16_peak=round(gemm_tflops / PEAK_TFLOPS[lc.dtype], 4)),
+        layer=dict(tflops=round(acct["layer_flops"] / (ms_step * 1e-3) / 1e12, 1),
+                   gbs=round(acct["layer_bytes"] / (ms_step * 1e-3) / 1e9, 1),
+                   hbm_frac=round(acct["layer_bytes"] / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                   mfma_frac=round(acct["layer_flops"] / (ms_step * 1e-3) / 1e12
+                                   / PEAK_TFLOPS[lc.dtype], 4)),
+        routing=dict(active_experts=acct["active_experts"], max_rows=int(counts.max()),
+                     mean_rows=float(counts.mean()), empty_experts=int((counts == 0).sum())),
+    )
+    if with_cpu:
+        res["cpu_baseline"] = cpu_baseline(lc, inp, cpu_seconds)
+    del layer, inp, H, Y, perm
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(lc, inp, seconds):
+    """The oracle as it stands, on a bounded sample of this workload's tokens
+    (the first n rows), all host threads.  Reported in tokens/s."""
+    import numpy as np
+
+    import oracle as O
+    from mixture_experts_ffn_sqrt_amd.synth import to_host_bits
+
+    threads = O.num_threads()
+    h = to_host_bits(inp["hidden"])
+    wr = to_host_bits(inp["w_router"])
+    bias = to_host_bits(inp.get("bias"))
+    off = to_host_bits(inp.get("logit_offset"))
+    w13 = to_host_bits(inp["w13"])
+    w2 = to_host_bits(inp["w2"])
+    s13 = to_host_bits(inp.get("w13_shared"))
+    s2 = to_host_bits(inp.get("w2_shared"))
+    grp = dict(n_group=lc.n_group, topk_group=lc.topk_group, group_topk=lc.group_topk)
+
+    def run(rows):
+        t0 = time.perf_counter()
+        O.layer(h, wr, w13, w2, k=lc.k, scoring=lc.scoring, rows=rows, bias=bias,
+                logit_offset=off, w13_shared=s13, w2_shared=s2, **grp)
+        return time.perf_counter() - t0
+
+    probe = np.arange(min(threads, lc.T), dtype=np.int32)
+    tp = run(probe)
+    reps = max(1, min(int(seconds / max(tp, 1e-3)), lc.T // max(len(probe), 1)))
+    rows = np.arange(min(lc.T, len(probe) * reps), dtype=np.int32)
+    t = run(rows)
+    return dict(value=round(len(rows) / t, 3), unit="tokens/s", cores=threads, kind="oracle",
+                sample="first %d of %d tokens of %s, full layer per token (float64 FFN), %.1f s"
+                       % (len(rows), lc.T, lc.name, t))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the layer runs on a single MI355X and this "
+              "build has no multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import mixture_experts_ffn_sqrt_amd as moe
+    moe.load_library()
+
+    head = run_workload(args.workload, args.steps, args.warmup, not args.no_cpu, args.cpu_seconds)
+    from mixture_experts_ffn_sqrt_amd.synth import CONFIGS
+    lc = CONFIGS[args.workload]
+    line = {
+        "metric": METRIC,
+        "value": round(head["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": lc.dtype,
+        "data": "synthetic (seeded N(0,1) hidden, N(0,1/fan_in) weights)",
+        "config": {"workload": lc.name, "T": lc.T, "d": lc.d, "E": lc.E, "k": lc.k,
+                   "d_ff": lc.d_ff, "n_shared": lc.n_shared, "scoring": lc.scoring,
+                   "n_group": lc.n_group, "topk_group": lc.topk_group,
+                   "group_topk": lc.group_topk, "parallelism": "single GPU"},
+        "roofline": head["roofline"],
+        "cpu_baseline": head.get("cpu_baseline"),
+        "grouped_gemm": head["grouped_gemm"],
+        "layer": head["layer"],
+        "routing": head["routing"],
+    }
+    if args.all:
+        others = {}
+        for name in CONFIGS:
+            if name == args.workload:
+                continue
+            r = run_workload(name, args.steps, args.warmup, False, 0)
+            others[name] = {kk: r[kk] for kk in ("ms_per_step", "tokens_per_s", "roofline",
+                                                  "grouped_gemm", "layer", "routing")}
+        line["workloads"] = others
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,179 @@
+/*
+ * moe.h -- C ABI of the single-GPU Mixture-of-Experts FFN layer for MI355X (gfx950).
+ *
+ * The layer, for each token x_t (a row of `hidden`):
+ *   logits  l = W_r x_t (+ optional per-expert logit offset)
+ *   scores  s = softmax / sigmoid / sqrt(softplus) of l; selection key s + bias
+ *   top-k   ids[t, 0..k-1] in descending key order, gates renormalised over
+ *           the selected unbiased scores
+ *   y_t     = sum_j g[t,j] * FFN_{ids[t,j]}(x_t) + FFN_shared(x_t)
+ *   FFN_e(x) = W2_e (SiLU(W1_e x) (.) W3_e x)
+ * Sources (web pages by title and section):
+ *   "MoE 的算量与通信" (arganzheng) chapter 二.1-二.3: SwiGLU FFN, router W_r [E, d],
+ *       top-k, renormalisation, weighted sum plus shared experts; 七.3: the
+ *       selection bias; 五.3: group-limited choice.
+ *   "MoE 架构与路由策略" (DeepSeek-V4 notes): equation dsv4-moe-softplus (sigmoid
+ *       and sqrt(softplus)), the V3 node-limited routing section, hash routing.
+ *   "DeepSeek-V4 MoE: Token 从路由到专家计算" (akiyangdev) sections 二 and 四:
+ *       MoEGate weight [n_routed_experts, hidden_size], topk_ids / topk_weights,
+ *       HashTopK's tid2eid, w13_weight (gate and up fused) and w2_weight,
+ *       the dispatch -> expert core -> combine hand-off.
+ *   "Mixture of Experts: Router, Token Dispatch, Grouped GEMM" (111qqz):
+ *       router worked example, permuted_token_ids / tokens_per_expert, grouped
+ *       GEMM over ragged row counts, index_add_ combine.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers on the current HIP device, row-major
+ *    and contiguous, 16-byte aligned.  Outputs must not alias inputs.  The caller
+ *    owns all memory, including the workspace; the library never allocates,
+ *    frees or synchronises.  Work is queued on `stream` (a hipStream_t; NULL is
+ *    the default stream) and completes asynchronously.  No global mutable state:
+ *    calls with distinct workspaces may run concurrently.
+ *  - Floating-point tensors (hidden, weights, expert outputs, out) are float32
+ *    when cfg->dtype == MOE_F32 and bfloat16 when MOE_BF16.  Logits, gates, bias
+ *    and logit offsets are always float32; accumulation is always float32.
+ *  - w13 is [E, 2*d_ff, d]: rows [0, d_ff) are W1 (gate, the SiLU input) and rows
+ *    [d_ff, 2*d_ff) are W3 (up).  w2 is [E, d, d_ff].  Shared-expert weights are
+ *    one expert's worth: w13_shared [2*d_ff, d], w2_shared [d, d_ff].
+ *  - Errors: every argument check runs on the host before any launch, so an
+ *    error return means no work was queued.  A failed launch returns
+ *    MOE_ERR_HIP; faults inside kernels surface at the caller's next
+ *    synchronisation of the stream.  T == 0 is valid and queues nothing.
+ *  - Device-side range errors (an expert id outside [0, E) in moe_permute's
+ *    input, a token id outside [0, vocab)) are not trapped: such a pair gets no
+ *    dispatch row, its dispatch_index entry is -1, and expert_offsets[E] counts
+ *    only the valid pairs.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1, /* null required pointer, inconsistent sizes */
+    MOE_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels handle */
+    MOE_ERR_WORKSPACE = -3,   /* workspace too small (see moe_workspace_size) */
+    MOE_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1, MOE_SCORE_SQRTSOFTPLUS = 2 } moe_scoring;
+typedef enum { MOE_ROUTE_LEARNED = 0, MOE_ROUTE_HASH = 1 } moe_route_mode;
+
+/* Layer shape and routing rule.
+ *   T tokens, hidden size d, E routed experts, k selected per token, expert
+ *   width d_ff, n_shared in {0, 1} unrouted experts.
+ *   Group-limited routing (DeepSeek-V3): n_group > 1 splits the experts into
+ *   n_group contiguous groups of E/n_group; each group scores the sum of its
+ *   group_topk largest keys; the topk_group best groups stay eligible; then top-k
+ *   among them.  n_group = 1 disables it (topk_group, group_topk ignored).
+ *   Hash routing (route_mode MOE_ROUTE_HASH): ids are tid2eid[token_ids[t]]
+ *   (a [vocab, k] table); gates are the token's affinities at those ids,
+ *   renormalised; the bias is unused.
+ *   logits_given (moe_route only): 1 = `logits` is an input and the router GEMM
+ *   is skipped.
+ * Limits: 1 <= k <= min(E, 16); E <= 1024; d, d_ff multiples of 64;
+ *   n_group <= 64 with E % n_group == 0, 1 <= topk_group <= n_group,
+ *   1 <= group_topk <= E/n_group and k <= topk_group*E/n_group;
+ *   T*(k+n_shared)*max(d, d_ff) < 2^31. */
+typedef struct moe_config {
+    int32_t T, d, E, k, d_ff, n_shared;
+    int32_t dtype;      /* moe_dtype */
+    int32_t scoring;    /* moe_scoring */
+    int32_t route_mode; /* moe_route_mode */
+    int32_t n_group, topk_group, group_topk;
+    int32_t vocab;        /* hash mode: rows of tid2eid */
+    int32_t logits_given; /* moe_route: read logits instead of computing them */
+} moe_config;
+
+/* Bytes of workspace moe_forward needs for this configuration (moe_permute and
+ * moe_expert_ffn need no more).  Returns MOE_OK or an argument error. */
+int moe_workspace_size(const moe_config *cfg, size_t *bytes);
+
+/* Router: logits, affinity scores, (group-limited) top-k and gates.
+ *   hidden [T, d], w_router [E, d]  (unused when cfg->logits_given)
+ *   logit_offset [E] float32, nullable: added to every token's logits
+ *   bias [E] float32, nullable: added to the scores for selection only
+ *   token_ids [T] int32, tid2eid [vocab, k] int32: hash mode only
+ *   logits [T, E] float32: output (input when cfg->logits_given)
+ *   topk_ids [T, k] int32, topk_weights [T, k] float32: outputs, slot j holds
+ *   the j-th largest key (equal keys: lower expert id first); in hash mode, the
+ *   table's order.  Needs no workspace. */
+int moe_route(const moe_config *cfg, const void *hidden, const void *w_router,
+              const float *logit_offset, const float *bias, const int32_t *token_ids,
+              const int32_t *tid2eid, float *logits, int32_t *topk_ids,
+              float *topk_weights, void *stream);
+
+/* Token dispatch: the T*k (token, slot) pairs sorted expert-major, tokens in
+ * ascending order inside each expert (a stable sort by expert id).
+ *   topk_ids [T, k] int32 (any slot order), topk_weights [T, k] float32
+ *   expert_counts [E], expert_offsets [E+1] (exclusive prefix sum; [E] = T*k)
+ *   sorted_token_ids [T*k]: token of each dispatch row
+ *   sorted_weights [T*k]: gate of each dispatch row
+ *   dispatch_index [T, k]: dispatch row of pair (t, j)
+ *   workspace: at least moe_workspace_size bytes. */
+int moe_permute(const moe_config *cfg, const int32_t *topk_ids, const float *topk_weights,
+                int32_t *expert_counts, int32_t *expert_offsets, int32_t *sorted_token_ids,
+                float *sorted_weights, int32_t *dispatch_index, void *workspace,
+                size_t workspace_bytes, void *stream);
+
+/* Grouped SwiGLU experts over ragged row counts: for every expert e and every
+ * dispatch row r in [expert_offsets[e], expert_offsets[e+1]),
+ *   expert_out[r] = FFN_e(hidden[sorted_token_ids[r]])   (unweighted)
+ * in cfg->dtype.  hidden [T, d]; sorted_token_ids [R]; expert_offsets [E+1]
+ * (device; R = expert_offsets[E] <= T*k); w13 [E, 2*d_ff, d]; w2 [E, d, d_ff];
+ * expert_out [T*k, d].  The intermediate SiLU(W1 x) (.) W3 x is rounded to
+ * cfg->dtype.  For the shared expert, call with E = 1, k = 1, identity rows
+ * (sorted_token_ids[t] = t) and offsets {0, T}. */
+int moe_expert_ffn(const moe_config *cfg, const void *hidden, const int32_t *sorted_token_ids,
+                   const int32_t *expert_offsets, const void *w13, const void *w2,
+                   void *expert_out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* The two stages of moe_expert_ffn, callable on their own (the pages' Linear-1
+ * with its activation, and Linear-2):
+ *   moe_expert_up:   h_out[r] = SiLU(W1_e x) (.) W3_e x,  x = hidden[sorted_token_ids[r]]
+ *                    h_out [T*k, d_ff] in cfg->dtype (rounded once from float32)
+ *   moe_expert_down: expert_out[r] = W2_e h[r]; h [T*k, d_ff], expert_out [T*k, d]
+ * for every expert e and dispatch row r in [expert_offsets[e], expert_offsets[e+1]).
+ * Other arguments as for moe_expert_ffn; rows past expert_offsets[E] are untouched. */
+int moe_expert_up(const moe_config *cfg, const void *hidden, const int32_t *sorted_token_ids,
+                  const int32_t *expert_offsets, const void *w13, void *h_out, void *workspace,
+                  size_t workspace_bytes, void *stream);
+int moe_expert_down(const moe_config *cfg, const void *h, const int32_t *expert_offsets,
+                    const void *w2, void *expert_out, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* Weighted combine back into token rows, in a fixed order (deterministic):
+ *   out[t] = sum_{j<k} topk_weights[t,j] * expert_out[dispatch_index[t,j]]
+ *            + shared_out[t]   (when shared_out is not NULL)
+ * summed in float32 in slot order j = 0..k-1, then the shared row; rounded once
+ * to cfg->dtype.  expert_out [T*k, d]; shared_out [T, d] nullable; out [T, d].
+ * Pairs with dispatch_index -1 are skipped.  Needs no workspace. */
+int moe_combine(const moe_config *cfg, const void *expert_out, const int32_t *dispatch_index,
+                const float *topk_weights, const void *shared_out, void *out, void *stream);
+
+/* The whole layer in one call: route, permute, grouped experts (routed and
+ * shared in the same grouped launches), combine.  Arguments as above;
+ * w13_shared / w2_shared are required when cfg->n_shared == 1.
+ * topk_ids_out [T, k] and topk_weights_out [T, k] are optional copies of the
+ * routing decision (nullable).  out [T, d]. */
+int moe_forward(const moe_config *cfg, const void *hidden, const void *w_router,
+                const float *logit_offset, const float *bias, const int32_t *token_ids,
+                const int32_t *tid2eid, const void *w13, const void *w2,
+                const void *w13_shared, const void *w2_shared, void *out,
+                int32_t *topk_ids_out, float *topk_weights_out, void *workspace,
+                size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *moe_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,294 @@
+// C ABI entry points (include/moe.h): argument checks on the host, workspace
+// carve-up, and the launch sequence on the caller's stream.  The library keeps
+// no state between calls and never allocates or synchronises.
+#include <algorithm>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+Workspace workspace_layout(const moe_config& c) {
+  const int64_t T = c.T, E = c.E, k = c.k, S = c.n_shared;
+  const int64_t R = T * k, P = R + S * T, G = E + S;
+  const int64_t es = c.dtype == MOE_F32 ? 4 : 2;
+  const int64_t nblk = std::max<int64_t>(1, (R + kPermuteChunk - 1) / kPermuteChunk);
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = off;
+    off = align_up(off + std::max<int64_t>(bytes, 1), 256);
+    return o;
+  };
+  Workspace w;
+  w.logits = take(T * E * 4);
+  w.ids = take(R * 4);
+  w.weights = take(R * 4);
+  w.blockcnt = take(nblk * E * 4);
+  w.counts = take(E * 4);
+  w.offsets = take((E + 1) * 4);
+  w.groups = take(2 * G * 4);
+  w.tile_prefix = take(kNumTileHeights * (G + 1) * 4);
+  w.sorted_tok = take(P * 4);
+  w.sorted_w = take(R * 4);
+  w.dispatch = take(R * 4);
+  w.H = take(P * c.d_ff * es);
+  w.Y = take(P * c.d * es);
+  w.total = off;
+  return w;
+}
+
+namespace {
+
+int check_cfg(const moe_config* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->T < 0 || c->d < 1 || c->E < 1 || c->k < 1 || c->d_ff < 1) return MOE_ERR_INVALID_ARG;
+  if (c->n_shared < 0 || c->n_shared > 1) return MOE_ERR_INVALID_ARG;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->scoring < MOE_SCORE_SOFTMAX || c->scoring > MOE_SCORE_SQRTSOFTPLUS)
+    return MOE_ERR_INVALID_ARG;
+  if (c->route_mode != MOE_ROUTE_LEARNED && c->route_mode != MOE_ROUTE_HASH)
+    return MOE_ERR_INVALID_ARG;
+  if (c->k > c->E) return MOE_ERR_INVALID_ARG;
+  if (c->E > 1024 || c->k > 16) return MOE_ERR_UNSUPPORTED;
+  if (c->d % 64 || c->d_ff % 64) return MOE_ERR_UNSUPPORTED;
+  if (c->n_group < 1) return MOE_ERR_INVALID_ARG;
+  if (c->n_group > 1) {
+    if (c->n_group > 64) return MOE_ERR_UNSUPPORTED;
+    if (c->E % c->n_group) return MOE_ERR_INVALID_ARG;
+    const int G = c->E / c->n_group;
+    if (c->topk_group < 1 || c->topk_group > c->n_group) return MOE_ERR_INVALID_ARG;
+    if (c->group_topk < 1 || c->group_topk > G) return MOE_ERR_INVALID_ARG;
+    if (c->k > c->topk_group * G) return MOE_ERR_INVALID_ARG;
+  }
+  if (c->route_mode == MOE_ROUTE_HASH && c->vocab < 1) return MOE_ERR_INVALID_ARG;
+  const int64_t P = static_cast<int64_t>(c->T) * (c->k + c->n_shared);
+  const int64_t width = std::max(c->d, c->d_ff);
+  if (P * width >= (int64_t(1) << 31) * 64 || P >= (int64_t(1) << 30) ||
+      static_cast<int64_t>(c->T) * c->E >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+template <typename T>
+T* at(void* ws, int64_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// Tile lists for the routed experts of the staged API (E groups, rows from the
+// caller's offsets) and the matching launch arguments.
+int staged_groups(const moe_config& c, const int32_t* expert_offsets, void* workspace,
+                  const Workspace& w, hipStream_t s, ExpertFfnArgs* a) {
+  int32_t* groups = at<int32_t>(workspace, w.groups);
+  int32_t* tiles = at<int32_t>(workspace, w.tile_prefix);
+  const int st = hip_status(
+      launch_build_tiles(expert_offsets, c.E, c.T * c.k, 0, 0, groups, tiles, nullptr, s));
+  *a = ExpertFfnArgs{};
+  a->g_begin = groups;
+  a->g_end = groups + c.E;
+  a->tile_prefix = tiles;
+  a->n_groups = c.E;
+  a->rows_bound = c.T * c.k;
+  a->routed_groups = c.E;
+  return st;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_workspace_size(const moe_config* cfg, size_t* bytes) {
+  const int st = check_cfg(cfg);
+  if (st) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = static_cast<size_t>(workspace_layout(*cfg).total);
+  return MOE_OK;
+}
+
+int moe_route(const moe_config* cfg, const void* hidden, const void* w_router,
+              const float* logit_offset, const float* bias, const int32_t* token_ids,
+              const int32_t* tid2eid, float* logits, int32_t* topk_ids, float* topk_weights,
+              void* stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  const moe_config& c = *cfg;
+  if (!logits || !topk_ids || !topk_weights) return MOE_ERR_INVALID_ARG;
+  if (!c.logits_given && (!hidden || !w_router)) return MOE_ERR_INVALID_ARG;
+  if (c.route_mode == MOE_ROUTE_HASH && (!token_ids || !tid2eid)) return MOE_ERR_INVALID_ARG;
+  if (c.T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!c.logits_given) {
+    st = hip_status(launch_router_gemm(c, hidden, w_router, logit_offset, logits, s));
+    if (st) return st;
+  }
+  return hip_status(launch_topk(c, logits, bias, token_ids, tid2eid, topk_ids, topk_weights, s));
+}
+
+int moe_permute(const moe_config* cfg, const int32_t* topk_ids, const float* topk_weights,
+                int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_token_ids,
+                float* sorted_weights, int32_t* dispatch_index, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  const int st = check_cfg(cfg);
+  if (st) return st;
+  const moe_config& c = *cfg;
+  if (!topk_ids || !topk_weights || !expert_counts || !expert_offsets || !sorted_token_ids ||
+      !sorted_weights || !dispatch_index || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  const Workspace w = workspace_layout(c);
+  if (workspace_bytes < static_cast<size_t>(w.total)) return MOE_ERR_WORKSPACE;
+  if (c.T == 0) return MOE_OK;
+  return hip_status(launch_permute(c, topk_ids, topk_weights, at<int32_t>(workspace, w.blockcnt),
+                                   expert_counts, expert_offsets, sorted_token_ids,
+                                   sorted_weights, dispatch_index,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int moe_expert_up(const moe_config* cfg, const void* hidden, const int32_t* sorted_token_ids,
+                  const int32_t* expert_offsets, const void* w13, void* h_out, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  const moe_config& c = *cfg;
+  if (!hidden || !sorted_token_ids || !expert_offsets || !w13 || !h_out || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  const Workspace w = workspace_layout(c);
+  if (workspace_bytes < static_cast<size_t>(w.total)) return MOE_ERR_WORKSPACE;
+  if (c.T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ExpertFfnArgs a;
+  if ((st = staged_groups(c, expert_offsets, workspace, w, s, &a))) return st;
+  a.hidden = hidden;
+  a.sorted_tok = sorted_token_ids;
+  a.w13 = w13;
+  a.H = h_out;
+  return hip_status(launch_expert_up(c, a, s));
+}
+
+int moe_expert_down(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
+                    const void* w2, void* expert_out, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  const moe_config& c = *cfg;
+  if (!h || !expert_offsets || !w2 || !expert_out || !workspace) return MOE_ERR_INVALID_ARG;
+  const Workspace w = workspace_layout(c);
+  if (workspace_bytes < static_cast<size_t>(w.total)) return MOE_ERR_WORKSPACE;
+  if (c.T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ExpertFfnArgs a;
+  if ((st = staged_groups(c, expert_offsets, workspace, w, s, &a))) return st;
+  a.H = const_cast<void*>(h);
+  a.w2 = w2;
+  a.Y = expert_out;
+  return hip_status(launch_expert_down(c, a, s));
+}
+
+int moe_expert_ffn(const moe_config* cfg, const void* hidden, const int32_t* sorted_token_ids,
+                   const int32_t* expert_offsets, const void* w13, const void* w2,
+                   void* expert_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  const moe_config& c = *cfg;
+  if (!hidden || !sorted_token_ids || !expert_offsets || !w13 || !w2 || !expert_out ||
+      !workspace)
+    return MOE_ERR_INVALID_ARG;
+  const Workspace w = workspace_layout(c);
+  if (workspace_bytes < static_cast<size_t>(w.total)) return MOE_ERR_WORKSPACE;
+  if (c.T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ExpertFfnArgs a;
+  if ((st = staged_groups(c, expert_offsets, workspace, w, s, &a))) return st;
+  a.hidden = hidden;
+  a.sorted_tok = sorted_token_ids;
+  a.w13 = w13;
+  a.w2 = w2;
+  a.H = at<char>(workspace, w.H);
+  a.Y = expert_out;
+  if ((st = hip_status(launch_expert_up(c, a, s)))) return st;
+  return hip_status(launch_expert_down(c, a, s));
+}
+
+int moe_combine(const moe_config* cfg, const void* expert_out, const int32_t* dispatch_index,
+                const float* topk_weights, const void* shared_out, void* out, void* stream) {
+  const int st = check_cfg(cfg);
+  if (st) return st;
+  if (!expert_out || !dispatch_index || !topk_weights || !out) return MOE_ERR_INVALID_ARG;
+  if (cfg->T == 0) return MOE_OK;
+  return hip_status(launch_combine(*cfg, expert_out, dispatch_index, topk_weights, shared_out,
+                                   out, static_cast<hipStream_t>(stream)));
+}
+
+int moe_forward(const moe_config* cfg, const void* hidden, const void* w_router,
+                const float* logit_offset, const float* bias, const int32_t* token_ids,
+                const int32_t* tid2eid, const void* w13, const void* w2, const void* w13_shared,
+                const void* w2_shared, void* out, int32_t* topk_ids_out,
+                float* topk_weights_out, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  const moe_config& c = *cfg;
+  if (!hidden || !w_router || !w13 || !w2 || !out || !workspace) return MOE_ERR_INVALID_ARG;
+  if (c.n_shared && (!w13_shared || !w2_shared)) return MOE_ERR_INVALID_ARG;
+  if (c.route_mode == MOE_ROUTE_HASH && (!token_ids || !tid2eid)) return MOE_ERR_INVALID_ARG;
+  const Workspace w = workspace_layout(c);
+  if (workspace_bytes < static_cast<size_t>(w.total)) return MOE_ERR_WORKSPACE;
+  if (c.T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  moe_config rc = c;
+  rc.logits_given = 0;
+  const int R = c.T * c.k;
+  float* logits = at<float>(workspace, w.logits);
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(workspace, w.ids);
+  float* gates = topk_weights_out ? topk_weights_out : at<float>(workspace, w.weights);
+  int32_t* sorted_tok = at<int32_t>(workspace, w.sorted_tok);
+  int32_t* dispatch = at<int32_t>(workspace, w.dispatch);
+  int32_t* offsets = at<int32_t>(workspace, w.offsets);
+  int32_t* groups = at<int32_t>(workspace, w.groups);
+  int32_t* tiles = at<int32_t>(workspace, w.tile_prefix);
+  const int G = c.E + c.n_shared;
+  if ((st = hip_status(launch_router_gemm(rc, hidden, w_router, logit_offset, logits, s)))) return st;
+  if ((st = hip_status(launch_topk(rc, logits, bias, token_ids, tid2eid, ids, gates, s)))) return st;
+  if ((st = hip_status(launch_permute(rc, ids, gates, at<int32_t>(workspace, w.blockcnt),
+                                      at<int32_t>(workspace, w.counts), offsets, sorted_tok,
+                                      at<float>(workspace, w.sorted_w), dispatch, s))))
+    return st;
+  if ((st = hip_status(launch_build_tiles(offsets, c.E, R, R, c.n_shared ? c.T : 0, groups,
+                                          tiles, sorted_tok, s))))
+    return st;
+  ExpertFfnArgs a{};
+  a.hidden = hidden;
+  a.sorted_tok = sorted_tok;
+  a.g_begin = groups;
+  a.g_end = groups + G;
+  a.tile_prefix = tiles;
+  a.n_groups = G;
+  a.rows_bound = R + c.n_shared * c.T;
+  a.routed_groups = c.E;
+  a.w13 = w13;
+  a.w2 = w2;
+  a.w13_last = c.n_shared ? w13_shared : nullptr;
+  a.w2_last = c.n_shared ? w2_shared : nullptr;
+  a.H = at<char>(workspace, w.H);
+  a.Y = at<char>(workspace, w.Y);
+  if ((st = hip_status(launch_expert_up(c, a, s)))) return st;
+  if ((st = hip_status(launch_expert_down(c, a, s)))) return st;
+  const int64_t es = c.dtype == MOE_F32 ? 4 : 2;
+  const char* shared_rows = c.n_shared ? at<char>(workspace, w.Y) + (int64_t)R * c.d * es : nullptr;
+  return hip_status(launch_combine(c, a.Y, dispatch, gates, shared_rows, out, s));
+}
+
+const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

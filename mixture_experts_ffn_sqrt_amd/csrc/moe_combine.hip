@@ -1,0 +1,104 @@
+// Weighted combine ("Mixture of Experts: Router, Token Dispatch, Grouped GEMM",
+// section Token Combine; "MoE 的算量与通信" 二.2 weighted sum plus shared experts;
+// "DeepSeek-V4 MoE" 四, y_A = 0.7 E1(x_A) + 0.3 E5(x_A)):
+//   out[t] = sum_j w[t,j] * Y[dispatch[t,j]]  (+ shared[t])
+// Each token gathers its k dispatch rows in slot order and sums in float32, so
+// the result does not depend on scheduling (no atomics).  One block per token,
+// 16 bytes per thread per step, coalesced along the row.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxK = 16;
+
+template <typename TE>
+struct Vec;  // 16 bytes of TE <-> float lanes
+template <>
+struct Vec<uint16_t> {
+  static constexpr int N = 8;
+  __device__ static void load(const void* p, float* x) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+  __device__ static void store(void* p, const float* x) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16(x[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16(x[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+template <>
+struct Vec<float> {
+  static constexpr int N = 4;
+  __device__ static void load(const void* p, float* x) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  }
+  __device__ static void store(void* p, const float* x) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  }
+};
+
+template <typename TE>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const TE* Y, const int32_t* dispatch,
+                                                           const float* w, const TE* shared,
+                                                           TE* out, int k, int d) {
+  constexpr int V = Vec<TE>::N;
+  const int t = blockIdx.x;
+  int rows[kMaxK];
+  float wt[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    rows[j] = j < k ? dispatch[static_cast<int64_t>(t) * k + j] : -1;
+    wt[j] = j < k ? w[static_cast<int64_t>(t) * k + j] : 0.0f;
+  }
+  for (int c = threadIdx.x * V; c < d; c += kThreads * V) {
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (rows[j] < 0) continue;
+      float x[V];
+      Vec<TE>::load(Y + static_cast<int64_t>(rows[j]) * d + c, x);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] += wt[j] * x[i];
+    }
+    if (shared) {
+      float x[V];
+      Vec<TE>::load(shared + static_cast<int64_t>(t) * d + c, x);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] += x[i];
+    }
+    Vec<TE>::store(out + static_cast<int64_t>(t) * d + c, acc);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const moe_config& c, const void* expert_out, const int32_t* dispatch,
+                          const float* weights, const void* shared_out, void* out,
+                          hipStream_t s) {
+  if (c.dtype == MOE_F32) {
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(c.T), dim3(kThreads), 0, s,
+                       static_cast<const float*>(expert_out), dispatch, weights,
+                       static_cast<const float*>(shared_out), static_cast<float*>(out), c.k, c.d);
+  } else {
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(c.T), dim3(kThreads), 0, s,
+                       static_cast<const uint16_t*>(expert_out), dispatch, weights,
+                       static_cast<const uint16_t*>(shared_out), static_cast<uint16_t*>(out),
+                       c.k, c.d);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,104 @@
+// Internal declarations shared by the HIP sources of the MoE layer library.
+// Nothing here is part of the C ABI (include/moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// scalar helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bfloat16, round to nearest even (finite inputs)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr int64_t align_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// Row-tile heights for which the permutation builds tile lists.  Index i holds
+// the cumulative m-tile count per group for BM = 16 << i.
+constexpr int kNumTileHeights = 5;  // 16, 32, 64, 128, 256
+__host__ __device__ constexpr int tile_height_index(int bm) {
+  return bm == 16 ? 0 : bm == 32 ? 1 : bm == 64 ? 2 : bm == 128 ? 3 : 4;
+}
+
+// pairs handled by one histogram / scatter block of the permutation
+constexpr int kPermuteChunk = 2048;
+
+// ---------------------------------------------------------------------------
+// workspace carve-up (byte offsets from the workspace base), shared by the
+// entry points so that moe_workspace_size is the maximum any of them needs
+// ---------------------------------------------------------------------------
+struct Workspace {
+  int64_t logits, ids, weights;        // [T*E] f32, [T*k] i32, [T*k] f32
+  int64_t blockcnt;                    // [nblk*E] i32
+  int64_t counts, offsets;             // [E] i32, [E+1] i32
+  int64_t groups;                      // [2*G] i32: first rows, then ends
+  int64_t tile_prefix;                 // [kNumTileHeights][G+1] i32
+  int64_t sorted_tok, sorted_w;        // [P] i32, [R] f32
+  int64_t dispatch;                    // [R] i32
+  int64_t H, Y;                        // [P*d_ff], [P*d] elements of the layer dtype
+  int64_t total;
+};
+
+Workspace workspace_layout(const moe_config& c);
+
+// ---------------------------------------------------------------------------
+// launchers (return hipError_t of the launch)
+// ---------------------------------------------------------------------------
+// logits = hidden W_r^T (+ offset); float32 out
+hipError_t launch_router_gemm(const moe_config& c, const void* hidden, const void* w_router,
+                              const float* logit_offset, float* logits, hipStream_t s);
+// scores, selection, gates from logits (learned or hash)
+hipError_t launch_topk(const moe_config& c, const float* logits, const float* bias,
+                       const int32_t* token_ids, const int32_t* tid2eid, int32_t* ids,
+                       float* weights, hipStream_t s);
+// histogram + scan + stable scatter
+hipError_t launch_permute(const moe_config& c, const int32_t* ids, const float* weights,
+                          int32_t* blockcnt, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_tok, float* sorted_w, int32_t* dispatch,
+                          hipStream_t s);
+// Group row ranges and row-tile prefixes from the routed experts' offsets
+// [E+1], clamped to [0, routed_limit].  With shared_rows > 0 the shared expert is group E, rows
+// [shared_begin, shared_begin + shared_rows), and identity token ids are written
+// to sorted_tok[shared_begin ..].  groups = [g_begin[G], g_end[G]].
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int routed_limit, int shared_begin,
+                              int shared_rows, int32_t* groups, int32_t* tile_prefix,
+                              int32_t* sorted_tok, hipStream_t s);
+
+struct ExpertFfnArgs {
+  const void* hidden;          // [T, d]
+  const int32_t* sorted_tok;   // [rows] token of each dispatch row
+  const int32_t* g_begin;      // [G] device: first dispatch row of each group
+  const int32_t* g_end;        // [G] device: one past its last row
+  const int32_t* tile_prefix;  // [kNumTileHeights][G+1] device
+  int n_groups;                // G (routed experts + shared)
+  int rows_bound;              // host bound on the total number of rows (T*(k+S))
+  int routed_groups;           // groups whose weights live in w13/w2 (E)
+  const void* w13;             // [E, 2*d_ff, d]
+  const void* w2;              // [E, d, d_ff]
+  const void* w13_last;        // weights of group E (shared) or nullptr
+  const void* w2_last;
+  void* H;                     // [rows, d_ff] intermediate
+  void* Y;                     // [rows, d] unweighted expert outputs
+};
+// GEMM 1 + SiLU(gate) * up -> H, and GEMM 2 -> Y
+hipError_t launch_expert_up(const moe_config& c, const ExpertFfnArgs& a, hipStream_t s);
+hipError_t launch_expert_down(const moe_config& c, const ExpertFfnArgs& a, hipStream_t s);
+
+hipError_t launch_combine(const moe_config& c, const void* expert_out, const int32_t* dispatch,
+                          const float* weights, const void* shared_out, void* out,
+                          hipStream_t s);
+
+}  // namespace moe

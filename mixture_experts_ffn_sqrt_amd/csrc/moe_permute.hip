@@ -1,0 +1,200 @@
+// Token dispatch ("Mixture of Experts: Router, Token Dispatch, Grouped GEMM",
+// section Token Dispatch; "MoE 的算量与通信" 二.3): the T*k (token, slot) pairs are
+// reordered expert-major with tokens ascending inside each expert, i.e. a stable
+// sort of the pairs by expert id.  Three kernels, no host synchronisation:
+//   1. per-chunk expert histogram in LDS (chunk = kPermuteChunk pairs)
+//   2. one block: per-expert totals, exclusive scan -> offsets, and each chunk's
+//      starting row per expert
+//   3. per chunk, one wavefront walks its pairs in order 64 at a time; lanes with
+//      the same expert are ranked by ballot + popcount, which keeps the order
+// A fourth small kernel turns the offsets into the grouped GEMMs' row ranges and
+// row-tile prefixes (routed experts, then the shared expert as one more group).
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kHistThreads = 256;
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kHistThreads) void hist_kernel(const int32_t* ids, int R, int E,
+                                                            int32_t* blockcnt) {
+  __shared__ int cnt[1024];
+  for (int e = threadIdx.x; e < E; e += kHistThreads) cnt[e] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * kPermuteChunk;
+  const int n = min(kPermuteChunk, R - base);
+  for (int i = threadIdx.x; i < n; i += kHistThreads) {
+    const int e = ids[base + i];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kHistThreads)
+    blockcnt[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
+}
+
+// exclusive prefix sum over the kScanThreads threads of one block
+__device__ int block_exclusive_scan(int v, int* wave_tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wave_tot[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kScanThreads / 64 ? wave_tot[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(w, off);
+      if (lane >= off) w += y;
+    }
+    if (lane < kScanThreads / 64) wave_tot[lane] = w;  // inclusive wave totals
+  }
+  __syncthreads();
+  const int before = wave > 0 ? wave_tot[wave - 1] : 0;
+  __syncthreads();
+  return before + x - v;
+}
+
+// counts, offsets, and blockcnt rewritten in place as each chunk's first row per expert
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* blockcnt, int nblk, int E,
+                                                            int32_t* counts, int32_t* offsets) {
+  __shared__ int wave_tot[kScanThreads / 64];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E)
+    for (int b = 0; b < nblk; ++b) total += blockcnt[static_cast<int64_t>(b) * E + e];
+  const int off = block_exclusive_scan(e < E ? total : 0, wave_tot);
+  if (e < E) {
+    counts[e] = total;
+    offsets[e] = off;
+    if (e == E - 1) offsets[E] = off + total;
+    int run = off;
+    for (int b = 0; b < nblk; ++b) {
+      int32_t* c = blockcnt + static_cast<int64_t>(b) * E + e;
+      const int n = *c;
+      *c = run;
+      run += n;
+    }
+  }
+}
+
+__global__ __launch_bounds__(64) void scatter_kernel(const int32_t* ids, const float* w, int R,
+                                                     int k, int E, const int32_t* blockbase,
+                                                     int32_t* sorted_tok, float* sorted_w,
+                                                     int32_t* dispatch) {
+  __shared__ int base[1024];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64)
+    base[e] = blockbase[static_cast<int64_t>(blockIdx.x) * E + e];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int start = blockIdx.x * kPermuteChunk;
+  const int end = min(start + kPermuteChunk, R);
+  for (int s = start; s < end; s += 64) {
+    const int pidx = s + lane;
+    const bool in = pidx < end;
+    const int e = in ? ids[pidx] : -1;
+    const bool valid = in && e >= 0 && e < E;
+    // lanes holding the same expert id
+    uint64_t m = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 10; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bb = __ballot(bit);
+      m &= bit ? bb : ~bb;
+    }
+    int row = -1;
+    if (valid) {
+      row = base[e] + __popcll(m & below);
+      sorted_tok[row] = pidx / k;
+      sorted_w[row] = w[pidx];
+    }
+    if (in) dispatch[pidx] = row;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (valid && (m >> lane) == 1ull) base[e] += __popcll(m);  // last lane of its expert
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+// Routed rows are clamped to [0, routed_limit] so that caller-given offsets can
+// never send the GEMMs past the dispatch arrays.
+__global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(const int32_t* offsets, int E,
+                                                                   int routed_limit,
+                                                                   int shared_begin,
+                                                                   int shared_rows, int32_t* groups,
+                                                                   int32_t* tile_prefix,
+                                                                   int32_t* sorted_tok) {
+  __shared__ int wave_tot[kScanThreads / 64];
+  __shared__ int pass_total;
+  const int G = E + (shared_rows > 0 ? 1 : 0);
+  int32_t* g_begin = groups;
+  int32_t* g_end = groups + G;
+  // G <= 1025: thread i handles groups i and (for i == 0) the shared group E
+  for (int h = 0; h < kNumTileHeights; ++h) {
+    const int bm = 16 << h;
+    int32_t* tp = tile_prefix + h * (G + 1);
+    int carry = 0;
+    for (int g0 = 0; g0 < G; g0 += kScanThreads) {
+      const int g = g0 + threadIdx.x;
+      int rows = 0, b = 0, en = 0;
+      if (g < E) {
+        b = min(max(offsets[g], 0), routed_limit);
+        en = min(max(offsets[g + 1], b), routed_limit);
+      } else if (g < G) {
+        b = shared_begin;
+        en = shared_begin + shared_rows;
+      }
+      rows = en - b;
+      if (h == 0 && g < G) {
+        g_begin[g] = b;
+        g_end[g] = en;
+      }
+      const int tiles = g < G ? (rows + bm - 1) / bm : 0;
+      const int ex = block_exclusive_scan(tiles, wave_tot);
+      if (g < G) tp[g] = carry + ex;
+      // total of this pass: last thread's exclusive prefix + its own count
+      if (threadIdx.x == kScanThreads - 1) pass_total = ex + tiles;
+      __syncthreads();
+      carry += pass_total;
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) tp[G] = carry;
+  }
+  for (int t = threadIdx.x; t < shared_rows; t += kScanThreads) sorted_tok[shared_begin + t] = t;
+}
+
+}  // namespace
+
+hipError_t launch_permute(const moe_config& c, const int32_t* ids, const float* weights,
+                          int32_t* blockcnt, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_tok, float* sorted_w, int32_t* dispatch,
+                          hipStream_t s) {
+  const int R = c.T * c.k;
+  const int nblk = ceil_div(R, kPermuteChunk);
+  hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(kHistThreads), 0, s, ids, R, c.E, blockcnt);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, blockcnt, nblk, c.E, counts,
+                     offsets);
+  hipLaunchKernelGGL(scatter_kernel, dim3(nblk), dim3(64), 0, s, ids, weights, R, c.k, c.E,
+                     blockcnt, sorted_tok, sorted_w, dispatch);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int routed_limit, int shared_begin,
+                              int shared_rows, int32_t* groups, int32_t* tile_prefix,
+                              int32_t* sorted_tok, hipStream_t s) {
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kScanThreads), 0, s, offsets, E,
+                     routed_limit, shared_begin, shared_rows, groups, tile_prefix, sorted_tok);
+  return hipGetLastError();
+}
+
+}  // namespace moe

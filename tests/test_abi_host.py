@@ -1,0 +1,111 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host before any launch (these
+calls never reach the GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import mixture_experts_ffn_sqrt_amd as moe
+from mixture_experts_ffn_sqrt_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_entry_points():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return sorted(set(re.findall(r"^(?:int|const char \*)\s*(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_abi():
+    assert declared_entry_points() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.load_library()
+    for name in declared_entry_points():
+        assert hasattr(L, name), name
+    assert moe.moe_strerror(0) == "ok"
+    assert "workspace" in moe.moe_strerror(-3)
+
+
+def cfg(**kw):
+    base = dict(T=16, d=64, E=8, k=2, d_ff=128, dtype="f32")
+    base.update(kw)
+    return moe.make_config(**base)
+
+
+def ws_status(c):
+    n = C.c_size_t(0)
+    return moe.load_library().moe_workspace_size(C.byref(c), C.byref(n)), n.value
+
+
+@pytest.mark.parametrize("kw, status", [
+    (dict(), 0),
+    (dict(T=0), 0),
+    (dict(T=-1), -1),
+    (dict(k=9), -1),                       # k > E
+    (dict(k=0), -1),
+    (dict(E=2000, k=2), -2),               # E > 1024
+    (dict(E=32, k=17), -2),                # k > 16
+    (dict(d=96), -2),                      # d not a multiple of 64
+    (dict(d_ff=100), -2),
+    (dict(n_shared=2), -1),
+    (dict(dtype=7), None),                 # make_config rejects unknown dtype names
+    (dict(scoring=5), -1),
+    (dict(route_mode=3), -1),
+    (dict(n_group=3), -1),                 # E % n_group
+    (dict(n_group=4, topk_group=5, group_topk=1), -1),
+    (dict(n_group=4, topk_group=2, group_topk=3), -1),   # group_topk > E/n_group
+    (dict(n_group=4, topk_group=1, group_topk=1, k=3), -1),  # k > topk_group*E/n_group
+    (dict(n_group=4, topk_group=2, group_topk=2, k=4), 0),
+    (dict(route_mode=1, vocab=0), -1),
+    (dict(n_group=0), -1),
+])
+def test_config_validation(kw, status):
+    if status is None:
+        with pytest.raises(KeyError):
+            cfg(**kw)
+        return
+    st, n = ws_status(cfg(**kw))
+    assert st == status
+    if st == 0:
+        assert n > 0
+
+
+def test_workspace_size_covers_buffers():
+    c = cfg(T=100, d=128, E=8, k=2, d_ff=256, n_shared=1, dtype="bf16")
+    _, n = ws_status(c)
+    P = 100 * 3
+    assert n >= P * 128 * 2 + P * 256 * 2 + 100 * 8 * 4
+
+
+def test_null_pointers_rejected_before_launch():
+    L = moe.load_library()
+    c = cfg()
+    z = None
+    bogus = C.c_void_p(0x1000)  # never dereferenced: every call below fails its checks
+    assert L.moe_route(C.byref(c), z, z, z, z, z, z, z, z, z, z) == -1
+    assert L.moe_route(C.byref(c), bogus, z, z, z, z, z, bogus, bogus, bogus, z) == -1
+    hc = cfg(route_mode=1, vocab=10)
+    assert L.moe_route(C.byref(hc), bogus, bogus, z, z, z, z, bogus, bogus, bogus, z) == -1
+    assert L.moe_permute(C.byref(c), z, z, z, z, z, z, z, z, 0, z) == -1
+    assert L.moe_permute(C.byref(c), *([bogus] * 8), 16, z) == -3  # workspace too small
+    assert L.moe_expert_ffn(C.byref(c), z, z, z, z, z, z, z, 0, z) == -1
+    assert L.moe_expert_ffn(C.byref(c), *([bogus] * 7), 16, z) == -3
+    assert L.moe_combine(C.byref(c), z, z, z, z, z, z) == -1
+    args = [bogus] * 2 + [z] * 4 + [bogus] * 2 + [z] * 2 + [bogus] + [z] * 2 + [bogus]
+    assert L.moe_forward(C.byref(c), *args, 16, z) == -3
+    sc = cfg(n_shared=1)
+    assert L.moe_forward(C.byref(sc), *args, 1 << 40, z) == -1  # shared weights missing
+    assert L.moe_forward(None, *args, 1 << 40, z) == -1
+
+
+def test_empty_batch_queues_nothing():
+    L = moe.load_library()
+    c = cfg(T=0)
+    bogus = C.c_void_p(0x1000)
+    assert L.moe_route(C.byref(c), bogus, bogus, None, None, None, None, bogus, bogus, bogus,
+                       None) == 0
+    assert L.moe_combine(C.byref(c), bogus, bogus, bogus, None, bogus, None) == 0
