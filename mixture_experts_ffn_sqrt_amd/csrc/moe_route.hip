@@ -40,9 +40,10 @@ __device__ __forceinline__ float affinity(float l, int scoring) {
   return l;
 }
 
-// float -> uint32 with the same order (finite and infinite values)
+// float -> uint32 with the same order (finite and infinite values); -0 and +0
+// compare equal as floats, so both map to the bits of +0
 __device__ __forceinline__ uint32_t order_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
+  const uint32_t u = (f == 0.0f) ? 0u : __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 

@@ -96,7 +96,8 @@ def check_layer(lc, inp, gpu_out, gpu_ids, gpu_gates, rows, route_mode=O.LEARNED
     g_out = to_f64(gpu_out)[rows]
     tie = (ref["margin"] <= TIE_LAYER) if route_mode == O.LEARNED else np.zeros(len(rows), bool)
     ok = ~tie
-    assert tie.mean() <= max_tie_frac, "too many near-ties: %d of %d" % (tie.sum(), len(rows))
+    assert tie.sum() <= max(2, max_tie_frac * len(rows)), \
+        "too many near-ties: %d of %d" % (tie.sum(), len(rows))
     assert np.array_equal(g_ids[ok], ref["ids"][ok]), "topk_ids differ on non-tie tokens"
     assert np.abs(g_gates[ok] - ref["gates"][ok]).max(initial=0) <= 1e-5
     err = row_rel_err(g_out[ok], ref["out"][ok])
