@@ -1,0 +1,854 @@
+// Grouped GEMM kernel templates (device code) of the MoE layer; instantiated by
+// moe_gemm.hip.  See moe_gemm.hip for what the three contractions are.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace gemm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte chunk
+
+enum Epilogue { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_LOGITS = 2 };
+
+struct GemmArgs {
+  const char* A;              // operand rows (hidden or H)
+  const int32_t* a_rows;      // dispatch row -> A row (nullptr: identity)
+  int64_t lda;                // bytes between A rows
+  const char* B;              // weights of group 0; group g at B + g * b_group
+  const char* B_last;         // weights of the last group when it is not in B (shared expert)
+  int64_t b_group;            // bytes between groups' weights
+  int64_t ldb;                // bytes between weight rows
+  int N;                      // output columns
+  int up_row;                 // SwiGLU: first weight row of the up projection (d_ff)
+  int K;                      // reduction length in elements
+  const int32_t* g_begin;     // [G] first dispatch row of each group (nullptr: dense)
+  const int32_t* g_end;       // [G] one past the last row
+  const int32_t* tile_prefix; // [G+1] cumulative row-tile counts for this tile height
+  int G;
+  int dense_rows;             // dense mode: number of rows
+  int n_tiles;                // column tiles
+  char* C;                    // output rows (indexed by dispatch row)
+  int64_t ldc;                // bytes between output rows
+  const float* col_add;       // EPI_LOGITS: per-column addend (nullable)
+  int chunk_w;                // column tiles per scheduling chunk (tile order)
+  uint32_t a_bytes;           // bytes of the A operand (buffer range; < 2^31)
+  uint32_t b_bytes;           // bytes of one group's weights (buffer range; < 2^31)
+};
+
+// Byte offset of 16-byte chunk `ch` (0..7) of LDS tile row `row`.  The chunk is
+// XOR-swizzled with the row so that the eight consecutive rows an MFMA fragment
+// read touches at one K position fall in eight different bank groups.
+__device__ __forceinline__ int lds_off(int row, int ch) {
+  return (row << 7) + ((ch ^ (row & 7)) << 4);
+}
+
+template <typename TE>
+struct Mma;
+
+template <>
+struct Mma<uint16_t> {  // bfloat16: one 16x16x32 step per 16-byte lane chunk
+  __device__ __forceinline__ static void run(f32x4& c, const u32x4& a, const u32x4& b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mma<float> {  // float32: four 16x16x4 steps; A and B take the same K order
+  __device__ __forceinline__ static void run(f32x4& c, const u32x4& a, const u32x4& b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[0]), __uint_as_float(b[0]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[1]), __uint_as_float(b[1]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[2]), __uint_as_float(b[2]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[3]), __uint_as_float(b[3]), c, 0, 0, 0);
+  }
+};
+
+template <typename TE>
+__device__ __forceinline__ void store_elem(char* p, float v);
+template <>
+__device__ __forceinline__ void store_elem<uint16_t>(char* p, float v) {
+  *reinterpret_cast<uint16_t*>(p) = f32_to_bf16(v);
+}
+template <>
+__device__ __forceinline__ void store_elem<float>(char* p, float v) {
+  *reinterpret_cast<float*>(p) = v;
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct TileCoord {
+  int grp, row0, nrows, nt;
+};
+
+// Which tile this block owns (see grouped_gemm_kernel); false: nothing to do.
+template <int BM>
+__device__ __forceinline__ bool decode_tile(const GemmArgs& p, TileCoord& tc) {
+  const int total_m = p.g_begin ? p.tile_prefix[p.G] : ceil_div(p.dense_rows, BM);
+  const int nact = total_m * p.n_tiles;
+  const int bid = blockIdx.x;
+  if (bid >= nact) return false;
+  // Blocks are handed to the 8 XCDs round-robin (block b -> XCD b % 8): give
+  // each XCD a contiguous run of logical tiles.  Logical order: column tiles
+  // in chunks of chunk_w; inside a chunk, row tiles fastest-outer, so the
+  // blocks running together on one XCD share both weight panels (same
+  // columns) and operand rows (same row tile).
+  const int q8 = nact >> 3, r8 = nact & 7, xcd = bid & 7;
+  const int logical = xcd * q8 + min(xcd, r8) + (bid >> 3);
+  const int per_chunk = total_m * p.chunk_w;
+  const int chunk = logical / per_chunk;
+  const int w = min(p.chunk_w, p.n_tiles - chunk * p.chunk_w);
+  const int rem = logical - chunk * per_chunk;
+  const int mt = rem / w;
+  tc.nt = chunk * p.chunk_w + (rem - mt * w);
+  tc.grp = 0;
+  if (p.g_begin) {
+    int lo = 0, hi = p.G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.tile_prefix[mid] <= mt) lo = mid; else hi = mid - 1;
+    }
+    tc.grp = lo;
+    tc.row0 = p.g_begin[lo] + (mt - p.tile_prefix[lo]) * BM;
+    tc.nrows = min(BM, p.g_end[lo] - tc.row0);
+  } else {
+    tc.row0 = mt * BM;
+    tc.nrows = min(BM, p.dense_rows - tc.row0);
+  }
+  return true;
+}
+
+// BM x BN tile (BN = weight rows; for SwiGLU the first half are gate rows and
+// the second half the matching up rows), WM x WN waves, 128 bytes of K per stage.
+template <typename TE, int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(GemmArgs p) {
+  constexpr int NT = 64 * WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 16, FN = WTN / 16;
+  constexpr bool SW = EPI == EPI_SWIGLU;
+  static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must hold whole fragments");
+  static_assert(!SW || FN % 2 == 0, "SwiGLU waves hold gate and up fragments in pairs");
+  constexpr int LA = ceil_div(BM * 8, NT), LB = ceil_div(BN * 8, NT);
+  // whether every thread owns a chunk in every load slot (no per-thread guard)
+  constexpr bool A_FULL = (BM * 8) % NT == 0, B_FULL = (BN * 8) % NT == 0;
+  constexpr int STAGE = (BM + BN) * 128;
+  extern __shared__ __align__(16) char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  TileCoord tc;
+  if (!decode_tile<BM>(p, tc)) return;
+  const int grp = tc.grp, row0 = tc.row0, nrows = tc.nrows, nt = tc.nt;
+  const char* Bg = (p.B_last && grp == p.G - 1) ? p.B_last : p.B + (int64_t)grp * p.b_group;
+
+  // ---- per-thread global sources and LDS destinations ------------------------
+  // Row slots past the tile's valid rows read the tile's first row: their
+  // results are never stored, and every read stays inside the operand.
+  const char* a_src[LA];
+  int a_dst[LA];
+  bool a_on[LA];
+#pragma unroll
+  for (int c = 0; c < LA; ++c) {
+    const int lin = c * NT + tid, row = lin >> 3, ch = lin & 7;
+    a_on[c] = A_FULL || lin < BM * 8;
+    const int rr = (row < nrows) ? row : 0;
+    const int arow = p.a_rows ? p.a_rows[row0 + rr] : row0 + rr;
+    a_src[c] = p.A + (int64_t)arow * p.lda + ch * 16;
+    a_dst[c] = lds_off(row, ch);
+  }
+  const char* b_src[LB];
+  int b_dst[LB];
+  bool b_on[LB];
+#pragma unroll
+  for (int c = 0; c < LB; ++c) {
+    const int lin = c * NT + tid, row = lin >> 3, ch = lin & 7;
+    b_on[c] = B_FULL || lin < BN * 8;
+    int brow;
+    if (SW) {
+      brow = (row < BN / 2) ? nt * (BN / 2) + row : p.up_row + nt * (BN / 2) + (row - BN / 2);
+    } else {
+      brow = nt * BN + row;
+      if (brow >= p.N) brow = p.N - 1;
+    }
+    b_src[c] = Bg + (int64_t)brow * p.ldb + ch * 16;
+    b_dst[c] = BM * 128 + lds_off(row, ch);
+  }
+
+  const int KT = (p.K * (int)sizeof(TE)) >> 7;
+  u32x4 ra[LA], rb[LB];
+#pragma unroll
+  for (int c = 0; c < LA; ++c)
+    if (a_on[c]) ra[c] = *reinterpret_cast<const u32x4*>(a_src[c]);
+#pragma unroll
+  for (int c = 0; c < LB; ++c)
+    if (b_on[c]) rb[c] = *reinterpret_cast<const u32x4*>(b_src[c]);
+#pragma unroll
+  for (int c = 0; c < LA; ++c)
+    if (a_on[c]) *reinterpret_cast<u32x4*>(smem + a_dst[c]) = ra[c];
+#pragma unroll
+  for (int c = 0; c < LB; ++c)
+    if (b_on[c]) *reinterpret_cast<u32x4*>(smem + b_dst[c]) = rb[c];
+  __syncthreads();
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int f = 0; f < FN; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // LDS rows of this lane's fragments
+  const int frow = lane & 15, fq = lane >> 4;
+  int a_row[FM], b_row[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) a_row[i] = wm * WTM + 16 * i + frow;
+#pragma unroll
+  for (int f = 0; f < FN; ++f) {
+    if (SW)
+      b_row[f] = (f < FN / 2) ? wn * (WTN / 2) + 16 * f : BN / 2 + wn * (WTN / 2) + 16 * (f - FN / 2);
+    else
+      b_row[f] = wn * WTN + 16 * f;
+    b_row[f] += frow;
+  }
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const char* cur = smem + (kt & 1) * STAGE;
+    const bool more = kt + 1 < KT;
+    if (more) {
+      const int off = (kt + 1) << 7;
+#pragma unroll
+      for (int c = 0; c < LA; ++c)
+        if (a_on[c]) ra[c] = *reinterpret_cast<const u32x4*>(a_src[c] + off);
+#pragma unroll
+      for (int c = 0; c < LB; ++c)
+        if (b_on[c]) rb[c] = *reinterpret_cast<const u32x4*>(b_src[c] + off);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int ch = kk * 4 + fq;
+      u32x4 fa[FM], fb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        fa[i] = *reinterpret_cast<const u32x4*>(cur + lds_off(a_row[i], ch));
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
+        fb[f] = *reinterpret_cast<const u32x4*>(cur + BM * 128 + lds_off(b_row[f], ch));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int f = 0; f < FN; ++f) Mma<TE>::run(acc[i][f], fa[i], fb[f]);
+    }
+    if (more) {
+      char* nxt = smem + ((kt + 1) & 1) * STAGE;
+#pragma unroll
+      for (int c = 0; c < LA; ++c)
+        if (a_on[c]) *reinterpret_cast<u32x4*>(nxt + a_dst[c]) = ra[c];
+#pragma unroll
+      for (int c = 0; c < LB; ++c)
+        if (b_on[c]) *reinterpret_cast<u32x4*>(nxt + b_dst[c]) = rb[c];
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds C[4*(lane/16) + r][lane % 16] of each fragment ----
+  const int ccol = lane & 15, crow = (lane >> 4) * 4;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int lr = wm * WTM + 16 * i + crow + r;
+      if (lr >= nrows) continue;
+      char* crow_ptr = p.C + (int64_t)(row0 + lr) * p.ldc;
+      if (SW) {
+#pragma unroll
+        for (int f = 0; f < FN / 2; ++f) {
+          const float g = acc[i][f][r], u = acc[i][f + FN / 2][r];
+          const float h = g / (1.0f + expf(-g)) * u;
+          const int col = nt * (BN / 2) + wn * (WTN / 2) + 16 * f + ccol;
+          store_elem<TE>(crow_ptr + (int64_t)col * sizeof(TE), h);
+        }
+      } else {
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          const int col = nt * BN + wn * WTN + 16 * f + ccol;
+          if (col >= p.N) continue;
+          if (EPI == EPI_LOGITS) {
+            const float v = acc[i][f][r] + (p.col_add ? p.col_add[col] : 0.0f);
+            reinterpret_cast<float*>(crow_ptr)[col] = v;
+          } else {
+            store_elem<TE>(crow_ptr + (int64_t)col * sizeof(TE), acc[i][f][r]);
+          }
+        }
+      }
+    }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Large-tile bf16 variant: MFMA 32x32x16, wave tiles of 32*FM x 32*FN, the
+// operand bases kept uniform (scalar registers) and per-lane 32-bit offsets,
+// fragments for the next K step read from LDS while the current step's MFMAs
+// run.  Same tile bookkeeping, swizzle and epilogue semantics as above.
+// Requires every A operand to span less than 4 GiB (checked by the launcher).
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int EPI, int MINB>
+__global__ __launch_bounds__(64 * WM * WN, MINB) void grouped_gemm_v2(GemmArgs p) {
+  constexpr int NT = 64 * WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr bool SW = EPI == EPI_SWIGLU;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must hold whole 32x32 fragments");
+  static_assert(!SW || FN % 2 == 0, "SwiGLU waves hold gate and up fragments in pairs");
+  static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "loads must split evenly");
+  static_assert(!SW || ((BN / 2) % (NT / 8)) == 0, "a load slot is all gate or all up rows");
+  constexpr int LA = BM * 8 / NT, LB = BN * 8 / NT;
+  constexpr int RPS = NT / 8;  // rows covered by one load slot
+  constexpr int STAGE = (BM + BN) * 128;
+  extern __shared__ __align__(16) char smem[];
+
+  TileCoord tc;
+  if (!decode_tile<BM>(p, tc)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const char* Bg = (p.B_last && tc.grp == p.G - 1) ? p.B_last : p.B + (int64_t)tc.grp * p.b_group;
+
+  // Buffer loads: a scalar resource per operand, per-lane 32-bit offsets that
+  // stay fixed, and the K position in the scalar offset.  Rows outside the
+  // tile (and weight rows past N) get an offset beyond the resource's range,
+  // which the hardware returns as zeros.
+  constexpr uint32_t kOut = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t a_rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.A), 0, (int)p.a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t b_rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Bg), 0, (int)p.b_bytes, 0x00020000);
+  const int lrow = tid >> 3, lch = tid & 7;
+  uint32_t a_off[LA];
+#pragma unroll
+  for (int c = 0; c < LA; ++c) {
+    const int row = c * RPS + lrow;
+    if (row < tc.nrows) {
+      const int arow = p.a_rows ? p.a_rows[tc.row0 + row] : tc.row0 + row;
+      a_off[c] = (uint32_t)arow * (uint32_t)p.lda + lch * 16;
+    } else {
+      a_off[c] = kOut;
+    }
+  }
+  uint32_t b_off[LB];
+#pragma unroll
+  for (int c = 0; c < LB; ++c) {
+    const int row = c * RPS + lrow;
+    int brow;
+    if (SW) {
+      brow = (c * RPS < BN / 2) ? tc.nt * (BN / 2) + row
+                                : p.up_row + tc.nt * (BN / 2) + (row - BN / 2);
+    } else {
+      brow = tc.nt * BN + row;
+    }
+    b_off[c] = (SW || brow < p.N) ? (uint32_t)brow * (uint32_t)p.ldb + lch * 16 : kOut;
+  }
+  const int st_a = lds_off(lrow, lch);  // + c * RPS * 128 (RPS is a multiple of 8)
+  const int st_b = BM * 128 + lds_off(lrow, lch);
+
+  const int KT = p.K >> 6;  // 64 bf16 per stage
+  u32x4 ra[LA], rb[LB];
+  auto gload = [&](int kt) {
+    const int ko = kt * 128;
+#pragma unroll
+    for (int c = 0; c < LA; ++c) ra[c] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_off[c], ko, 0);
+#pragma unroll
+    for (int c = 0; c < LB; ++c) rb[c] = __builtin_amdgcn_raw_buffer_load_b128(b_rs, b_off[c], ko, 0);
+  };
+  auto lstore = [&](char* buf) {
+#pragma unroll
+    for (int c = 0; c < LA; ++c) *reinterpret_cast<u32x4*>(buf + st_a + c * RPS * 128) = ra[c];
+#pragma unroll
+    for (int c = 0; c < LB; ++c) *reinterpret_cast<u32x4*>(buf + st_b + c * RPS * 128) = rb[c];
+  };
+
+  gload(0);
+  lstore(smem);
+  __syncthreads();
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
+
+  // LDS read offsets: row (lane & 31) of each fragment, 16-byte chunk
+  // 2*kk + (lane >> 5) of the 128-byte row, swizzled by row & 7 == lane & 7
+  const int fr = lane & 31, fh = lane >> 5, fx = lane & 7;
+  int a_rd[4], b_rd[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int sw = ((2 * kk + fh) ^ fx) << 4;
+    a_rd[kk] = (wm * WTM + fr) * 128 + sw;
+    b_rd[kk] = BM * 128 + fr * 128 + sw;
+  }
+  int b_row[FN];
+#pragma unroll
+  for (int f = 0; f < FN; ++f)
+    b_row[f] = SW ? ((f < FN / 2) ? wn * (WTN / 2) + 32 * f : BN / 2 + wn * (WTN / 2) + 32 * (f - FN / 2))
+                  : wn * WTN + 32 * f;
+
+  u32x4 fa[2][FM], fb[2][FN];
+  auto fload = [&](const char* buf, int kk, int slot) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[slot][i] = *reinterpret_cast<const u32x4*>(buf + a_rd[kk] + i * 32 * 128);
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+      fb[slot][f] = *reinterpret_cast<const u32x4*>(buf + b_rd[kk] + b_row[f] * 128);
+  };
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const char* cur = smem + (kt & 1) * STAGE;
+    const bool more = kt + 1 < KT;
+    if (more) gload(kt + 1);
+    fload(cur, 0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk + 1 < 4) fload(cur, kk + 1, (kk + 1) & 1);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+          acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, fa[kk & 1][i]), __builtin_bit_cast(bf16x8, fb[kk & 1][f]),
+              acc[i][f], 0, 0, 0);
+    }
+    if (more) lstore(smem + ((kt + 1) & 1) * STAGE);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds C[8*(r/4) + 4*(lane/32) + r%4][lane % 32] of each fragment
+  const int ccol = lane & 31, crow = (lane >> 5) * 4;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int lr = wm * WTM + 32 * i + 8 * (r >> 2) + crow + (r & 3);
+      if (lr >= tc.nrows) continue;
+      char* crow_ptr = p.C + (int64_t)(tc.row0 + lr) * p.ldc;
+      if (SW) {
+#pragma unroll
+        for (int f = 0; f < FN / 2; ++f) {
+          const float g = acc[i][f][r], u = acc[i][f + FN / 2][r];
+          const float h = g / (1.0f + expf(-g)) * u;
+          const int col = tc.nt * (BN / 2) + wn * (WTN / 2) + 32 * f + ccol;
+          *reinterpret_cast<uint16_t*>(crow_ptr + (int64_t)col * 2) = f32_to_bf16(h);
+        }
+      } else {
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          const int col = tc.nt * BN + wn * WTN + 32 * f + ccol;
+          if (col >= p.N) continue;
+          if (EPI == EPI_LOGITS) {
+            reinterpret_cast<float*>(crow_ptr)[col] =
+                acc[i][f][r] + (p.col_add ? p.col_add[col] : 0.0f);
+          } else {
+            *reinterpret_cast<uint16_t*>(crow_ptr + (int64_t)col * 2) = f32_to_bf16(acc[i][f][r]);
+          }
+        }
+      }
+    }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Deep-pipelined bf16 variant: direct global->LDS buffer loads (16 bytes per
+// lane; a wavefront's load fills 1 KB of LDS, lane l at byte 16*l), STAGES LDS
+// buffers of 32 K-elements (64 bytes per row), loads issued STAGES-1 stages
+// ahead, one barrier per stage, MFMA 32x32x16.
+//
+// LDS row layout: row r holds four 16-byte chunks; chunk c sits in slot
+// c ^ swz(r), swz(r) = ((r >> 1) ^ (r >> 3)) & 3, so that the 8 or 16 rows one
+// MFMA fragment read touches at one K position use distinct bank groups.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz64(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wavefront are outstanding (vmcnt in bits [3:0] and [15:14]; expcnt and
+// lgkmcnt left at their no-wait maxima)
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// one 16-byte-per-lane buffer load straight into LDS at `dst` (+16 * lane)
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, char* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)dst, 16, voff, 0, 0, 0);
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES, bool SKIP = true>
+__global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_v3(GemmArgs p) {
+  constexpr int NT = 64 * WM * WN, NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr bool SW = EPI == EPI_SWIGLU;
+  constexpr int ROWB = 64;                          // bytes of K per row per stage
+  constexpr int STAGE = (BM + BN) * ROWB;
+  constexpr int LA = BM / 16 / NW, LB = BN / 16 / NW;  // 1 KB loads per wave per stage
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "whole 32x32 fragments");
+  static_assert(!SW || FN % 2 == 0, "SwiGLU waves hold gate and up fragments in pairs");
+  static_assert(LA * NW * 16 == BM && LB * NW * 16 == BN, "loads must split evenly");
+  static_assert(!SW || (BN / 2) % 16 == 0, "a 16-row load is all gate or all up rows");
+  static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024, "LDS budget");
+  extern __shared__ __align__(16) char smem[];
+
+  TileCoord tc;
+  if (!decode_tile<BM>(p, tc)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const char* Bg = (p.B_last && tc.grp == p.G - 1) ? p.B_last : p.B + (int64_t)tc.grp * p.b_group;
+  constexpr uint32_t kOut = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t a_rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.A), 0, (int)p.a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t b_rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Bg), 0, (int)p.b_bytes, 0x00020000);
+
+  // Load slot j of this wave covers tile rows [16 * (wave + NW * j), +16); lane l
+  // fills LDS slot l % 4 of row l / 4, i.e. logical chunk (l % 4) ^ swz(row).
+  const int lr = lane >> 2, lq = lane & 3;
+  uint32_t a_off[LA], b_off[LB];
+#pragma unroll
+  for (int j = 0; j < LA; ++j) {
+    const int row = 16 * (wave + NW * j) + lr;
+    const int ch = lq ^ swz64(row);
+    if (row < tc.nrows) {
+      const int arow = p.a_rows ? p.a_rows[tc.row0 + row] : tc.row0 + row;
+      a_off[j] = (uint32_t)arow * (uint32_t)p.lda + ch * 16;
+    } else {
+      a_off[j] = kOut;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < LB; ++j) {
+    const int row = 16 * (wave + NW * j) + lr;
+    const int ch = lq ^ swz64(row);
+    int brow;
+    bool ok = true;
+    if (SW) {
+      brow = (16 * (wave + NW * j) < BN / 2) ? tc.nt * (BN / 2) + row
+                                             : p.up_row + tc.nt * (BN / 2) + (row - BN / 2);
+    } else {
+      brow = tc.nt * BN + row;
+      ok = brow < p.N;
+    }
+    b_off[j] = ok ? (uint32_t)brow * (uint32_t)p.ldb + ch * 16 : kOut;
+  }
+  const int KT = p.K >> 5;  // 32 bf16 per stage
+  // Stage kt's loads; stages past the end reload the last one (never read;
+  // keeps the number of loads in flight constant).
+#define MOE_V3_ISSUE(kt_)                                                                \
+  do {                                                                                   \
+    const int kc_ = (kt_) < KT ? (kt_) : KT - 1;                                         \
+    char* buf_ = smem + ((kt_) % STAGES) * STAGE;                                        \
+    const uint32_t ko_ = (uint32_t)kc_ * ROWB;                                           \
+    _Pragma("unroll") for (int j = 0; j < LA; ++j)                                        \
+        load_lds16(a_rs, buf_ + (16 * (wave + NW * j)) * ROWB, a_off[j] + ko_);          \
+    _Pragma("unroll") for (int j = 0; j < LB; ++j)                                        \
+        load_lds16(b_rs, buf_ + BM * ROWB + (16 * (wave + NW * j)) * ROWB, b_off[j] + ko_); \
+  } while (0)
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
+
+  // fragment read offsets: row lane % 32 of each fragment, chunk 2*kk + lane/32
+  const int fr = lane & 31, fh = lane >> 5, fs = swz64(fr);
+  int a_rd[2], b_rd[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int sl = ((2 * kk + fh) ^ fs) << 4;
+    a_rd[kk] = (wm * WTM + fr) * ROWB + sl;
+    b_rd[kk] = BM * ROWB + fr * ROWB + sl;
+  }
+  int b_row[FN];
+#pragma unroll
+  for (int f = 0; f < FN; ++f)
+    b_row[f] = SW ? ((f < FN / 2) ? wn * (WTN / 2) + 32 * f : BN / 2 + wn * (WTN / 2) + 32 * (f - FN / 2))
+                  : wn * WTN + 32 * f;
+
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) MOE_V3_ISSUE(s);
+
+  for (int kt = 0; kt < KT; ++kt) {
+    // this wave's loads of stage kt are done when at most (STAGES-2) stages'
+    // worth of later loads are still in flight; the barrier then publishes
+    // every wave's loads and retires every wave's reads of stage kt-1
+    static_assert((STAGES - 2) * (LA + LB) <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * (LA + LB)));
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
+    __builtin_amdgcn_s_barrier();
+    MOE_V3_ISSUE(kt + STAGES - 1);
+    const char* cur = smem + (kt % STAGES) * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 fa[FM], fb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        fa[i] = *reinterpret_cast<const u32x4*>(cur + a_rd[kk] + i * 32 * ROWB);
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
+        fb[f] = *reinterpret_cast<const u32x4*>(cur + b_rd[kk] + b_row[f] * ROWB);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        // a fragment whose 32 rows all lie past the tile's valid rows would
+        // only produce discarded results (the row count is uniform per block)
+        if (SKIP && wm * WTM + 32 * i >= tc.nrows) continue;
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+          acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, fa[i]), __builtin_bit_cast(bf16x8, fb[f]), acc[i][f],
+              0, 0, 0);
+      }
+    }
+  }
+#undef MOE_V3_ISSUE
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no LDS load may still be in flight at exit
+
+  // epilogue: lane holds C[8*(r/4) + 4*(lane/32) + r%4][lane % 32] of each fragment
+  const int ccol = lane & 31, crow = (lane >> 5) * 4;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int lrw = wm * WTM + 32 * i + 8 * (r >> 2) + crow + (r & 3);
+      if (lrw >= tc.nrows) continue;
+      char* crow_ptr = p.C + (int64_t)(tc.row0 + lrw) * p.ldc;
+      if (SW) {
+#pragma unroll
+        for (int f = 0; f < FN / 2; ++f) {
+          const float g = acc[i][f][r], u = acc[i][f + FN / 2][r];
+          const float h = g / (1.0f + expf(-g)) * u;
+          const int col = tc.nt * (BN / 2) + wn * (WTN / 2) + 32 * f + ccol;
+          *reinterpret_cast<uint16_t*>(crow_ptr + (int64_t)col * 2) = f32_to_bf16(h);
+        }
+      } else {
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          const int col = tc.nt * BN + wn * WTN + 32 * f + ccol;
+          if (col >= p.N) continue;
+          if (EPI == EPI_LOGITS) {
+            reinterpret_cast<float*>(crow_ptr)[col] =
+                acc[i][f][r] + (p.col_add ? p.col_add[col] : 0.0f);
+          } else {
+            *reinterpret_cast<uint16_t*>(crow_ptr + (int64_t)col * 2) = f32_to_bf16(acc[i][f][r]);
+          }
+        }
+      }
+    }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Software-pipelined bf16 variant.  Per stage: KSTEPS MFMA k-steps of 16 bf16
+// (ROWB = 32*KSTEPS bytes of K per row), STAGES LDS buffers filled by direct
+// global->LDS loads issued STAGES-1 stages ahead.  Fragments are double
+// buffered in registers: the reads of k-step kk+1 are interleaved with the
+// MFMAs of k-step kk, and the barrier that publishes the next stage sits in
+// the middle of the current stage's last k-step, so the MFMA pipe keeps
+// working across it.
+// ---------------------------------------------------------------------------
+template <int ROWB>
+__device__ __forceinline__ int swz_row(int r) {
+  if constexpr (ROWB == 128) return r & 7;
+  else return swz64(r);
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int KSTEPS>
+__global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_v4(GemmArgs p) {
+  constexpr int NT = 64 * WM * WN, NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr bool SW = EPI == EPI_SWIGLU;
+  constexpr int ROWB = 32 * KSTEPS;        // bytes of K per row per stage
+  constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
+  constexpr int RPL = 1024 / ROWB;         // rows filled by one wavefront load
+  constexpr int STAGE = (BM + BN) * ROWB;
+  constexpr int LA = BM / RPL / NW, LB = BN / RPL / NW;
+  constexpr int PEND = (STAGES - 2) * (LA + LB);  // loads allowed in flight at a stage switch
+  static_assert(KSTEPS == 2 || KSTEPS == 4, "64- or 128-byte rows");
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "whole 32x32 fragments");
+  static_assert(!SW || FN % 2 == 0, "SwiGLU waves hold gate and up fragments in pairs");
+  static_assert(LA * NW * RPL == BM && LB * NW * RPL == BN, "loads must split evenly");
+  static_assert(!SW || (BN / 2) % RPL == 0, "a load is all gate or all up rows");
+  static_assert(STAGES >= 3 && STAGES * STAGE <= 160 * 1024, "LDS budget");
+  static_assert(PEND <= 63, "vmcnt range");
+  extern __shared__ __align__(16) char smem[];
+
+  TileCoord tc;
+  if (!decode_tile<BM>(p, tc)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const char* Bg = (p.B_last && tc.grp == p.G - 1) ? p.B_last : p.B + (int64_t)tc.grp * p.b_group;
+  constexpr uint32_t kOut = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t a_rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.A), 0, (int)p.a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t b_rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Bg), 0, (int)p.b_bytes, 0x00020000);
+
+  // load j of this wave fills tile rows [RPL * (wave + NW * j), +RPL); lane l
+  // fills LDS slot l % CPR of row l / CPR, i.e. logical chunk slot ^ swz(row)
+  const int lr = lane / CPR, lq = lane % CPR;
+  uint32_t a_off[LA], b_off[LB];
+#pragma unroll
+  for (int j = 0; j < LA; ++j) {
+    const int row = RPL * (wave + NW * j) + lr;
+    const int ch = lq ^ swz_row<ROWB>(row);
+    if (row < tc.nrows) {
+      const int arow = p.a_rows ? p.a_rows[tc.row0 + row] : tc.row0 + row;
+      a_off[j] = (uint32_t)arow * (uint32_t)p.lda + ch * 16;
+    } else {
+      a_off[j] = kOut;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < LB; ++j) {
+    const int row = RPL * (wave + NW * j) + lr;
+    const int ch = lq ^ swz_row<ROWB>(row);
+    int brow;
+    bool ok = true;
+    if (SW) {
+      brow = (RPL * (wave + NW * j) < BN / 2) ? tc.nt * (BN / 2) + row
+                                              : p.up_row + tc.nt * (BN / 2) + (row - BN / 2);
+    } else {
+      brow = tc.nt * BN + row;
+      ok = brow < p.N;
+    }
+    b_off[j] = ok ? (uint32_t)brow * (uint32_t)p.ldb + ch * 16 : kOut;
+  }
+  const int KT = p.K / (ROWB / 2);
+#define MOE_V4_ISSUE(kt_)                                                                 \
+  do {                                                                                    \
+    const int kc_ = (kt_) < KT ? (kt_) : KT - 1;                                          \
+    char* buf_ = smem + ((kt_) % STAGES) * STAGE;                                         \
+    const uint32_t ko_ = (uint32_t)kc_ * ROWB;                                            \
+    _Pragma("unroll") for (int j = 0; j < LA; ++j)                                         \
+        load_lds16(a_rs, buf_ + (RPL * (wave + NW * j)) * ROWB, a_off[j] + ko_);          \
+    _Pragma("unroll") for (int j = 0; j < LB; ++j)                                         \
+        load_lds16(b_rs, buf_ + BM * ROWB + (RPL * (wave + NW * j)) * ROWB, b_off[j] + ko_); \
+  } while (0)
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
+
+  const int fr = lane & 31, fh = lane >> 5, fs = swz_row<ROWB>(fr);
+  int rd[KSTEPS];  // byte offset of this lane's chunk for k-step kk within a fragment row block
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) rd[kk] = fr * ROWB + (((2 * kk + fh) ^ fs) << 4);
+  int b_row[FN];
+#pragma unroll
+  for (int f = 0; f < FN; ++f)
+    b_row[f] = SW ? ((f < FN / 2) ? wn * (WTN / 2) + 32 * f : BN / 2 + wn * (WTN / 2) + 32 * (f - FN / 2))
+                  : wn * WTN + 32 * f;
+
+  u32x4 fa[2][FM], fb[2][FN];
+#define MOE_V4_READ(buf_, kk_, sl_)                                                        \
+  do {                                                                                     \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i) fa[sl_][i] =                             \
+        *reinterpret_cast<const u32x4*>((buf_) + (wm * WTM + 32 * i) * ROWB + rd[kk_]);    \
+    _Pragma("unroll") for (int f = 0; f < FN; ++f) fb[sl_][f] =                             \
+        *reinterpret_cast<const u32x4*>((buf_) + BM * ROWB + b_row[f] * ROWB + rd[kk_]);   \
+  } while (0)
+#define MOE_V4_MFMA(sl_, i0_, i1_)                                                         \
+  _Pragma("unroll") for (int i = (i0_); i < (i1_); ++i)                                     \
+  _Pragma("unroll") for (int f = 0; f < FN; ++f)                                            \
+    acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[sl_][i]), \
+                                                       __builtin_bit_cast(bf16x8, fb[sl_][f]), \
+                                                       acc[i][f], 0, 0, 0)
+
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) MOE_V4_ISSUE(s);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(PEND));
+  __builtin_amdgcn_s_barrier();
+  MOE_V4_READ(smem, 0, 0);
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const char* cur = smem + (kt % STAGES) * STAGE;
+    const char* nxt = smem + ((kt + 1) % STAGES) * STAGE;
+    // the buffer being refilled held stage kt-1: every wave finished reading it
+    // before the barrier that published stage kt
+    MOE_V4_ISSUE(kt + STAGES - 1);
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const int sl = kk & 1;
+      if (kk + 1 < KSTEPS) {
+        MOE_V4_READ(cur, kk + 1, sl ^ 1);
+        MOE_V4_MFMA(sl, 0, FM);
+#pragma unroll
+        for (int q = 0; q < FM + FN; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+      } else {
+        MOE_V4_MFMA(sl, 0, FM / 2);
+        __builtin_amdgcn_sched_barrier(0);
+        // stage kt+1: this wave's loads landed (at most PEND newer ones in
+        // flight), this wave's reads of stage kt returned; the barrier makes
+        // both true for every wave
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(PEND) & 0xC0FF);  // vmcnt(PEND) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + 1 < KT) MOE_V4_READ(nxt, 0, sl ^ 1);
+        MOE_V4_MFMA(sl, FM / 2, FM);
+      }
+    }
+  }
+#undef MOE_V4_ISSUE
+#undef MOE_V4_READ
+#undef MOE_V4_MFMA
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no LDS load may still be in flight at exit
+
+  const int ccol = lane & 31, crow = (lane >> 5) * 4;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int lrw = wm * WTM + 32 * i + 8 * (r >> 2) + crow + (r & 3);
+      if (lrw >= tc.nrows) continue;
+      char* crow_ptr = p.C + (int64_t)(tc.row0 + lrw) * p.ldc;
+      if (SW) {
+#pragma unroll
+        for (int f = 0; f < FN / 2; ++f) {
+          const float g = acc[i][f][r], u = acc[i][f + FN / 2][r];
+          const float h = g / (1.0f + expf(-g)) * u;
+          const int col = tc.nt * (BN / 2) + wn * (WTN / 2) + 32 * f + ccol;
+          *reinterpret_cast<uint16_t*>(crow_ptr + (int64_t)col * 2) = f32_to_bf16(h);
+        }
+      } else {
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          const int col = tc.nt * BN + wn * WTN + 32 * f + ccol;
+          if (col >= p.N) continue;
+          if (EPI == EPI_LOGITS) {
+            reinterpret_cast<float*>(crow_ptr)[col] =
+                acc[i][f][r] + (p.col_add ? p.col_add[col] : 0.0f);
+          } else {
+            *reinterpret_cast<uint16_t*>(crow_ptr + (int64_t)col * 2) = f32_to_bf16(acc[i][f][r]);
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace gemm
+}  // namespace moe

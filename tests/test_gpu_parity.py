@@ -221,6 +221,8 @@ def test_permute_random(T, k, E, mode):
     ("bf16", 40, 256, 64, 6, 128),     # ~4 rows/expert: skinny tiles
     ("bf16", 1, 512, 16, 4, 256),      # single token
     ("bf16", 700, 128, 3, 3, 64),      # k = E: every expert gets every token
+    ("bf16", 700, 320, 4, 2, 256),     # 256x256 tiles: ragged rows, partial last column tile
+    ("bf16", 2000, 512, 8, 2, 384),    # 256x256 tiles, several row tiles per expert
 ])
 def test_expert_ffn_and_combine(dtype, T, d, E, k, d_ff):
     lc = CONFIGS["tiny_fp32"].with_(T=T, d=d, E=E, k=k, d_ff=d_ff, dtype=dtype, seed=23)
@@ -283,6 +285,8 @@ SMALL_LAYERS = {
                                                        bias_std=0.01, E=16, k=3),
     "grouped_square_tiles": CONFIGS["dsv3_prefill"].with_(T=1024, d=256, E=16, k=4, d_ff=128,
                                                           n_group=4, topk_group=2, group_topk=2),
+    "v4pro_skew_square_tiles": CONFIGS["v4pro_skew_prefill"].with_(T=2048, d=256, E=16, k=4,
+                                                                   d_ff=256),
     "single_dense_expert": CONFIGS["mixtral_prefill"].with_(T=130, d=256, E=1, k=1, d_ff=128),
     "decode_T1": CONFIGS["v4flash_decode"].with_(T=1, d=256, d_ff=128),
 }
