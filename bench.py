@@ -35,7 +35,39 @@ def parse():
     ap.add_argument("--all", action="store_true", help="also time the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the workload, copy 1 GiB three times (counter calibration)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the vendor-library bf16 GEMM and copy reference points")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = ("mixture_experts_ffn_sqrt_amd/csrc/moe_gemm_kernels.h",
+                  "mixture_experts_ffn_sqrt_amd/csrc/moe_gemm.hip")
+
+
+def kernel_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (profiles/traffic.json), or None when it is absent or was taken on
+    different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tab = json.load(f)
+    ent = tab.get(workload)
+    if not ent or ent.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return int(ent["fetch_bytes_per_launch"] + ent["write_bytes_per_launch"])
 
 
 def accounting(lc, counts):
@@ -135,7 +167,8 @@ def run_workload(name, steps, warmup, with_cpu, cpu_seconds):
         peak = PEAK_TFLOPS[lc.dtype]
         roof = dict(bound="mfma", achieved=round(ach, 1), peak=peak, unit="TFLOP/s",
                     frac=round(ach / peak, 4), traffic=None)
-    roof["kernel"] = "grouped_gemm_kernel (GEMM 1 + SwiGLU, routed rows)"
+    roof["traffic"] = measured_traffic(name)
+    roof["kernel"] = "grouped GEMM 1 + SwiGLU (moe_expert_up, routed rows)"
     roof["kernel_ms"] = round(ms_up, 4)
     gemm_tflops = 6 * lc.d * lc.d_ff * T * k / ((ms_up + ms_down) * 1e-3) / 1e12
     res = dict(
@@ -157,6 +190,38 @@ def run_workload(name, steps, warmup, with_cpu, cpu_seconds):
     del layer, inp, H, Y, perm
     torch.cuda.empty_cache()
     return res
+
+
+def peaks():
+    """Reference points on random N(0,1) bf16 data: the vendor BLAS (torch.mm ->
+    hipBLASLt) on an 8192^3 GEMM, and a device-to-device copy."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    n = 8192
+    a = torch.randn((n, n), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    b = torch.randn((n, n), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    ms, _ = time_gpu(lambda: torch.mm(a, b), 10, 3, torch.cuda.current_stream())
+    gemm = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    del a, b
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms, _ = time_gpu(lambda: dst.copy_(src), 10, 3, torch.cuda.current_stream())
+    copy = 2 * (1 << 30) / (ms * 1e-3) / 1e9
+    return dict(vendor_bf16_gemm_8192_tflops=round(gemm, 1),
+                vendor_bf16_gemm_frac_of_spec=round(gemm / PEAK_TFLOPS["bf16"], 4),
+                copy_1gib_gbs_read_plus_write=round(copy, 1))
+
+
+def calibrate_copy():
+    """A plain copy of known size for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("[bench] calibration copy: 3 x %d bytes" % (1 << 30), file=sys.stderr, flush=True)
 
 
 def cpu_baseline(lc, inp, seconds):
@@ -242,6 +307,10 @@ def main():
             others[name] = {kk: r[kk] for kk in ("ms_per_step", "tokens_per_s", "roofline",
                                                   "grouped_gemm", "layer", "routing")}
         line["workloads"] = others
+    if not args.no_peaks:
+        line["context"] = peaks()
+    if args.calibrate_copy:
+        calibrate_copy()
     print(json.dumps(line), flush=True)
 
 
