@@ -485,25 +485,46 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, char* dst,
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)dst, 16, voff, 0, 0, 0);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int STAGES, bool SKIP = true>
+// Swizzle of the 16-byte chunks of an LDS row, from the row index modulo 32:
+// SWZ 0 = none, 1 = (r>>1 ^ r>>3), 2 = r, 3 = r>>1, 4 = r>>2 (masked to the
+// chunk count).
+template <int ROWB, int SWZ>
+__device__ __forceinline__ int swz_sel(int r) {
+  constexpr int M = ROWB / 16 - 1;
+  r &= 31;  // fragment reads see the row modulo 32: the writes must agree
+  if constexpr (SWZ == 0) return 0;
+  else if constexpr (SWZ == 1) return ((r >> 1) ^ (r >> 3)) & M;
+  else if constexpr (SWZ == 2) return r & M;
+  else if constexpr (SWZ == 3) return (r >> 1) & M;
+  else return (r >> 2) & M;
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES, bool SKIP = true, int ROWB = 64,
+          int SWZ = 1>
 __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_v3(GemmArgs p) {
   constexpr int NT = 64 * WM * WN, NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr bool SW = EPI == EPI_SWIGLU;
-  constexpr int ROWB = 64;                          // bytes of K per row per stage
+  constexpr int KSTEPS = ROWB / 32;                 // MFMA k-steps of 16 bf16 per stage
+  constexpr int CPR = ROWB / 16;                    // 16-byte chunks per row
+  constexpr int RPL = 1024 / ROWB;                  // rows filled by one wavefront load
   constexpr int STAGE = (BM + BN) * ROWB;
-  constexpr int LA = BM / 16 / NW, LB = BN / 16 / NW;  // 1 KB loads per wave per stage
+  constexpr int LA = BM / RPL / NW, LB = BN / RPL / NW;  // 1 KB loads per wave per stage
+  static_assert(ROWB == 64 || ROWB == 128, "64- or 128-byte LDS rows");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "whole 32x32 fragments");
   static_assert(!SW || FN % 2 == 0, "SwiGLU waves hold gate and up fragments in pairs");
-  static_assert(LA * NW * 16 == BM && LB * NW * 16 == BN, "loads must split evenly");
-  static_assert(!SW || (BN / 2) % 16 == 0, "a 16-row load is all gate or all up rows");
+  static_assert(LA * NW * RPL == BM && LB * NW * RPL == BN, "loads must split evenly");
+  static_assert(!SW || (BN / 2) % RPL == 0, "a load is all gate or all up rows");
   static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024, "LDS budget");
   extern __shared__ __align__(16) char smem[];
 
   TileCoord tc;
   if (!decode_tile<BM>(p, tc)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wavefront index is uniform: say so, so that everything derived from it
+  // (LDS bases, fragment liveness) lives in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const char* Bg = (p.B_last && tc.grp == p.G - 1) ? p.B_last : p.B + (int64_t)tc.grp * p.b_group;
   constexpr uint32_t kOut = 0x80000000u;
@@ -512,14 +533,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_v3(GemmArgs p) {
   const __amdgpu_buffer_rsrc_t b_rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Bg), 0, (int)p.b_bytes, 0x00020000);
 
-  // Load slot j of this wave covers tile rows [16 * (wave + NW * j), +16); lane l
-  // fills LDS slot l % 4 of row l / 4, i.e. logical chunk (l % 4) ^ swz(row).
-  const int lr = lane >> 2, lq = lane & 3;
+  // Load slot j of this wave covers tile rows [RPL * (wave + NW * j), +RPL); lane
+  // l fills LDS slot l % CPR of row l / CPR, i.e. logical chunk slot ^ swz(row).
+  const int lr = lane / CPR, lq = lane % CPR;
   uint32_t a_off[LA], b_off[LB];
 #pragma unroll
   for (int j = 0; j < LA; ++j) {
-    const int row = 16 * (wave + NW * j) + lr;
-    const int ch = lq ^ swz64(row);
+    const int row = RPL * (wave + NW * j) + lr;
+    const int ch = lq ^ swz_sel<ROWB, SWZ>(row);
     if (row < tc.nrows) {
       const int arow = p.a_rows ? p.a_rows[tc.row0 + row] : tc.row0 + row;
       a_off[j] = (uint32_t)arow * (uint32_t)p.lda + ch * 16;
@@ -529,20 +550,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_v3(GemmArgs p) {
   }
 #pragma unroll
   for (int j = 0; j < LB; ++j) {
-    const int row = 16 * (wave + NW * j) + lr;
-    const int ch = lq ^ swz64(row);
+    const int row = RPL * (wave + NW * j) + lr;
+    const int ch = lq ^ swz_sel<ROWB, SWZ>(row);
     int brow;
     bool ok = true;
     if (SW) {
-      brow = (16 * (wave + NW * j) < BN / 2) ? tc.nt * (BN / 2) + row
-                                             : p.up_row + tc.nt * (BN / 2) + (row - BN / 2);
+      brow = (RPL * (wave + NW * j) < BN / 2) ? tc.nt * (BN / 2) + row
+                                              : p.up_row + tc.nt * (BN / 2) + (row - BN / 2);
     } else {
       brow = tc.nt * BN + row;
       ok = brow < p.N;
     }
     b_off[j] = ok ? (uint32_t)brow * (uint32_t)p.ldb + ch * 16 : kOut;
   }
-  const int KT = p.K >> 5;  // 32 bf16 per stage
+  const int KT = p.K / (ROWB / 2);  // ROWB/2 bf16 per stage
   // Stage kt's loads; stages past the end reload the last one (never read;
   // keeps the number of loads in flight constant).
 #define MOE_V3_ISSUE(kt_)                                                                \
@@ -551,9 +572,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_v3(GemmArgs p) {
     char* buf_ = smem + ((kt_) % STAGES) * STAGE;                                        \
     const uint32_t ko_ = (uint32_t)kc_ * ROWB;                                           \
     _Pragma("unroll") for (int j = 0; j < LA; ++j)                                        \
-        load_lds16(a_rs, buf_ + (16 * (wave + NW * j)) * ROWB, a_off[j] + ko_);          \
+        load_lds16(a_rs, buf_ + (RPL * (wave + NW * j)) * ROWB, a_off[j] + ko_);         \
     _Pragma("unroll") for (int j = 0; j < LB; ++j)                                        \
-        load_lds16(b_rs, buf_ + BM * ROWB + (16 * (wave + NW * j)) * ROWB, b_off[j] + ko_); \
+        load_lds16(b_rs, buf_ + BM * ROWB + (RPL * (wave + NW * j)) * ROWB, b_off[j] + ko_); \
   } while (0)
 
   f32x16 acc[FM][FN];
@@ -565,10 +586,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_v3(GemmArgs p) {
       for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
 
   // fragment read offsets: row lane % 32 of each fragment, chunk 2*kk + lane/32
-  const int fr = lane & 31, fh = lane >> 5, fs = swz64(fr);
-  int a_rd[2], b_rd[2];
+  const int fr = lane & 31, fh = lane >> 5, fs = swz_sel<ROWB, SWZ>(fr);
+  int a_rd[KSTEPS], b_rd[KSTEPS];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
+  for (int kk = 0; kk < KSTEPS; ++kk) {
     const int sl = ((2 * kk + fh) ^ fs) << 4;
     a_rd[kk] = (wm * WTM + fr) * ROWB + sl;
     b_rd[kk] = BM * ROWB + fr * ROWB + sl;
@@ -582,38 +603,38 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_v3(GemmArgs p) {
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) MOE_V3_ISSUE(s);
 
-  for (int kt = 0; kt < KT; ++kt) {
-    // this wave's loads of stage kt are done when at most (STAGES-2) stages'
-    // worth of later loads are still in flight; the barrier then publishes
-    // every wave's loads and retires every wave's reads of stage kt-1
-    static_assert((STAGES - 2) * (LA + LB) <= 63, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * (LA + LB)));
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
-    __builtin_amdgcn_s_barrier();
-    MOE_V3_ISSUE(kt + STAGES - 1);
-    const char* cur = smem + (kt % STAGES) * STAGE;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      u32x4 fa[FM], fb[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        fa[i] = *reinterpret_cast<const u32x4*>(cur + a_rd[kk] + i * 32 * ROWB);
-#pragma unroll
-      for (int f = 0; f < FN; ++f)
-        fb[f] = *reinterpret_cast<const u32x4*>(cur + b_rd[kk] + b_row[f] * ROWB);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        // a fragment whose 32 rows all lie past the tile's valid rows would
-        // only produce discarded results (the row count is uniform per block)
-        if (SKIP && wm * WTM + 32 * i >= tc.nrows) continue;
-#pragma unroll
-        for (int f = 0; f < FN; ++f)
-          acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, fa[i]), __builtin_bit_cast(bf16x8, fb[f]), acc[i][f],
-              0, 0, 0);
-      }
-    }
+  // Fragments of this wave whose 32 rows hold at least one valid row; a full
+  // tile takes the branch-free loop.
+  const int live = SKIP ? min(FM, max(0, (tc.nrows - wm * WTM + 31) / 32)) : FM;
+#define MOE_V3_MAIN(CHECK)                                                                   \
+  for (int kt = 0; kt < KT; ++kt) {                                                          \
+    static_assert((STAGES - 2) * (LA + LB) <= 63, "vmcnt range");                            \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * (LA + LB)));                         \
+    __builtin_amdgcn_s_waitcnt(0xC07F);                                                      \
+    __builtin_amdgcn_s_barrier();                                                            \
+    MOE_V3_ISSUE(kt + STAGES - 1);                                                           \
+    const char* cur = smem + (kt % STAGES) * STAGE;                                          \
+    _Pragma("unroll") for (int kk = 0; kk < KSTEPS; ++kk) {                                  \
+      u32x4 fa[FM], fb[FN];                                                                  \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i)                                          \
+          fa[i] = *reinterpret_cast<const u32x4*>(cur + a_rd[kk] + i * 32 * ROWB);           \
+      _Pragma("unroll") for (int f = 0; f < FN; ++f)                                          \
+          fb[f] = *reinterpret_cast<const u32x4*>(cur + b_rd[kk] + b_row[f] * ROWB);         \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                        \
+        if (CHECK && i >= live) continue;                                                    \
+        _Pragma("unroll") for (int f = 0; f < FN; ++f)                                        \
+            acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                             \
+                __builtin_bit_cast(bf16x8, fa[i]), __builtin_bit_cast(bf16x8, fb[f]),        \
+                acc[i][f], 0, 0, 0);                                                         \
+      }                                                                                      \
+    }                                                                                        \
   }
+  if (live == FM) {
+    MOE_V3_MAIN(false)
+  } else {
+    MOE_V3_MAIN(true)
+  }
+#undef MOE_V3_MAIN
 #undef MOE_V3_ISSUE
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no LDS load may still be in flight at exit
 
