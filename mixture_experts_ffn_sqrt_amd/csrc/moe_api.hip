@@ -19,7 +19,8 @@ Workspace workspace_layout(const moe_config& c) {
     return o;
   };
   Workspace w;
-  w.logits = take(T * E * 4);
+  const int splits = router_splits(c);
+  w.logits = take(splits > 1 ? (int64_t)splits * T * router_part_ld(c) * 4 : (int64_t)T * E * 4);
   w.ids = take(R * 4);
   w.weights = take(R * 4);
   w.blockcnt = take(nblk * E * 4);
@@ -121,10 +122,11 @@ int moe_route(const moe_config* cfg, const void* hidden, const void* w_router,
   if (c.T == 0) return MOE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!c.logits_given) {
-    st = hip_status(launch_router_gemm(c, hidden, w_router, logit_offset, logits, s));
+    st = hip_status(launch_router_gemm(c, hidden, w_router, logit_offset, logits, 1, s));
     if (st) return st;
   }
-  return hip_status(launch_topk(c, logits, bias, token_ids, tid2eid, topk_ids, topk_weights, s));
+  return hip_status(launch_topk(c, logits, nullptr, 0, nullptr, bias, token_ids, tid2eid,
+                                topk_ids, topk_weights, nullptr, s));
 }
 
 int moe_permute(const moe_config* cfg, const int32_t* topk_ids, const float* topk_weights,
@@ -249,8 +251,13 @@ int moe_forward(const moe_config* cfg, const void* hidden, const void* w_router,
   int32_t* groups = at<int32_t>(workspace, w.groups);
   int32_t* tiles = at<int32_t>(workspace, w.tile_prefix);
   const int G = c.E + c.n_shared;
-  if ((st = hip_status(launch_router_gemm(rc, hidden, w_router, logit_offset, logits, s)))) return st;
-  if ((st = hip_status(launch_topk(rc, logits, bias, token_ids, tid2eid, ids, gates, s)))) return st;
+  const int splits = router_splits(rc);
+  if ((st = hip_status(launch_router_gemm(rc, hidden, w_router, logit_offset, logits, splits, s))))
+    return st;
+  if ((st = hip_status(launch_topk(rc, splits > 1 ? nullptr : logits, splits > 1 ? logits : nullptr,
+                                   splits > 1 ? splits : 0, logit_offset, bias, token_ids, tid2eid,
+                                   ids, gates, nullptr, s))))
+    return st;
   if ((st = hip_status(launch_permute(rc, ids, gates, at<int32_t>(workspace, w.blockcnt),
                                       at<int32_t>(workspace, w.counts), offsets, sorted_tok,
                                       at<float>(workspace, w.sorted_w), dispatch, s))))

@@ -25,7 +25,7 @@ namespace {
 using namespace gemm;
 
 template <typename TE, int BM, int BN, int WM, int WN, int EPI>
-hipError_t launch_gemm(GemmArgs p, int m_tiles_bound, hipStream_t s) {
+hipError_t launch_gemm(GemmArgs p, int m_tiles_bound, hipStream_t s, int splits = 1) {
   constexpr int NT = 64 * WM * WN;
   constexpr int LDS = 2 * (BM + BN) * 128;
   if (p.chunk_w <= 0 || p.chunk_w > p.n_tiles) p.chunk_w = p.n_tiles;
@@ -35,19 +35,19 @@ hipError_t launch_gemm(GemmArgs p, int m_tiles_bound, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), LDS, s, p);
+  hipLaunchKernelGGL(kern, dim3(grid, splits), dim3(NT), LDS, s, p);
   return hipGetLastError();
 }
 
-// Deep-pipelined bf16 kernel (direct-to-LDS loads, STAGES buffers of 32 K-elements)
-template <int BM, int BN, int WM, int WN, int EPI, int ST>
+// Large-tile bf16 kernel (direct-to-LDS loads, ST LDS buffers of ROWB/2 K-elements)
+template <int BM, int BN, int WM, int WN, int EPI, int ST, int ROWB, int SWZ>
 hipError_t launch_gemm_v3(GemmArgs p, int m_tiles_bound, hipStream_t s) {
   constexpr int NT = 64 * WM * WN;
-  constexpr int LDS = ST * (BM + BN) * 64;
+  constexpr int LDS = ST * (BM + BN) * ROWB;
   if (p.chunk_w <= 0 || p.chunk_w > p.n_tiles) p.chunk_w = p.n_tiles;
   const int grid = m_tiles_bound * p.n_tiles;
   if (grid <= 0) return hipSuccess;
-  auto kern = grouped_gemm_v3<BM, BN, WM, WN, EPI, ST>;
+  auto kern = grouped_gemm_v3<BM, BN, WM, WN, EPI, ST, true, ROWB, SWZ>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   if (e != hipSuccess) return e;
@@ -64,8 +64,21 @@ int tile_bound(int64_t rows, int groups, int bm) {
 
 }  // namespace
 
+int router_splits(const moe_config& c) {
+  // split K so that a small router GEMM still fills the chip: about 1024 blocks,
+  // each split a whole number of 128-byte K stages; at most 16 partials, which
+  // the top-k kernel sums with all its loads in flight at once
+  if (c.dtype == MOE_F32) return 1;
+  const int tiles = ceil_div(c.T, 64) * ceil_div(c.E, 64);
+  const int stages = c.d / 64;
+  int s = 1;
+  while (s * 2 <= kMaxRouterSplits && tiles * s < 1024 && stages % (s * 2) == 0) s *= 2;
+  return s;
+}
+
 hipError_t launch_router_gemm(const moe_config& c, const void* hidden, const void* w_router,
-                              const float* logit_offset, float* logits, hipStream_t s) {
+                              const float* logit_offset, float* out, int splits,
+                              hipStream_t s) {
   GemmArgs p{};
   const int es = c.dtype == MOE_F32 ? 4 : 2;
   p.A = static_cast<const char*>(hidden);
@@ -76,15 +89,20 @@ hipError_t launch_router_gemm(const moe_config& c, const void* hidden, const voi
   p.K = c.d;
   p.G = 1;
   p.dense_rows = c.T;
-  p.C = reinterpret_cast<char*>(logits);
+  p.C = reinterpret_cast<char*>(out);
   p.ldc = (int64_t)c.E * 4;
-  p.col_add = logit_offset;
+  p.col_add = splits > 1 ? nullptr : logit_offset;  // with splits, added when summed
   if (c.dtype == MOE_F32) {
     p.n_tiles = ceil_div(c.E, 16);
     return launch_gemm<float, 16, 16, 1, 1, EPI_LOGITS>(p, ceil_div(c.T, 16), s);
   }
   p.n_tiles = ceil_div(c.E, 64);
-  return launch_gemm<uint16_t, 64, 64, 2, 2, EPI_LOGITS>(p, ceil_div(c.T, 64), s);
+  if (splits > 1) {  // partial rows padded to whole 16-byte chunks
+    p.k_chunk = c.d / splits;
+    p.ldc = (int64_t)router_part_ld(c) * 4;
+    p.c_split = (int64_t)c.T * p.ldc;
+  }
+  return launch_gemm<uint16_t, 64, 64, 2, 2, EPI_LOGITS>(p, ceil_div(c.T, 64), s, splits);
 }
 
 namespace {
@@ -150,7 +168,7 @@ hipError_t launch_expert_up(const moe_config& c, const ExpertFfnArgs& a, hipStre
       g.chunk_w = kChunkW;
       g.a_bytes = (uint32_t)((int64_t)c.T * c.d * es);
       g.b_bytes = (uint32_t)(2 * F * d * es);
-      return launch_gemm_v3<256, 256, 2, 2, EPI_SWIGLU, 4>(g, mb, s);
+      return launch_gemm_v3<256, 256, 4, 4, EPI_SWIGLU, 2, 128, 3>(g, mb, s);
     default:
       g.n_tiles = c.d_ff / 64;
       return launch_gemm<uint16_t, 128, 128, 2, 2, EPI_SWIGLU>(g, mb, s);
@@ -191,7 +209,7 @@ hipError_t launch_expert_down(const moe_config& c, const ExpertFfnArgs& a, hipSt
       g.chunk_w = kChunkW;
       g.a_bytes = (uint32_t)((int64_t)a.rows_bound * F * es);
       g.b_bytes = (uint32_t)(d * F * es);
-      return launch_gemm_v3<256, 256, 2, 2, EPI_STORE, 4>(g, mb, s);
+      return launch_gemm_v3<256, 256, 4, 4, EPI_STORE, 2, 128, 3>(g, mb, s);
     default:
       g.n_tiles = ceil_div(c.d, 128);
       return launch_gemm<uint16_t, 128, 128, 2, 2, EPI_STORE>(g, mb, s);

@@ -34,6 +34,8 @@ struct GemmArgs {
   int64_t ldc;                // bytes between output rows
   const float* col_add;       // EPI_LOGITS: per-column addend (nullable)
   int chunk_w;                // column tiles per scheduling chunk (tile order)
+  int k_chunk;                // dense split-K: elements of K per grid row y (0: no split)
+  int64_t c_split;            // dense split-K: bytes between the partial outputs of y and y+1
   uint32_t a_bytes;           // bytes of the A operand (buffer range; < 2^31)
   uint32_t b_bytes;           // bytes of one group's weights (buffer range; < 2^31)
 };
@@ -142,6 +144,13 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(GemmArgs p) 
   TileCoord tc;
   if (!decode_tile<BM>(p, tc)) return;
   const int grp = tc.grp, row0 = tc.row0, nrows = tc.nrows, nt = tc.nt;
+  if (p.k_chunk) {  // split-K over grid rows: this block's slice of K and its partial output
+    const int64_t ko = (int64_t)blockIdx.y * p.k_chunk * (int64_t)sizeof(TE);
+    p.A += ko;
+    p.B += ko;
+    p.C += (int64_t)blockIdx.y * p.c_split;
+    p.K = p.k_chunk;
+  }
   const char* Bg = (p.B_last && grp == p.G - 1) ? p.B_last : p.B + (int64_t)grp * p.b_group;
 
   // ---- per-thread global sources and LDS destinations ------------------------
@@ -462,14 +471,18 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void grouped_gemm_v2(GemmArgs p
 
 
 // ---------------------------------------------------------------------------
-// Deep-pipelined bf16 variant: direct global->LDS buffer loads (16 bytes per
-// lane; a wavefront's load fills 1 KB of LDS, lane l at byte 16*l), STAGES LDS
-// buffers of 32 K-elements (64 bytes per row), loads issued STAGES-1 stages
-// ahead, one barrier per stage, MFMA 32x32x16.
+// Large-tile bf16 variant: direct global->LDS buffer loads (16 bytes per lane;
+// a wavefront's load fills 1 KB of LDS, lane l at byte 16*l), STAGES LDS
+// buffers of ROWB/2 K-elements (ROWB bytes per tile row), loads issued
+// STAGES-1 stages ahead, one barrier per stage, MFMA 32x32x16.
 //
-// LDS row layout: row r holds four 16-byte chunks; chunk c sits in slot
-// c ^ swz(r), swz(r) = ((r >> 1) ^ (r >> 3)) & 3, so that the 8 or 16 rows one
-// MFMA fragment read touches at one K position use distinct bank groups.
+// LDS row layout: row r holds ROWB/16 16-byte chunks; logical chunk c sits in
+// slot c ^ swz(r).  A fragment read (ds_read_b128) is served 16 lanes at a
+// time, i.e. 16 consecutive rows at one K position; gfx950's LDS has 64 banks
+// (256 bytes per cycle), so the swizzle must spread those 16 rows over all 16
+// bank groups: (r >> 2) & 3 does for 64-byte rows and (r >> 1) & 7 for
+// 128-byte rows (4 cycles per read, measured), while the plain layout costs 4x
+// (64-byte rows) or 8x (128-byte rows).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int swz64(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
@@ -711,7 +724,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_v4(GemmArgs p) {
 
   TileCoord tc;
   if (!decode_tile<BM>(p, tc)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const char* Bg = (p.B_last && tc.grp == p.G - 1) ? p.B_last : p.B + (int64_t)tc.grp * p.b_group;
   constexpr uint32_t kOut = 0x80000000u;

@@ -41,7 +41,7 @@ constexpr int kPermuteChunk = 2048;
 // entry points so that moe_workspace_size is the maximum any of them needs
 // ---------------------------------------------------------------------------
 struct Workspace {
-  int64_t logits, ids, weights;        // [T*E] f32, [T*k] i32, [T*k] f32
+  int64_t logits, ids, weights;        // [splits*T*E] f32 partial logits, [T*k] i32, [T*k] f32
   int64_t blockcnt;                    // [nblk*E] i32
   int64_t counts, offsets;             // [E] i32, [E+1] i32
   int64_t groups;                      // [2*G] i32: first rows, then ends
@@ -57,13 +57,25 @@ Workspace workspace_layout(const moe_config& c);
 // ---------------------------------------------------------------------------
 // launchers (return hipError_t of the launch)
 // ---------------------------------------------------------------------------
-// logits = hidden W_r^T (+ offset); float32 out
+// Router logits = hidden W_r^T.  With splits == 1, `out` is [T,E] and holds the
+// logits plus the offset; with splits > 1 (bf16 only), `out` is [splits,T,Ep]
+// (Ep = router_part_ld(c), rows padded to 16 bytes) of partial sums over K
+// slices, and the offset is added when the top-k kernel sums them.
+// router_splits() is the split count moe_forward uses (at most kMaxRouterSplits).
+constexpr int kMaxRouterSplits = 16;
+inline int router_part_ld(const moe_config& c) { return align_up(c.E, 4); }
+int router_splits(const moe_config& c);
 hipError_t launch_router_gemm(const moe_config& c, const void* hidden, const void* w_router,
-                              const float* logit_offset, float* logits, hipStream_t s);
-// scores, selection, gates from logits (learned or hash)
-hipError_t launch_topk(const moe_config& c, const float* logits, const float* bias,
-                       const int32_t* token_ids, const int32_t* tid2eid, int32_t* ids,
-                       float* weights, hipStream_t s);
+                              const float* logit_offset, float* out, int splits,
+                              hipStream_t s);
+// Scores, selection, gates from logits (learned or hash).  With nparts > 0 the
+// logits are the sum of nparts partial rows (part s at parts + s*T*E, summed in
+// order s = 0, 1, ...) plus logit_offset; else `logits` is read as is.
+// logits_out (nullable) receives the summed logits.
+hipError_t launch_topk(const moe_config& c, const float* logits, const float* parts, int nparts,
+                       const float* logit_offset, const float* bias, const int32_t* token_ids,
+                       const int32_t* tid2eid, int32_t* ids, float* weights, float* logits_out,
+                       hipStream_t s);
 // histogram + scan + stable scatter
 hipError_t launch_permute(const moe_config& c, const int32_t* ids, const float* weights,
                           int32_t* blockcnt, int32_t* counts, int32_t* offsets,

@@ -24,8 +24,14 @@ namespace {
 constexpr int kMaxPerLane = 16;  // E <= 1024
 constexpr int kWavesPerBlock = 4;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 struct TopkArgs {
-  const float* logits;   // [T, E]
+  const float* logits;   // [T, E] (when nparts == 0)
+  const float* parts;    // [nparts, T, part_ld] partial logits (when nparts > 0)
+  int nparts, part_ld;
+  const float* offset;   // [E] added to summed partials, or nullptr
+  float* logits_out;     // [T, E] summed logits, or nullptr
   const float* bias;     // [E] or nullptr
   const int32_t* token_ids;
   const int32_t* tid2eid;
@@ -98,10 +104,48 @@ __device__ __forceinline__ void write_gates(const TopkArgs& p, const float* l, i
 
 __global__ __launch_bounds__(64 * kWavesPerBlock) void topk_kernel(TopkArgs p) {
   __shared__ float skey[kWavesPerBlock][1024];
+  __shared__ float slog[kWavesPerBlock][1024];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * kWavesPerBlock + wave;
   if (t >= p.T) return;  // whole wavefronts only; no block barrier below
-  const float* l = p.logits + static_cast<int64_t>(t) * p.E;
+  // this token's logits row, in LDS: the given row, or the sum of the split-K
+  // partials taken in a fixed order (part 0 first) plus the offset
+  float* l = slog[wave];
+  if (p.nparts > 0) {
+    const int64_t pstride = static_cast<int64_t>(p.T) * p.part_ld;
+    const float* prow = p.parts + static_cast<int64_t>(t) * p.part_ld;
+    for (int c = lane; c * 4 < p.E; c += 64) {
+      f32x4 acc = *reinterpret_cast<const f32x4*>(prow + 4 * c);
+      for (int q0 = 1; q0 < p.nparts; q0 += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (q0 + j < p.nparts)
+            v[j] = *reinterpret_cast<const f32x4*>(prow + (q0 + j) * pstride + 4 * c);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (q0 + j < p.nparts) acc += v[j];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = 4 * c + u;
+        if (e < p.E) {
+          const float x = p.offset ? acc[u] + p.offset[e] : acc[u];
+          l[e] = x;
+          if (p.logits_out) p.logits_out[static_cast<int64_t>(t) * p.E + e] = x;
+        }
+      }
+    }
+  } else {
+    const float* lrow = p.logits + static_cast<int64_t>(t) * p.E;
+    for (int e = lane; e < p.E; e += 64) {
+      l[e] = lrow[e];
+      if (p.logits_out) p.logits_out[static_cast<int64_t>(t) * p.E + e] = lrow[e];
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   if (p.mode == MOE_ROUTE_HASH) {
     int e = -1;
@@ -195,11 +239,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void topk_kernel(TopkArgs p) {
 
 }  // namespace
 
-hipError_t launch_topk(const moe_config& c, const float* logits, const float* bias,
-                       const int32_t* token_ids, const int32_t* tid2eid, int32_t* ids,
-                       float* weights, hipStream_t s) {
-  TopkArgs p{logits, bias, token_ids, tid2eid, ids, weights, c.T, c.E, c.k, c.scoring,
-             c.route_mode, c.n_group, c.topk_group, c.group_topk, c.vocab};
+hipError_t launch_topk(const moe_config& c, const float* logits, const float* parts, int nparts,
+                       const float* logit_offset, const float* bias, const int32_t* token_ids,
+                       const int32_t* tid2eid, int32_t* ids, float* weights, float* logits_out,
+                       hipStream_t s) {
+  TopkArgs p{logits, parts, nparts, router_part_ld(c), logit_offset, logits_out, bias, token_ids, tid2eid, ids,
+             weights, c.T, c.E, c.k, c.scoring, c.route_mode, c.n_group, c.topk_group,
+             c.group_topk, c.vocab};
   hipLaunchKernelGGL(topk_kernel, dim3(ceil_div(c.T, kWavesPerBlock)), dim3(64 * kWavesPerBlock),
                      0, s, p);
   return hipGetLastError();
