@@ -28,7 +28,6 @@ template <typename TE, int BM, int BN, int WM, int WN, int EPI>
 hipError_t launch_gemm(GemmArgs p, int m_tiles_bound, hipStream_t s, int splits = 1) {
   constexpr int NT = 64 * WM * WN;
   constexpr int LDS = 2 * (BM + BN) * 128;
-  if (p.chunk_w <= 0 || p.chunk_w > p.n_tiles) p.chunk_w = p.n_tiles;
   const int grid = m_tiles_bound * p.n_tiles;
   if (grid <= 0) return hipSuccess;
   auto kern = grouped_gemm_kernel<TE, BM, BN, WM, WN, EPI>;
@@ -44,7 +43,6 @@ template <int BM, int BN, int WM, int WN, int EPI, int ST, int ROWB, int SWZ>
 hipError_t launch_gemm_v3(GemmArgs p, int m_tiles_bound, hipStream_t s) {
   constexpr int NT = 64 * WM * WN;
   constexpr int LDS = ST * (BM + BN) * ROWB;
-  if (p.chunk_w <= 0 || p.chunk_w > p.n_tiles) p.chunk_w = p.n_tiles;
   const int grid = m_tiles_bound * p.n_tiles;
   if (grid <= 0) return hipSuccess;
   auto kern = grouped_gemm_v3<BM, BN, WM, WN, EPI, ST, true, ROWB, SWZ>;
@@ -129,7 +127,6 @@ int tile_rows(FfnTiles t) {
   return t == FfnTiles::BF16_256 ? 256 : t == FfnTiles::BF16_128 ? 128 : 16;
 }
 
-constexpr int kChunkW = 8;  // column tiles per scheduling chunk (tile order)
 
 }  // namespace
 
@@ -165,7 +162,6 @@ hipError_t launch_expert_up(const moe_config& c, const ExpertFfnArgs& a, hipStre
       return launch_gemm<uint16_t, 16, 128, 1, 4, EPI_SWIGLU>(g, mb, s);
     case FfnTiles::BF16_256:
       g.n_tiles = c.d_ff / 128;
-      g.chunk_w = kChunkW;
       g.a_bytes = (uint32_t)((int64_t)c.T * c.d * es);
       g.b_bytes = (uint32_t)(2 * F * d * es);
       return launch_gemm_v3<256, 256, 4, 4, EPI_SWIGLU, 2, 128, 3>(g, mb, s);
@@ -206,7 +202,6 @@ hipError_t launch_expert_down(const moe_config& c, const ExpertFfnArgs& a, hipSt
       return launch_gemm<uint16_t, 16, 128, 1, 4, EPI_STORE>(g, mb, s);
     case FfnTiles::BF16_256:
       g.n_tiles = ceil_div(c.d, 256);
-      g.chunk_w = kChunkW;
       g.a_bytes = (uint32_t)((int64_t)a.rows_bound * F * es);
       g.b_bytes = (uint32_t)(d * F * es);
       return launch_gemm_v3<256, 256, 4, 4, EPI_STORE, 2, 128, 3>(g, mb, s);

@@ -33,7 +33,6 @@ struct GemmArgs {
   char* C;                    // output rows (indexed by dispatch row)
   int64_t ldc;                // bytes between output rows
   const float* col_add;       // EPI_LOGITS: per-column addend (nullable)
-  int chunk_w;                // column tiles per scheduling chunk (tile order)
   int k_chunk;                // dense split-K: elements of K per grid row y (0: no split)
   int64_t c_split;            // dense split-K: bytes between the partial outputs of y and y+1
   uint32_t a_bytes;           // bytes of the A operand (buffer range; < 2^31)
@@ -85,40 +84,68 @@ struct TileCoord {
   int grp, row0, nrows, nt;
 };
 
-// Which tile this block owns (see grouped_gemm_kernel); false: nothing to do.
+// Row tiles of one group that run next to each other on an XCD (see
+// decode_tile).
+constexpr int kSuperRows = 8;
+
+// Which tile this block owns; false: nothing to do.
+//
+// Tiles: group g's rows are cut into tile_prefix[g+1] - tile_prefix[g] tiles
+// of group_tile_rows(M_g, BM) rows (dense mode: one group of dense_rows rows),
+// times n_tiles column tiles.  Order: group by group; inside a group, row tiles
+// are taken in super-rows of at most kSuperRows (near-equal heights), and a
+// super-row is walked column by column with its row tiles fastest.  So the
+// tiles that run together share one weight panel per column and a handful of
+// operand panels, and every tile of a super-row has about the same work,
+// which keeps co-running blocks in step and their K slabs in L2.
+//
+// Blocks are handed to the 8 XCDs round-robin (block b -> XCD b % 8), so block
+// b takes logical tile xcd * q + min(xcd, r) + b / 8: each XCD walks a
+// contiguous run of the order above.
 template <int BM>
 __device__ __forceinline__ bool decode_tile(const GemmArgs& p, TileCoord& tc) {
-  const int total_m = p.g_begin ? p.tile_prefix[p.G] : ceil_div(p.dense_rows, BM);
-  const int nact = total_m * p.n_tiles;
+  const int nt_all = p.n_tiles;
+  const int total_m = p.g_begin ? p.tile_prefix[p.G] : group_tiles(p.dense_rows, BM);
+  const int nact = total_m * nt_all;
   const int bid = blockIdx.x;
   if (bid >= nact) return false;
-  // Blocks are handed to the 8 XCDs round-robin (block b -> XCD b % 8): give
-  // each XCD a contiguous run of logical tiles.  Logical order: column tiles
-  // in chunks of chunk_w; inside a chunk, row tiles fastest-outer, so the
-  // blocks running together on one XCD share both weight panels (same
-  // columns) and operand rows (same row tile).
   const int q8 = nact >> 3, r8 = nact & 7, xcd = bid & 7;
   const int logical = xcd * q8 + min(xcd, r8) + (bid >> 3);
-  const int per_chunk = total_m * p.chunk_w;
-  const int chunk = logical / per_chunk;
-  const int w = min(p.chunk_w, p.n_tiles - chunk * p.chunk_w);
-  const int rem = logical - chunk * per_chunk;
-  const int mt = rem / w;
-  tc.nt = chunk * p.chunk_w + (rem - mt * w);
-  tc.grp = 0;
+
+  int g = 0, t0 = 0, mt_g = total_m, M = p.dense_rows, rbeg = 0;
   if (p.g_begin) {
+    // the group whose tiles [tile_prefix[g], tile_prefix[g+1]) * n_tiles hold it
+    const int r = logical / nt_all;
     int lo = 0, hi = p.G - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (p.tile_prefix[mid] <= mt) lo = mid; else hi = mid - 1;
+      if (p.tile_prefix[mid] <= r) lo = mid; else hi = mid - 1;
     }
-    tc.grp = lo;
-    tc.row0 = p.g_begin[lo] + (mt - p.tile_prefix[lo]) * BM;
-    tc.nrows = min(BM, p.g_end[lo] - tc.row0);
-  } else {
-    tc.row0 = mt * BM;
-    tc.nrows = min(BM, p.dense_rows - tc.row0);
+    g = lo;
+    t0 = p.tile_prefix[g];
+    mt_g = p.tile_prefix[g + 1] - t0;
+    rbeg = p.g_begin[g];
+    M = p.g_end[g] - rbeg;
   }
+  const int l = logical - t0 * nt_all;  // tile index inside the group
+  const int nsr = ceil_div(mt_g, kSuperRows);
+  const int base = mt_g / nsr, extra = mt_g - base * nsr;  // first `extra` super-rows: base + 1
+  const int rt = l / nt_all;
+  int s0, h;
+  if (rt < extra * (base + 1)) {
+    h = base + 1;
+    s0 = (rt / h) * h;
+  } else {
+    h = base;
+    s0 = extra * (base + 1) + ((rt - extra * (base + 1)) / base) * base;
+  }
+  const int ls = l - s0 * nt_all;
+  tc.nt = ls / h;
+  const int mt = s0 + (ls - tc.nt * h);
+  const int c = group_tile_rows(M, BM);
+  tc.grp = g;
+  tc.row0 = rbeg + mt * c;
+  tc.nrows = min(c, M - mt * c);
   return true;
 }
 
@@ -697,8 +724,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_v3(GemmArgs p) {
 // ---------------------------------------------------------------------------
 template <int ROWB>
 __device__ __forceinline__ int swz_row(int r) {
-  if constexpr (ROWB == 128) return r & 7;
-  else return swz64(r);
+  if constexpr (ROWB == 128) return (r >> 1) & 7;
+  else return (r >> 2) & 3;
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int KSTEPS>

@@ -33,6 +33,20 @@ __host__ __device__ constexpr int tile_height_index(int bm) {
   return bm == 16 ? 0 : bm == 32 ? 1 : bm == 64 ? 2 : bm == 128 ? 3 : 4;
 }
 
+// Rows per tile of a group of M rows cut into tiles of at most BM rows: the
+// group is split into ceil(M/BM) near-equal tiles, each rounded up to a
+// multiple of min(32, BM) (whole MFMA fragments), so a group never ends in a
+// sliver tile that costs a full tile's operand loads for a few rows, and the
+// tiles of a group take about the same time.  The group then has
+// ceil(M / group_tile_rows(M, BM)) <= ceil(M / BM) tiles.
+__host__ __device__ constexpr int group_tile_rows(int M, int bm) {
+  return M <= 0 ? bm
+                : (int)align_up(ceil_div(M, ceil_div(M, bm)), bm < 32 ? bm : 32);
+}
+__host__ __device__ constexpr int group_tiles(int M, int bm) {
+  return M <= 0 ? 0 : ceil_div(M, group_tile_rows(M, bm));
+}
+
 // pairs handled by one histogram / scatter block of the permutation
 constexpr int kPermuteChunk = 2048;
 

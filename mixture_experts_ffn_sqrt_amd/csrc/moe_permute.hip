@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(const int32_t
         g_begin[g] = b;
         g_end[g] = en;
       }
-      const int tiles = g < G ? (rows + bm - 1) / bm : 0;
+      const int tiles = g < G ? group_tiles(rows, bm) : 0;
       const int ex = block_exclusive_scan(tiles, wave_tot);
       if (g < G) tp[g] = carry + ex;
       // total of this pass: last thread's exclusive prefix + its own count
