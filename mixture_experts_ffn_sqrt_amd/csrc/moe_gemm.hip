@@ -1,6 +1,6 @@
 // Grouped GEMMs of the MoE layer on gfx950 MFMA.
 //
-// One kernel template serves three contractions, all "TN" (both operands
+// Two kernel templates serve three contractions, all "TN" (both operands
 // contiguous along the reduction dimension K):
 //   router   logits[t, e]  = hidden[t] . W_r[e]            (+ logit offset), float out
 //   GEMM 1   H[r, f]       = SiLU(x . W1_e[f]) * (x . W3_e[f]),  x = hidden[token of row r]
@@ -15,9 +15,13 @@
 // reads the device-side tile prefix to find its (group, row tile), and blocks
 // past the real tile count exit at once.
 //
-// Tile pipeline: global -> registers -> LDS (XOR-swizzled 128-byte rows, two
-// stages), MFMA 16x16x32 bf16 (or 16x16x4 f32) from LDS fragments, float32
-// accumulation, epilogue straight from the accumulators.
+// grouped_gemm_dma (bf16): direct global -> LDS buffer loads into a ring of
+// LDS stages, MFMA 32x32x16.  256x256 tiles on 16 wavefronts when experts have
+// many rows (MFMA-bound prefill); 32-row tiles with a four-stage ring when
+// they have a few (each expert's weights streamed once, HBM-bound decode).
+// grouped_gemm_staged (any element type): global -> registers -> LDS, two
+// stages, MFMA 16x16; the router GEMM (split over K), the fp32 configurations
+// and shapes the buffer-load kernel does not take.
 #include "moe_gemm_kernels.h"
 
 namespace moe {
@@ -30,7 +34,7 @@ hipError_t launch_gemm(GemmArgs p, int m_tiles_bound, hipStream_t s, int splits 
   constexpr int LDS = 2 * (BM + BN) * 128;
   const int grid = m_tiles_bound * p.n_tiles;
   if (grid <= 0) return hipSuccess;
-  auto kern = grouped_gemm_kernel<TE, BM, BN, WM, WN, EPI>;
+  auto kern = grouped_gemm_staged<TE, BM, BN, WM, WN, EPI>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   if (e != hipSuccess) return e;
@@ -38,14 +42,14 @@ hipError_t launch_gemm(GemmArgs p, int m_tiles_bound, hipStream_t s, int splits 
   return hipGetLastError();
 }
 
-// Large-tile bf16 kernel (direct-to-LDS loads, ST LDS buffers of ROWB/2 K-elements)
+// Direct-to-LDS bf16 kernel (ST LDS buffers of ROWB/2 K-elements)
 template <int BM, int BN, int WM, int WN, int EPI, int ST, int ROWB, int SWZ>
-hipError_t launch_gemm_v3(GemmArgs p, int m_tiles_bound, hipStream_t s) {
+hipError_t launch_gemm_dma(GemmArgs p, int m_tiles_bound, hipStream_t s) {
   constexpr int NT = 64 * WM * WN;
   constexpr int LDS = ST * (BM + BN) * ROWB;
   const int grid = m_tiles_bound * p.n_tiles;
   if (grid <= 0) return hipSuccess;
-  auto kern = grouped_gemm_v3<BM, BN, WM, WN, EPI, ST, true, ROWB, SWZ>;
+  auto kern = grouped_gemm_dma<BM, BN, WM, WN, EPI, ST, ROWB, SWZ>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   if (e != hipSuccess) return e;
@@ -110,23 +114,26 @@ namespace {
 // decode-shaped batches; prefill-shaped batches take 256x256 tiles on the
 // deep-pipelined kernel when the shapes allow it (d_ff a multiple of 128 and
 // operands addressable with 31-bit offsets), else 128-row tiles.
-enum class FfnTiles { F32_16, BF16_16, BF16_128, BF16_256 };
+enum class FfnTiles { F32_16, BF16_16, BF16_32, BF16_128, BF16_256 };
 
 FfnTiles pick_tiles(const moe_config& c, const ExpertFfnArgs& a) {
   if (c.dtype == MOE_F32) return FfnTiles::F32_16;
   const int64_t avg_rows = a.rows_bound / (a.n_groups > 0 ? a.n_groups : 1);
-  if (avg_rows < 48) return FfnTiles::BF16_16;
+  // the buffer-load kernels address each operand with 32-bit offsets
   const int64_t lim = int64_t(1) << 31;
   const bool fits = c.d_ff % 128 == 0 && (int64_t)c.T * c.d * 2 < lim &&
                     (int64_t)a.rows_bound * c.d_ff * 2 < lim &&
                     (int64_t)2 * c.d_ff * c.d * 2 < lim;
+  // a few rows per expert: the GEMMs stream each expert's weights once
+  // (HBM-bound); 32-row tiles with a deep direct-to-LDS pipeline
+  if (avg_rows < 48) return fits ? FfnTiles::BF16_32 : FfnTiles::BF16_16;
   return fits ? FfnTiles::BF16_256 : FfnTiles::BF16_128;
 }
 
 int tile_rows(FfnTiles t) {
-  return t == FfnTiles::BF16_256 ? 256 : t == FfnTiles::BF16_128 ? 128 : 16;
+  return t == FfnTiles::BF16_256 ? 256 : t == FfnTiles::BF16_128 ? 128
+                                         : t == FfnTiles::BF16_32  ? 32 : 16;
 }
-
 
 }  // namespace
 
@@ -160,11 +167,16 @@ hipError_t launch_expert_up(const moe_config& c, const ExpertFfnArgs& a, hipStre
     case FfnTiles::BF16_16:
       g.n_tiles = c.d_ff / 64;
       return launch_gemm<uint16_t, 16, 128, 1, 4, EPI_SWIGLU>(g, mb, s);
+    case FfnTiles::BF16_32:
+      g.n_tiles = c.d_ff / 128;
+      g.a_bytes = (uint32_t)((int64_t)c.T * c.d * es);
+      g.b_bytes = (uint32_t)(2 * F * d * es);
+      return launch_gemm_dma<32, 256, 1, 4, EPI_SWIGLU, 4, 128, 3>(g, mb, s);
     case FfnTiles::BF16_256:
       g.n_tiles = c.d_ff / 128;
       g.a_bytes = (uint32_t)((int64_t)c.T * c.d * es);
       g.b_bytes = (uint32_t)(2 * F * d * es);
-      return launch_gemm_v3<256, 256, 4, 4, EPI_SWIGLU, 2, 128, 3>(g, mb, s);
+      return launch_gemm_dma<256, 256, 4, 4, EPI_SWIGLU, 2, 128, 3>(g, mb, s);
     default:
       g.n_tiles = c.d_ff / 64;
       return launch_gemm<uint16_t, 128, 128, 2, 2, EPI_SWIGLU>(g, mb, s);
@@ -200,11 +212,16 @@ hipError_t launch_expert_down(const moe_config& c, const ExpertFfnArgs& a, hipSt
     case FfnTiles::BF16_16:
       g.n_tiles = ceil_div(c.d, 128);
       return launch_gemm<uint16_t, 16, 128, 1, 4, EPI_STORE>(g, mb, s);
+    case FfnTiles::BF16_32:
+      g.n_tiles = ceil_div(c.d, 128);
+      g.a_bytes = (uint32_t)((int64_t)a.rows_bound * F * es);
+      g.b_bytes = (uint32_t)(d * F * es);
+      return launch_gemm_dma<32, 128, 1, 2, EPI_STORE, 4, 128, 3>(g, mb, s);
     case FfnTiles::BF16_256:
       g.n_tiles = ceil_div(c.d, 256);
       g.a_bytes = (uint32_t)((int64_t)a.rows_bound * F * es);
       g.b_bytes = (uint32_t)(d * F * es);
-      return launch_gemm_v3<256, 256, 4, 4, EPI_STORE, 2, 128, 3>(g, mb, s);
+      return launch_gemm_dma<256, 256, 4, 4, EPI_STORE, 2, 128, 3>(g, mb, s);
     default:
       g.n_tiles = ceil_div(c.d, 128);
       return launch_gemm<uint16_t, 128, 128, 2, 2, EPI_STORE>(g, mb, s);

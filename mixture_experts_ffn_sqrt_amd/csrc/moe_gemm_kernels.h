@@ -149,10 +149,12 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& p, TileCoord& tc) {
   return true;
 }
 
-// BM x BN tile (BN = weight rows; for SwiGLU the first half are gate rows and
-// the second half the matching up rows), WM x WN waves, 128 bytes of K per stage.
+// Register-staged kernel (any element type; small tiles): BM x BN tile (BN =
+// weight rows; for SwiGLU the first half are gate rows and the second half the
+// matching up rows), WM x WN waves, MFMA 16x16, 128 bytes of K per stage, the
+// next stage loaded to registers while the current one is multiplied from LDS.
 template <typename TE, int BM, int BN, int WM, int WN, int EPI>
-__global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_staged(GemmArgs p) {
   constexpr int NT = 64 * WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
@@ -324,181 +326,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(GemmArgs p) 
 
 
 // ---------------------------------------------------------------------------
-// Large-tile bf16 variant: MFMA 32x32x16, wave tiles of 32*FM x 32*FN, the
-// operand bases kept uniform (scalar registers) and per-lane 32-bit offsets,
-// fragments for the next K step read from LDS while the current step's MFMAs
-// run.  Same tile bookkeeping, swizzle and epilogue semantics as above.
-// Requires every A operand to span less than 4 GiB (checked by the launcher).
-// ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int EPI, int MINB>
-__global__ __launch_bounds__(64 * WM * WN, MINB) void grouped_gemm_v2(GemmArgs p) {
-  constexpr int NT = 64 * WM * WN;
-  constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr bool SW = EPI == EPI_SWIGLU;
-  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must hold whole 32x32 fragments");
-  static_assert(!SW || FN % 2 == 0, "SwiGLU waves hold gate and up fragments in pairs");
-  static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "loads must split evenly");
-  static_assert(!SW || ((BN / 2) % (NT / 8)) == 0, "a load slot is all gate or all up rows");
-  constexpr int LA = BM * 8 / NT, LB = BN * 8 / NT;
-  constexpr int RPS = NT / 8;  // rows covered by one load slot
-  constexpr int STAGE = (BM + BN) * 128;
-  extern __shared__ __align__(16) char smem[];
-
-  TileCoord tc;
-  if (!decode_tile<BM>(p, tc)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const char* Bg = (p.B_last && tc.grp == p.G - 1) ? p.B_last : p.B + (int64_t)tc.grp * p.b_group;
-
-  // Buffer loads: a scalar resource per operand, per-lane 32-bit offsets that
-  // stay fixed, and the K position in the scalar offset.  Rows outside the
-  // tile (and weight rows past N) get an offset beyond the resource's range,
-  // which the hardware returns as zeros.
-  constexpr uint32_t kOut = 0x80000000u;
-  const __amdgpu_buffer_rsrc_t a_rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.A), 0, (int)p.a_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t b_rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Bg), 0, (int)p.b_bytes, 0x00020000);
-  const int lrow = tid >> 3, lch = tid & 7;
-  uint32_t a_off[LA];
-#pragma unroll
-  for (int c = 0; c < LA; ++c) {
-    const int row = c * RPS + lrow;
-    if (row < tc.nrows) {
-      const int arow = p.a_rows ? p.a_rows[tc.row0 + row] : tc.row0 + row;
-      a_off[c] = (uint32_t)arow * (uint32_t)p.lda + lch * 16;
-    } else {
-      a_off[c] = kOut;
-    }
-  }
-  uint32_t b_off[LB];
-#pragma unroll
-  for (int c = 0; c < LB; ++c) {
-    const int row = c * RPS + lrow;
-    int brow;
-    if (SW) {
-      brow = (c * RPS < BN / 2) ? tc.nt * (BN / 2) + row
-                                : p.up_row + tc.nt * (BN / 2) + (row - BN / 2);
-    } else {
-      brow = tc.nt * BN + row;
-    }
-    b_off[c] = (SW || brow < p.N) ? (uint32_t)brow * (uint32_t)p.ldb + lch * 16 : kOut;
-  }
-  const int st_a = lds_off(lrow, lch);  // + c * RPS * 128 (RPS is a multiple of 8)
-  const int st_b = BM * 128 + lds_off(lrow, lch);
-
-  const int KT = p.K >> 6;  // 64 bf16 per stage
-  u32x4 ra[LA], rb[LB];
-  auto gload = [&](int kt) {
-    const int ko = kt * 128;
-#pragma unroll
-    for (int c = 0; c < LA; ++c) ra[c] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_off[c], ko, 0);
-#pragma unroll
-    for (int c = 0; c < LB; ++c) rb[c] = __builtin_amdgcn_raw_buffer_load_b128(b_rs, b_off[c], ko, 0);
-  };
-  auto lstore = [&](char* buf) {
-#pragma unroll
-    for (int c = 0; c < LA; ++c) *reinterpret_cast<u32x4*>(buf + st_a + c * RPS * 128) = ra[c];
-#pragma unroll
-    for (int c = 0; c < LB; ++c) *reinterpret_cast<u32x4*>(buf + st_b + c * RPS * 128) = rb[c];
-  };
-
-  gload(0);
-  lstore(smem);
-  __syncthreads();
-
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int f = 0; f < FN; ++f)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
-
-  // LDS read offsets: row (lane & 31) of each fragment, 16-byte chunk
-  // 2*kk + (lane >> 5) of the 128-byte row, swizzled by row & 7 == lane & 7
-  const int fr = lane & 31, fh = lane >> 5, fx = lane & 7;
-  int a_rd[4], b_rd[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int sw = ((2 * kk + fh) ^ fx) << 4;
-    a_rd[kk] = (wm * WTM + fr) * 128 + sw;
-    b_rd[kk] = BM * 128 + fr * 128 + sw;
-  }
-  int b_row[FN];
-#pragma unroll
-  for (int f = 0; f < FN; ++f)
-    b_row[f] = SW ? ((f < FN / 2) ? wn * (WTN / 2) + 32 * f : BN / 2 + wn * (WTN / 2) + 32 * (f - FN / 2))
-                  : wn * WTN + 32 * f;
-
-  u32x4 fa[2][FM], fb[2][FN];
-  auto fload = [&](const char* buf, int kk, int slot) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-      fa[slot][i] = *reinterpret_cast<const u32x4*>(buf + a_rd[kk] + i * 32 * 128);
-#pragma unroll
-    for (int f = 0; f < FN; ++f)
-      fb[slot][f] = *reinterpret_cast<const u32x4*>(buf + b_rd[kk] + b_row[f] * 128);
-  };
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const char* cur = smem + (kt & 1) * STAGE;
-    const bool more = kt + 1 < KT;
-    if (more) gload(kt + 1);
-    fload(cur, 0, 0);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (kk + 1 < 4) fload(cur, kk + 1, (kk + 1) & 1);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int f = 0; f < FN; ++f)
-          acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, fa[kk & 1][i]), __builtin_bit_cast(bf16x8, fb[kk & 1][f]),
-              acc[i][f], 0, 0, 0);
-    }
-    if (more) lstore(smem + ((kt + 1) & 1) * STAGE);
-    __syncthreads();
-  }
-
-  // epilogue: lane holds C[8*(r/4) + 4*(lane/32) + r%4][lane % 32] of each fragment
-  const int ccol = lane & 31, crow = (lane >> 5) * 4;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int lr = wm * WTM + 32 * i + 8 * (r >> 2) + crow + (r & 3);
-      if (lr >= tc.nrows) continue;
-      char* crow_ptr = p.C + (int64_t)(tc.row0 + lr) * p.ldc;
-      if (SW) {
-#pragma unroll
-        for (int f = 0; f < FN / 2; ++f) {
-          const float g = acc[i][f][r], u = acc[i][f + FN / 2][r];
-          const float h = g / (1.0f + expf(-g)) * u;
-          const int col = tc.nt * (BN / 2) + wn * (WTN / 2) + 32 * f + ccol;
-          *reinterpret_cast<uint16_t*>(crow_ptr + (int64_t)col * 2) = f32_to_bf16(h);
-        }
-      } else {
-#pragma unroll
-        for (int f = 0; f < FN; ++f) {
-          const int col = tc.nt * BN + wn * WTN + 32 * f + ccol;
-          if (col >= p.N) continue;
-          if (EPI == EPI_LOGITS) {
-            reinterpret_cast<float*>(crow_ptr)[col] =
-                acc[i][f][r] + (p.col_add ? p.col_add[col] : 0.0f);
-          } else {
-            *reinterpret_cast<uint16_t*>(crow_ptr + (int64_t)col * 2) = f32_to_bf16(acc[i][f][r]);
-          }
-        }
-      }
-    }
-  }
-}
-
-
-// ---------------------------------------------------------------------------
-// Large-tile bf16 variant: direct global->LDS buffer loads (16 bytes per lane;
+// Direct-to-LDS bf16 kernel: direct global->LDS buffer loads (16 bytes per lane;
 // a wavefront's load fills 1 KB of LDS, lane l at byte 16*l), STAGES LDS
 // buffers of ROWB/2 K-elements (ROWB bytes per tile row), loads issued
 // STAGES-1 stages ahead, one barrier per stage, MFMA 32x32x16.
@@ -511,14 +339,22 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void grouped_gemm_v2(GemmArgs p
 // 128-byte rows (4 cycles per read, measured), while the plain layout costs 4x
 // (64-byte rows) or 8x (128-byte rows).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz64(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wavefront are outstanding (vmcnt in bits [3:0] and [15:14]; expcnt and
 // lgkmcnt left at their no-wait maxima)
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Workgroup barrier without a memory fence (so outstanding direct-to-LDS loads
+// need not drain), fenced for the compiler: no LDS access may be moved across
+// it, since the barrier is what orders one wave's LDS reads against another
+// wave's loads into the same buffer.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
 
 // one 16-byte-per-lane buffer load straight into LDS at `dst` (+16 * lane)
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, char* dst, uint32_t voff) {
@@ -539,9 +375,8 @@ __device__ __forceinline__ int swz_sel(int r) {
   else return (r >> 2) & M;
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int STAGES, bool SKIP = true, int ROWB = 64,
-          int SWZ = 1>
-__global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_v3(GemmArgs p) {
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int ROWB, int SWZ>
+__global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) {
   constexpr int NT = 64 * WM * WN, NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -606,7 +441,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_v3(GemmArgs p) {
   const int KT = p.K / (ROWB / 2);  // ROWB/2 bf16 per stage
   // Stage kt's loads; stages past the end reload the last one (never read;
   // keeps the number of loads in flight constant).
-#define MOE_V3_ISSUE(kt_)                                                                \
+#define MOE_DMA_ISSUE(kt_)                                                                \
   do {                                                                                   \
     const int kc_ = (kt_) < KT ? (kt_) : KT - 1;                                         \
     char* buf_ = smem + ((kt_) % STAGES) * STAGE;                                        \
@@ -640,19 +475,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_v3(GemmArgs p) {
     b_row[f] = SW ? ((f < FN / 2) ? wn * (WTN / 2) + 32 * f : BN / 2 + wn * (WTN / 2) + 32 * (f - FN / 2))
                   : wn * WTN + 32 * f;
 
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) MOE_V3_ISSUE(s);
-
   // Fragments of this wave whose 32 rows hold at least one valid row; a full
   // tile takes the branch-free loop.
-  const int live = SKIP ? min(FM, max(0, (tc.nrows - wm * WTM + 31) / 32)) : FM;
-#define MOE_V3_MAIN(CHECK)                                                                   \
+  const int live = min(FM, max(0, (tc.nrows - wm * WTM + 31) / 32));
+
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) MOE_DMA_ISSUE(s);
+#define MOE_DMA_MAIN(CHECK)                                                                   \
   for (int kt = 0; kt < KT; ++kt) {                                                          \
     static_assert((STAGES - 2) * (LA + LB) <= 63, "vmcnt range");                            \
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * (LA + LB)));                         \
     __builtin_amdgcn_s_waitcnt(0xC07F);                                                      \
-    __builtin_amdgcn_s_barrier();                                                            \
-    MOE_V3_ISSUE(kt + STAGES - 1);                                                           \
+    lds_barrier();                                                            \
+    MOE_DMA_ISSUE(kt + STAGES - 1);                                                           \
     const char* cur = smem + (kt % STAGES) * STAGE;                                          \
     _Pragma("unroll") for (int kk = 0; kk < KSTEPS; ++kk) {                                  \
       u32x4 fa[FM], fb[FN];                                                                  \
@@ -670,12 +505,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_v3(GemmArgs p) {
     }                                                                                        \
   }
   if (live == FM) {
-    MOE_V3_MAIN(false)
+    MOE_DMA_MAIN(false)
   } else {
-    MOE_V3_MAIN(true)
+    MOE_DMA_MAIN(true)
   }
-#undef MOE_V3_MAIN
-#undef MOE_V3_ISSUE
+#undef MOE_DMA_MAIN
+#undef MOE_DMA_ISSUE
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no LDS load may still be in flight at exit
 
   // epilogue: lane holds C[8*(r/4) + 4*(lane/32) + r%4][lane % 32] of each fragment
@@ -712,205 +547,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_v3(GemmArgs p) {
   }
 }
 
-
-// ---------------------------------------------------------------------------
-// Software-pipelined bf16 variant.  Per stage: KSTEPS MFMA k-steps of 16 bf16
-// (ROWB = 32*KSTEPS bytes of K per row), STAGES LDS buffers filled by direct
-// global->LDS loads issued STAGES-1 stages ahead.  Fragments are double
-// buffered in registers: the reads of k-step kk+1 are interleaved with the
-// MFMAs of k-step kk, and the barrier that publishes the next stage sits in
-// the middle of the current stage's last k-step, so the MFMA pipe keeps
-// working across it.
-// ---------------------------------------------------------------------------
-template <int ROWB>
-__device__ __forceinline__ int swz_row(int r) {
-  if constexpr (ROWB == 128) return (r >> 1) & 7;
-  else return (r >> 2) & 3;
-}
-
-template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int KSTEPS>
-__global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_v4(GemmArgs p) {
-  constexpr int NT = 64 * WM * WN, NW = WM * WN;
-  constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr bool SW = EPI == EPI_SWIGLU;
-  constexpr int ROWB = 32 * KSTEPS;        // bytes of K per row per stage
-  constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
-  constexpr int RPL = 1024 / ROWB;         // rows filled by one wavefront load
-  constexpr int STAGE = (BM + BN) * ROWB;
-  constexpr int LA = BM / RPL / NW, LB = BN / RPL / NW;
-  constexpr int PEND = (STAGES - 2) * (LA + LB);  // loads allowed in flight at a stage switch
-  static_assert(KSTEPS == 2 || KSTEPS == 4, "64- or 128-byte rows");
-  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "whole 32x32 fragments");
-  static_assert(!SW || FN % 2 == 0, "SwiGLU waves hold gate and up fragments in pairs");
-  static_assert(LA * NW * RPL == BM && LB * NW * RPL == BN, "loads must split evenly");
-  static_assert(!SW || (BN / 2) % RPL == 0, "a load is all gate or all up rows");
-  static_assert(STAGES >= 3 && STAGES * STAGE <= 160 * 1024, "LDS budget");
-  static_assert(PEND <= 63, "vmcnt range");
-  extern __shared__ __align__(16) char smem[];
-
-  TileCoord tc;
-  if (!decode_tile<BM>(p, tc)) return;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN, wn = wave % WN;
-  const char* Bg = (p.B_last && tc.grp == p.G - 1) ? p.B_last : p.B + (int64_t)tc.grp * p.b_group;
-  constexpr uint32_t kOut = 0x80000000u;
-  const __amdgpu_buffer_rsrc_t a_rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.A), 0, (int)p.a_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t b_rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Bg), 0, (int)p.b_bytes, 0x00020000);
-
-  // load j of this wave fills tile rows [RPL * (wave + NW * j), +RPL); lane l
-  // fills LDS slot l % CPR of row l / CPR, i.e. logical chunk slot ^ swz(row)
-  const int lr = lane / CPR, lq = lane % CPR;
-  uint32_t a_off[LA], b_off[LB];
-#pragma unroll
-  for (int j = 0; j < LA; ++j) {
-    const int row = RPL * (wave + NW * j) + lr;
-    const int ch = lq ^ swz_row<ROWB>(row);
-    if (row < tc.nrows) {
-      const int arow = p.a_rows ? p.a_rows[tc.row0 + row] : tc.row0 + row;
-      a_off[j] = (uint32_t)arow * (uint32_t)p.lda + ch * 16;
-    } else {
-      a_off[j] = kOut;
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < LB; ++j) {
-    const int row = RPL * (wave + NW * j) + lr;
-    const int ch = lq ^ swz_row<ROWB>(row);
-    int brow;
-    bool ok = true;
-    if (SW) {
-      brow = (RPL * (wave + NW * j) < BN / 2) ? tc.nt * (BN / 2) + row
-                                              : p.up_row + tc.nt * (BN / 2) + (row - BN / 2);
-    } else {
-      brow = tc.nt * BN + row;
-      ok = brow < p.N;
-    }
-    b_off[j] = ok ? (uint32_t)brow * (uint32_t)p.ldb + ch * 16 : kOut;
-  }
-  const int KT = p.K / (ROWB / 2);
-#define MOE_V4_ISSUE(kt_)                                                                 \
-  do {                                                                                    \
-    const int kc_ = (kt_) < KT ? (kt_) : KT - 1;                                          \
-    char* buf_ = smem + ((kt_) % STAGES) * STAGE;                                         \
-    const uint32_t ko_ = (uint32_t)kc_ * ROWB;                                            \
-    _Pragma("unroll") for (int j = 0; j < LA; ++j)                                         \
-        load_lds16(a_rs, buf_ + (RPL * (wave + NW * j)) * ROWB, a_off[j] + ko_);          \
-    _Pragma("unroll") for (int j = 0; j < LB; ++j)                                         \
-        load_lds16(b_rs, buf_ + BM * ROWB + (RPL * (wave + NW * j)) * ROWB, b_off[j] + ko_); \
-  } while (0)
-
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int f = 0; f < FN; ++f)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
-
-  const int fr = lane & 31, fh = lane >> 5, fs = swz_row<ROWB>(fr);
-  int rd[KSTEPS];  // byte offset of this lane's chunk for k-step kk within a fragment row block
-#pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk) rd[kk] = fr * ROWB + (((2 * kk + fh) ^ fs) << 4);
-  int b_row[FN];
-#pragma unroll
-  for (int f = 0; f < FN; ++f)
-    b_row[f] = SW ? ((f < FN / 2) ? wn * (WTN / 2) + 32 * f : BN / 2 + wn * (WTN / 2) + 32 * (f - FN / 2))
-                  : wn * WTN + 32 * f;
-
-  u32x4 fa[2][FM], fb[2][FN];
-#define MOE_V4_READ(buf_, kk_, sl_)                                                        \
-  do {                                                                                     \
-    _Pragma("unroll") for (int i = 0; i < FM; ++i) fa[sl_][i] =                             \
-        *reinterpret_cast<const u32x4*>((buf_) + (wm * WTM + 32 * i) * ROWB + rd[kk_]);    \
-    _Pragma("unroll") for (int f = 0; f < FN; ++f) fb[sl_][f] =                             \
-        *reinterpret_cast<const u32x4*>((buf_) + BM * ROWB + b_row[f] * ROWB + rd[kk_]);   \
-  } while (0)
-#define MOE_V4_MFMA(sl_, i0_, i1_)                                                         \
-  _Pragma("unroll") for (int i = (i0_); i < (i1_); ++i)                                     \
-  _Pragma("unroll") for (int f = 0; f < FN; ++f)                                            \
-    acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[sl_][i]), \
-                                                       __builtin_bit_cast(bf16x8, fb[sl_][f]), \
-                                                       acc[i][f], 0, 0, 0)
-
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) MOE_V4_ISSUE(s);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(PEND));
-  __builtin_amdgcn_s_barrier();
-  MOE_V4_READ(smem, 0, 0);
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const char* cur = smem + (kt % STAGES) * STAGE;
-    const char* nxt = smem + ((kt + 1) % STAGES) * STAGE;
-    // the buffer being refilled held stage kt-1: every wave finished reading it
-    // before the barrier that published stage kt
-    MOE_V4_ISSUE(kt + STAGES - 1);
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      const int sl = kk & 1;
-      if (kk + 1 < KSTEPS) {
-        MOE_V4_READ(cur, kk + 1, sl ^ 1);
-        MOE_V4_MFMA(sl, 0, FM);
-#pragma unroll
-        for (int q = 0; q < FM + FN; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
-      } else {
-        MOE_V4_MFMA(sl, 0, FM / 2);
-        __builtin_amdgcn_sched_barrier(0);
-        // stage kt+1: this wave's loads landed (at most PEND newer ones in
-        // flight), this wave's reads of stage kt returned; the barrier makes
-        // both true for every wave
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(PEND) & 0xC0FF);  // vmcnt(PEND) lgkmcnt(0)
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        if (kt + 1 < KT) MOE_V4_READ(nxt, 0, sl ^ 1);
-        MOE_V4_MFMA(sl, FM / 2, FM);
-      }
-    }
-  }
-#undef MOE_V4_ISSUE
-#undef MOE_V4_READ
-#undef MOE_V4_MFMA
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no LDS load may still be in flight at exit
-
-  const int ccol = lane & 31, crow = (lane >> 5) * 4;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int lrw = wm * WTM + 32 * i + 8 * (r >> 2) + crow + (r & 3);
-      if (lrw >= tc.nrows) continue;
-      char* crow_ptr = p.C + (int64_t)(tc.row0 + lrw) * p.ldc;
-      if (SW) {
-#pragma unroll
-        for (int f = 0; f < FN / 2; ++f) {
-          const float g = acc[i][f][r], u = acc[i][f + FN / 2][r];
-          const float h = g / (1.0f + expf(-g)) * u;
-          const int col = tc.nt * (BN / 2) + wn * (WTN / 2) + 32 * f + ccol;
-          *reinterpret_cast<uint16_t*>(crow_ptr + (int64_t)col * 2) = f32_to_bf16(h);
-        }
-      } else {
-#pragma unroll
-        for (int f = 0; f < FN; ++f) {
-          const int col = tc.nt * BN + wn * WTN + 32 * f + ccol;
-          if (col >= p.N) continue;
-          if (EPI == EPI_LOGITS) {
-            reinterpret_cast<float*>(crow_ptr)[col] =
-                acc[i][f][r] + (p.col_add ? p.col_add[col] : 0.0f);
-          } else {
-            *reinterpret_cast<uint16_t*>(crow_ptr + (int64_t)col * 2) = f32_to_bf16(acc[i][f][r]);
-          }
-        }
-      }
-    }
-  }
-}
 
 }  // namespace gemm
 }  // namespace moe

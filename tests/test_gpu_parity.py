@@ -218,7 +218,9 @@ def test_permute_random(T, k, E, mode):
     ("f32", 16, 64, 8, 2, 128),
     ("f32", 50, 128, 5, 3, 192),
     ("bf16", 300, 256, 5, 2, 192),     # ~120 rows/expert: square tiles, ragged tails
-    ("bf16", 40, 256, 64, 6, 128),     # ~4 rows/expert: skinny tiles
+    ("bf16", 40, 256, 64, 6, 128),     # ~4 rows/expert: 32-row streaming tiles
+    ("bf16", 200, 256, 16, 2, 256),    # ~25 rows/expert: 32-row tiles, some experts span two
+    ("bf16", 40, 256, 64, 6, 192),     # ~4 rows/expert, d_ff not a multiple of 128: 16-row tiles
     ("bf16", 1, 512, 16, 4, 256),      # single token
     ("bf16", 700, 128, 3, 3, 64),      # k = E: every expert gets every token
     ("bf16", 700, 320, 4, 2, 256),     # 256x256 tiles: ragged rows, partial last column tile
