@@ -67,14 +67,14 @@ int tile_bound(int64_t rows, int groups, int bm) {
 }  // namespace
 
 int router_splits(const moe_config& c) {
-  // split K so that a small router GEMM still fills the chip: about 1024 blocks,
-  // each split a whole number of 128-byte K stages; at most 16 partials, which
-  // the top-k kernel sums with all its loads in flight at once
+  // Split K so that a small router GEMM still fills the chip (E = 8 or T = 64
+  // give only a handful of 64x64 tiles), each split a whole number of 128-byte
+  // K stages.  The count depends on d only, never on T: a token's logits are
+  // then summed in the same order whatever batch it comes in.
   if (c.dtype == MOE_F32) return 1;
-  const int tiles = ceil_div(c.T, 64) * ceil_div(c.E, 64);
   const int stages = c.d / 64;
   int s = 1;
-  while (s * 2 <= kMaxRouterSplits && tiles * s < 1024 && stages % (s * 2) == 0) s *= 2;
+  while (s * 2 <= kRouterSplits && stages % (s * 2) == 0) s *= 2;
   return s;
 }
 
@@ -110,10 +110,15 @@ hipError_t launch_router_gemm(const moe_config& c, const void* hidden, const voi
 namespace {
 
 // Tile shape of the grouped expert GEMMs.  Rows per group on average (known on
-// the host from T, k and the group count) picks skinny 16-row tiles for
-// decode-shaped batches; prefill-shaped batches take 256x256 tiles on the
-// deep-pipelined kernel when the shapes allow it (d_ff a multiple of 128 and
-// operands addressable with 31-bit offsets), else 128-row tiles.
+// the host from T, k and the group count) picks 32-row tiles for
+// decode-shaped batches and 256x256 tiles for prefill-shaped ones, both on the
+// direct-to-LDS kernel when the shapes allow it (d_ff a multiple of 128 and
+// operands addressable with 31-bit offsets), else 16- or 128-row tiles on the
+// register-staged kernel.  The two direct-to-LDS shapes accumulate K in the
+// same order (64-element slabs, 16-element MFMA steps, one fp32 accumulator
+// per output), so a row's result does not depend on which of them runs: with
+// the router's T-independent split, the layer output of a token does not
+// depend on the batch it is in.
 enum class FfnTiles { F32_16, BF16_16, BF16_32, BF16_128, BF16_256 };
 
 FfnTiles pick_tiles(const moe_config& c, const ExpertFfnArgs& a) {

@@ -75,8 +75,8 @@ Workspace workspace_layout(const moe_config& c);
 // logits plus the offset; with splits > 1 (bf16 only), `out` is [splits,T,Ep]
 // (Ep = router_part_ld(c), rows padded to 16 bytes) of partial sums over K
 // slices, and the offset is added when the top-k kernel sums them.
-// router_splits() is the split count moe_forward uses (at most kMaxRouterSplits).
-constexpr int kMaxRouterSplits = 16;
+// router_splits() is the split count moe_forward uses (at most kRouterSplits).
+constexpr int kRouterSplits = 8;
 inline int router_part_ld(const moe_config& c) { return align_up(c.E, 4); }
 int router_splits(const moe_config& c);
 hipError_t launch_router_gemm(const moe_config& c, const void* hidden, const void* w_router,

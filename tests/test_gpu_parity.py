@@ -355,3 +355,35 @@ def test_forward_full_size_sampled(name):
         rows = np.unique(np.r_[rows, np.nonzero((ids_np == hot).any(1))[0][:2]])
     res = H.check_layer(lc, inp, out, ids, gates, rows=rows, max_tie_frac=0.2)
     assert res["rows"] - res["ties"] >= n // 2
+
+
+# ----------------------------------------------------------------------------
+# batch invariance: a token's output, ids and gates do not depend on the batch
+# it is computed in ("MoE 架构与路由策略", table dsv4-moe-batch-invariance: the
+# MoE reduction order is fixed, no split-K whose split depends on the batch)
+# ----------------------------------------------------------------------------
+BATCH_INVARIANT = {
+    # the full batch runs 256x256 tiles, the slices 32-row tiles
+    "mixtral_small": CONFIGS["mixtral_prefill"].with_(T=512, d=512, d_ff=1024),
+    "dsv3_groups_shared": CONFIGS["dsv3_prefill"].with_(T=1024, d=256, E=16, k=4, d_ff=128,
+                                                        n_group=4, topk_group=2, group_topk=2),
+    "v4pro_skew": CONFIGS["v4pro_skew_prefill"].with_(T=2048, d=512, E=16, k=4, d_ff=256),
+    "tiny_fp32": CONFIGS["tiny_fp32"].with_(T=64),
+}
+
+
+@pytest.mark.parametrize("name", list(BATCH_INVARIANT))
+def test_forward_batch_invariant(name):
+    lc = BATCH_INVARIANT[name]
+    inp = make_inputs(lc, "cuda")
+    full, full_ids, full_gates = (t.clone() for t in H.gpu_forward(H.cfg_of(lc), inp))
+    T = lc.T
+    for a, b in [(0, 1), (5, 42), (T // 2, min(T, T // 2 + 64)), (T - 3, T)]:
+        sub = dict(inp)
+        sub["hidden"] = inp["hidden"][a:b].contiguous()
+        if inp.get("token_ids") is not None:
+            sub["token_ids"] = inp["token_ids"][a:b].contiguous()
+        out, ids, gates = H.gpu_forward(H.cfg_of(lc, T=b - a), sub)
+        assert torch.equal(ids, full_ids[a:b]), (a, b)
+        assert torch.equal(gates, full_gates[a:b]), (a, b)
+        assert torch.equal(out, full[a:b]), (a, b, (out.float() - full[a:b].float()).abs().max())
