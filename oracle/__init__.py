@@ -44,6 +44,19 @@ def lib():
         L.oracle_layer.argtypes = [I, P, I, I, I, I, I, I, I, I, I, I, I,
                                    P, P, P, P, P, P, I, P, P, P, P, P, P, P, P]
         L.oracle_num_threads.argtypes = []
+        L.oracle_e4m3_decode.argtypes = [C.c_uint8]
+        L.oracle_e4m3_decode.restype = C.c_double
+        L.oracle_e4m3_encode.argtypes = [F]
+        L.oracle_e4m3_encode.restype = C.c_uint8
+        L.oracle_quantize_rows.argtypes = [I, I, P, P, P]
+        L.oracle_quantize_rows.restype = None
+        L.oracle_quantize_blocks.argtypes = [I, I, P, I, P, P]
+        L.oracle_quantize_blocks.restype = None
+        L.oracle_expert_ffn_fp8.argtypes = [I, I, P, P, P, P, P, P, P]
+        L.oracle_expert_ffn_fp8.restype = None
+        L.oracle_layer_fp8.argtypes = [I, P, I, I, I, I, I, I, I, I, I, I, I,
+                                       P, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P, P, P, P]
+        L.oracle_layer_fp8.restype = I
         for name in ("oracle_route", "oracle_hash_route", "oracle_permute",
                      "oracle_layer", "oracle_num_threads"):
             getattr(L, name).restype = I
@@ -218,3 +231,108 @@ def layer(hidden, w_router, w13, w2, k, scoring, rows=None, bias=None,
 
 def num_threads():
     return lib().oracle_num_threads()
+
+
+# ----------------------------------------------------------------------------
+# FP8 (E4M3) experts
+# ----------------------------------------------------------------------------
+def e4m3_decode(codes):
+    """E4M3 codes (uint8 array or int) -> float64 values."""
+    c = np.asarray(codes, np.uint8)
+    f = np.vectorize(lambda v: lib().oracle_e4m3_decode(int(v)), otypes=[np.float64])
+    return f(c)
+
+
+def e4m3_encode(values):
+    """float32 values -> nearest E4M3 codes (ties to even, saturated to +-448)."""
+    v = np.asarray(values, np.float32)
+    f = np.vectorize(lambda x: lib().oracle_e4m3_encode(float(x)), otypes=[np.uint8])
+    return f(v)
+
+
+def quantize_rows(x):
+    """float32 [n, K] (K a multiple of 128) -> (codes uint8 [n, K], scales float32 [n, K/128])."""
+    x = _c(x, np.float32)
+    n, K = x.shape
+    q = np.zeros((n, K), np.uint8)
+    s = np.zeros((n, K // 128), np.float32)
+    lib().oracle_quantize_rows(n, K, _p(x), _p(q), _p(s))
+    return q, s
+
+
+def quantize_blocks(w):
+    """[R, C] float32 or bf16 bits (both multiples of 128) -> (codes uint8 [R, C],
+    scales float32 [R/128, C/128]), one scale per 128x128 tile."""
+    w, dt = _tensor(w)
+    R, Cc = w.shape
+    q = np.zeros((R, Cc), np.uint8)
+    s = np.zeros((R // 128, Cc // 128), np.float32)
+    lib().oracle_quantize_blocks(R, Cc, _p(w), dt, _p(q), _p(s))
+    return q, s
+
+
+def expert_ffn_fp8(xq, xs, w13q, w13s, w2q, w2s):
+    """One FP8 SwiGLU expert on one quantized row (codes xq [d], scales xs [d/128])."""
+    xq, xs = _c(xq, np.uint8), _c(xs, np.float32)
+    w13q, w13s, w2q, w2s = (_c(w13q, np.uint8), _c(w13s, np.float32), _c(w2q, np.uint8),
+                            _c(w2s, np.float32))
+    d = xq.shape[0]
+    d_ff = w13q.shape[0] // 2
+    y = np.zeros(d, np.float64)
+    lib().oracle_expert_ffn_fp8(d, d_ff, _p(xq), _p(xs), _p(w13q), _p(w13s), _p(w2q), _p(w2s),
+                                _p(y))
+    return y
+
+
+def layer_fp8(hidden, w_router, w13q, w13s, w2q, w2s, k, scoring, rows=None, bias=None,
+              logit_offset=None, n_group=1, topk_group=1, group_topk=0, shared=None,
+              route_mode=LEARNED, token_ids=None, tid2eid=None):
+    """The layer with FP8 experts for the listed token rows.  w13q/w13s/w2q/w2s:
+    sequences over experts of per-expert arrays (None where not needed); shared:
+    None or a tuple (w13q, w13s, w2q, w2s).  Returns dict(out, ids, gates, margin)."""
+    h, dt = _tensor(hidden)
+    wr, _ = _tensor(w_router)
+    T, d = h.shape
+    E = wr.shape[0]
+    keep = []
+
+    def ptrs(ws, dtype):
+        arr = (C.c_void_p * E)()
+        for e in range(E):
+            if ws[e] is None:
+                arr[e] = None
+            else:
+                a = _c(ws[e], dtype)
+                keep.append(a)
+                arr[e] = a.ctypes.data
+        return arr
+
+    pq13, ps13 = ptrs(w13q, np.uint8), ptrs(w13s, np.float32)
+    pq2, ps2 = ptrs(w2q, np.uint8), ptrs(w2s, np.float32)
+    first = next(w for w in w13q if w is not None)
+    d_ff = np.asarray(first).shape[0] // 2
+    sh = [None] * 4
+    if shared is not None:
+        sh = [_c(shared[0], np.uint8), _c(shared[1], np.float32), _c(shared[2], np.uint8),
+              _c(shared[3], np.float32)]
+    r = np.arange(T, dtype=np.int32) if rows is None else _c(rows, np.int32)
+    n = len(r)
+    out = np.zeros((n, d), np.float64)
+    ids = np.zeros((n, k), np.int32)
+    gates = np.zeros((n, k), np.float32)
+    margin = np.zeros(n, np.float32)
+    b = None if bias is None else _c(bias, np.float32)
+    off = None if logit_offset is None else _c(logit_offset, np.float32)
+    tok = None if token_ids is None else _c(token_ids, np.int32)
+    tab = None if tid2eid is None else _c(tid2eid, np.int32)
+    vocab = 0 if tab is None else tab.shape[0]
+    rc = lib().oracle_layer_fp8(n, _p(r), d, E, k, d_ff, 0 if shared is None else 1, dt,
+                                scoring, route_mode, n_group, topk_group, group_topk, _p(h),
+                                _p(wr), _p(b), _p(off), _p(tok), _p(tab), vocab,
+                                C.cast(pq13, C.c_void_p), C.cast(ps13, C.c_void_p),
+                                C.cast(pq2, C.c_void_p), C.cast(ps2, C.c_void_p),
+                                _p(sh[0]), _p(sh[1]), _p(sh[2]), _p(sh[3]),
+                                _p(out), _p(ids), _p(gates), _p(margin))
+    if rc:
+        raise ValueError("oracle_layer_fp8 rejected its arguments (missing expert weights?)")
+    return dict(out=out, ids=ids, gates=gates, margin=margin)

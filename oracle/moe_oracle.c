@@ -43,6 +43,19 @@
  *    affinities of the token's logits at those ids, renormalised (bias unused).
  *  - shared experts are added with weight 1; no routed scaling factor.
  *
+ *  - FP8 experts ([P2] FP4 QAT section and table dsv4-moe-fp4-vs-fp8: E4M3 with
+ *    one scale per 128x128 weight tile; [P2] table dsv4-moe-stages: activation
+ *    then FP8 cast between Linear-1 and Linear-2; [P3] 五.2: FP8 dispatch; [P3]
+ *    closing section: promotion to FP32 accumulation every 128 elements).  The
+ *    pages fix the weight tile; activations are read as one scale per token per
+ *    128 channels (1x128, the K blocks of the weight tiles).  A scale is the
+ *    group's max |x| / 448 in float, a code is E4M3 of x / scale rounded to
+ *    nearest-even with the division in float (the precision the GPU decides
+ *    in), saturated to +-448; an all-zero group has scale 0 and zero codes.
+ *    Products are summed per 128-element K block and each block sum is scaled
+ *    by the two block scales (in double here).  h = SiLU(g)*u is rounded to
+ *    float before it is quantized.
+ *
  * Pins: the tests check this file against the pages' worked examples (router
  * example, two-token toy, dispatch/combine toy, EP4 per-expert counts), closed
  * forms of the affinities, invariants of routing and permutation, a dense SwiGLU
@@ -352,6 +365,34 @@ void oracle_logits(int n, const int32_t *rows, int d, int E, const void *hidden,
     }
 }
 
+/* Route listed token q: logits (double, then float), learned or hash routing.
+   Returns the routing status; ids/gates/margin as route_one. */
+static int route_listed(int q, const int32_t *rows, int d, int E, int k, int scoring,
+                        int route_mode, int n_group, int topk_group, int group_topk,
+                        const void *hidden, const void *w_router, int dtype,
+                        const float *bias, const float *logit_offset,
+                        const int32_t *token_ids, const int32_t *tid2eid, int vocab,
+                        int32_t *ids, float *gates, float *margin)
+{
+    double *lg = malloc(sizeof(double) * E);
+    float *lf = malloc(sizeof(float) * E);
+    size_t t = (size_t)rows[q];
+    oracle_logits(1, rows + q, d, E, hidden, w_router, dtype, logit_offset, lg);
+    for (int e = 0; e < E; ++e)
+        lf[e] = (float)lg[e];
+    int rc;
+    *margin = INFINITY;
+    if (route_mode == 1)
+        rc = oracle_hash_route(1, E, k, scoring, lf, token_ids + t, tid2eid, vocab, ids,
+                               gates);
+    else
+        rc = route_one(E, k, scoring, n_group, topk_group, group_topk, lf, bias, ids, gates,
+                       margin);
+    free(lg);
+    free(lf);
+    return rc;
+}
+
 /* ---------------------------------------------------------------------------
  * The whole layer for a list of tokens ([P3] 二.2 and 二.3):
  *   y_t = sum_j g[t,j] * FFN_{ids[t,j]}(x_t) + sum_s FFN^shared_s(x_t)
@@ -376,23 +417,14 @@ int oracle_layer(int n, const int32_t *rows, int d, int E, int k, int d_ff,
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
     for (int q = 0; q < n; ++q) {
         int32_t ids[64];
-        float gates[64], margin = INFINITY;
-        double *lg = malloc(sizeof(double) * E);
-        float *lf = malloc(sizeof(float) * E);
+        float gates[64], margin;
         double *x = malloc(sizeof(double) * d);
         double *y = malloc(sizeof(double) * d);
         double *o = out + (size_t)q * d;
         size_t t = (size_t)rows[q];
-        oracle_logits(1, rows + q, d, E, hidden, w_router, dtype, logit_offset, lg);
-        for (int e = 0; e < E; ++e)
-            lf[e] = (float)lg[e];
-        int rc;
-        if (route_mode == 1)
-            rc = oracle_hash_route(1, E, k, scoring, lf, token_ids + t, tid2eid,
-                                   vocab, ids, gates);
-        else
-            rc = route_one(E, k, scoring, n_group, topk_group, group_topk, lf,
-                           bias, ids, gates, &margin);
+        int rc = route_listed(q, rows, d, E, k, scoring, route_mode, n_group, topk_group,
+                              group_topk, hidden, w_router, dtype, bias, logit_offset,
+                              token_ids, tid2eid, vocab, ids, gates, &margin);
         for (int i = 0; i < d; ++i) {
             x[i] = elem(hidden, t * d + i, dtype);
             o[i] = 0.0;
@@ -421,9 +453,219 @@ int oracle_layer(int n, const int32_t *rows, int d, int E, int k, int d_ff,
         }
         if (margin_out)
             margin_out[q] = margin;
-        free(lg);
-        free(lf);
         free(x);
+        free(y);
+    }
+    return bad ? -1 : 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * FP8 E4M3 ([P2] table dsv4-moe-fp4-vs-fp8: 4 exponent bits, 3 mantissa bits).
+ * Code layout (the OCP "E4M3FN" encoding): sign bit, exponent field E (bias 7),
+ * mantissa field m.  E = 0: m * 2^-9 (subnormal); E = 1..15: (1 + m/8) * 2^(E-7),
+ * except E = 15, m = 7, which is NaN; there are no infinities, so the largest
+ * finite magnitude is (1 + 6/8) * 2^8 = 448.
+ * ------------------------------------------------------------------------- */
+double oracle_e4m3_decode(uint8_t c)
+{
+    int E = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (E == 15 && m == 7)
+        return NAN;
+    v = E == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, E - 7);
+    return (c & 0x80) ? -v : v;
+}
+
+/* nearest code to a finite float, ties to the even mantissa; magnitudes at or
+   past 448 give +-448 */
+uint8_t oracle_e4m3_encode(float v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs((double)v);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    if (a < ldexp(1.0, -6)) /* subnormal range: multiples of 2^-9 (8 * 2^-9 is code 0x08) */
+        return sign | (uint8_t)nearbyint(a * 512.0);
+    int e;
+    double fr = frexp(a, &e); /* a = (2 fr) * 2^(e-1), 2 fr in [1, 2) */
+    double m = nearbyint((2.0 * fr - 1.0) * 8.0);
+    int E = e - 1 + 7;
+    if (m == 8.0) {
+        m = 0.0;
+        ++E;
+    }
+    unsigned code = ((unsigned)E << 3) | (unsigned)m;
+    return sign | (uint8_t)(code > 0x7E ? 0x7E : code);
+}
+
+static uint8_t quantize_one(float x, float scale)
+{
+    if (scale == 0.0f)
+        return 0;
+    float v = x / scale;
+    v = v > 448.0f ? 448.0f : (v < -448.0f ? -448.0f : v);
+    return oracle_e4m3_encode(v);
+}
+
+/* Rows of a float [n, K] matrix in groups of 128 columns (the 1x128 reading for
+   activations): s[r, g] = max |x| / 448 over the group, q = E4M3(x / s). */
+void oracle_quantize_rows(int n, int K, const float *x, uint8_t *q, float *s)
+{
+    int G = K / 128;
+    for (int r = 0; r < n; ++r)
+        for (int g = 0; g < G; ++g) {
+            const float *xr = x + (size_t)r * K + (size_t)g * 128;
+            float amax = 0.0f;
+            for (int i = 0; i < 128; ++i)
+                amax = fmaxf(amax, fabsf(xr[i]));
+            float sc = amax / 448.0f;
+            s[(size_t)r * G + g] = sc;
+            for (int i = 0; i < 128; ++i)
+                q[(size_t)r * K + (size_t)g * 128 + i] = quantize_one(xr[i], sc);
+        }
+}
+
+/* A [R, C] weight matrix (float or bf16) in 128x128 tiles, one scale per tile
+   ([P2] FP4 QAT section: FP8 quantized per 128x128 tile): s[R/128, C/128]. */
+void oracle_quantize_blocks(int R, int C, const void *w, int dtype, uint8_t *q, float *s)
+{
+    int GC = C / 128;
+    for (int br = 0; br < R / 128; ++br)
+        for (int bc = 0; bc < GC; ++bc) {
+            float amax = 0.0f;
+            for (int i = 0; i < 128; ++i)
+                for (int j = 0; j < 128; ++j) {
+                    size_t at = (size_t)(br * 128 + i) * C + (size_t)bc * 128 + j;
+                    amax = fmaxf(amax, fabsf((float)elem(w, at, dtype)));
+                }
+            float sc = amax / 448.0f;
+            s[(size_t)br * GC + bc] = sc;
+            for (int i = 0; i < 128; ++i)
+                for (int j = 0; j < 128; ++j) {
+                    size_t at = (size_t)(br * 128 + i) * C + (size_t)bc * 128 + j;
+                    q[at] = quantize_one((float)elem(w, at, dtype), sc);
+                }
+        }
+}
+
+/* sum_kb sa[kb] * sb[kb] * sum_{k in kb} dec(a_k) dec(b_k), in double: the dot
+   product of two FP8 vectors of length K with one scale per 128 elements each */
+static double dot_fp8(int K, const uint8_t *a, const float *sa, const uint8_t *b,
+                      const float *sb)
+{
+    double acc = 0.0;
+    for (int kb = 0; kb < K / 128; ++kb) {
+        double part = 0.0;
+        for (int i = kb * 128; i < kb * 128 + 128; ++i)
+            part += oracle_e4m3_decode(a[i]) * oracle_e4m3_decode(b[i]);
+        acc += (double)sa[kb] * (double)sb[kb] * part;
+    }
+    return acc;
+}
+
+/* ---------------------------------------------------------------------------
+ * One SwiGLU expert with FP8 operands.  x: the token's codes xq[d] and scales
+ * xs[d/128]; w13q [2 d_ff, d] with tile scales w13s [2 d_ff/128, d/128]; w2q
+ * [d, d_ff] with w2s [d/128, d_ff/128].  h = SiLU(g) * u is rounded to float,
+ * quantized in 1x128 groups, and the down projection reads those codes.
+ * ------------------------------------------------------------------------- */
+void oracle_expert_ffn_fp8(int d, int d_ff, const uint8_t *xq, const float *xs,
+                           const uint8_t *w13q, const float *w13s, const uint8_t *w2q,
+                           const float *w2s, double *y)
+{
+    int Gd = d / 128, Gf = d_ff / 128;
+    float *h = malloc(sizeof(float) * d_ff);
+    uint8_t *hq = malloc(d_ff);
+    float *hs = malloc(sizeof(float) * Gf);
+    float *sb = malloc(sizeof(float) * (Gd > Gf ? Gd : Gf));
+    for (int f = 0; f < d_ff; ++f) {
+        for (int kb = 0; kb < Gd; ++kb)
+            sb[kb] = w13s[(size_t)(f / 128) * Gd + kb];
+        double g = dot_fp8(d, xq, xs, w13q + (size_t)f * d, sb);
+        for (int kb = 0; kb < Gd; ++kb)
+            sb[kb] = w13s[(size_t)((d_ff + f) / 128) * Gd + kb];
+        double u = dot_fp8(d, xq, xs, w13q + (size_t)(d_ff + f) * d, sb);
+        h[f] = (float)(g / (1.0 + exp(-g)) * u);
+    }
+    oracle_quantize_rows(1, d_ff, h, hq, hs);
+    for (int o = 0; o < d; ++o) {
+        for (int kb = 0; kb < Gf; ++kb)
+            sb[kb] = w2s[(size_t)(o / 128) * Gf + kb];
+        y[o] = dot_fp8(d_ff, hq, hs, w2q + (size_t)o * d_ff, sb);
+    }
+    free(h);
+    free(hq);
+    free(hs);
+    free(sb);
+}
+
+/* ---------------------------------------------------------------------------
+ * The layer with FP8 experts: routing exactly as oracle_layer (from the bf16 or
+ * float hidden states and router weight); each listed token's hidden row is
+ * quantized (1x128, [P3] 五.2 FP8 dispatch) and goes through the FP8 experts;
+ * the gated sum is formed in double.  w13q/w13s/w2q/w2s: per-expert pointers
+ * (NULL for experts no listed token selects); shared expert likewise.
+ * ------------------------------------------------------------------------- */
+int oracle_layer_fp8(int n, const int32_t *rows, int d, int E, int k, int d_ff,
+                     int n_shared, int dtype, int scoring, int route_mode, int n_group,
+                     int topk_group, int group_topk, const void *hidden,
+                     const void *w_router, const float *bias, const float *logit_offset,
+                     const int32_t *token_ids, const int32_t *tid2eid, int vocab,
+                     const uint8_t *const *w13q, const float *const *w13s,
+                     const uint8_t *const *w2q, const float *const *w2s,
+                     const uint8_t *w13q_sh, const float *w13s_sh, const uint8_t *w2q_sh,
+                     const float *w2s_sh, double *out, int32_t *ids_out, float *gates_out,
+                     float *margin_out)
+{
+    int bad = 0;
+    if (k < 1 || k > 64 || k > E || n_shared < 0 || n_shared > 1 || d % 128 || d_ff % 128)
+        return -1;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int q = 0; q < n; ++q) {
+        int32_t ids[64];
+        float gates[64], margin;
+        float *xf = malloc(sizeof(float) * d);
+        uint8_t *xq = malloc(d);
+        float *xs = malloc(sizeof(float) * (d / 128));
+        double *y = malloc(sizeof(double) * d);
+        double *o = out + (size_t)q * d;
+        size_t t = (size_t)rows[q];
+        int rc = route_listed(q, rows, d, E, k, scoring, route_mode, n_group, topk_group,
+                              group_topk, hidden, w_router, dtype, bias, logit_offset,
+                              token_ids, tid2eid, vocab, ids, gates, &margin);
+        for (int i = 0; i < d; ++i) {
+            xf[i] = (float)elem(hidden, t * d + i, dtype);
+            o[i] = 0.0;
+        }
+        oracle_quantize_rows(1, d, xf, xq, xs);
+        for (int j = 0; !rc && j < k; ++j) {
+            int e = ids[j];
+            if (!w13q[e] || !w13s[e] || !w2q[e] || !w2s[e]) {
+                rc = -1;
+                break;
+            }
+            oracle_expert_ffn_fp8(d, d_ff, xq, xs, w13q[e], w13s[e], w2q[e], w2s[e], y);
+            for (int i = 0; i < d; ++i)
+                o[i] += (double)gates[j] * y[i];
+        }
+        if (!rc && n_shared == 1) {
+            oracle_expert_ffn_fp8(d, d_ff, xq, xs, w13q_sh, w13s_sh, w2q_sh, w2s_sh, y);
+            for (int i = 0; i < d; ++i)
+                o[i] += y[i];
+        }
+        if (rc)
+            bad = 1;
+        for (int j = 0; j < k; ++j) {
+            if (ids_out)
+                ids_out[(size_t)q * k + j] = rc ? -1 : ids[j];
+            if (gates_out)
+                gates_out[(size_t)q * k + j] = rc ? 0.0f : gates[j];
+        }
+        if (margin_out)
+            margin_out[q] = margin;
+        free(xf);
+        free(xq);
+        free(xs);
         free(y);
     }
     return bad ? -1 : 0;
