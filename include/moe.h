@@ -170,6 +170,69 @@ int moe_forward(const moe_config *cfg, const void *hidden, const void *w_router,
                 int32_t *topk_ids_out, float *topk_weights_out, void *workspace,
                 size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * FP8 experts.  Codes are E4M3 (the OCP "FN" encoding: sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits, no infinities, largest finite 448; one byte each)
+ * with float32 scales ("MoE 架构与路由策略", FP4 QAT section and table
+ * dsv4-moe-fp4-vs-fp8: E4M3 with one scale per 128x128 weight tile; table
+ * dsv4-moe-stages: the FP8 cast after the SwiGLU activation, between Linear-1
+ * and Linear-2; "MoE 的算量与通信" 五.2: FP8 dispatch, BF16 combine).
+ *   Weights: w13q [E, 2*d_ff, d] uint8 with w13s [E, 2*d_ff/128, d/128] float32,
+ *            w2q [E, d, d_ff] with w2s [E, d/128, d_ff/128]: one scale per
+ *            128x128 tile (row-major over tiles).  Shared expert: one expert's worth.
+ *   Activations (hidden rows before Linear-1, h after the activation): one scale
+ *            per row per 128 columns: codes [rows, K], scales [rows, K/128].
+ *   A group's scale is max |x| / 448 in float32 and its codes are E4M3(x / scale)
+ *   (float32 division, nearest-even, saturated to +-448); an all-zero group has
+ *   scale 0 and zero codes.  A dot product sums each 128-element K block, scales
+ *   the block sum by the two block scales and accumulates in float32.
+ * The FP8 entry points need cfg->dtype == MOE_BF16 (hidden, router weight,
+ * expert_out and out are bfloat16; the router stays bfloat16) and d, d_ff
+ * multiples of 128 (else MOE_ERR_UNSUPPORTED), and every operand smaller than
+ * 2 GiB.  Workspace: moe_workspace_size covers them. */
+
+/* Quantize the rows of x [n, K] (in_dtype MOE_F32 or MOE_BF16) in groups of 128
+ * columns: q [n, K] uint8 codes, scales [n, K/128].  K a multiple of 128 (else
+ * MOE_ERR_UNSUPPORTED).  Needs no workspace; n == 0 queues nothing. */
+int moe_quantize_fp8_rows(int n, int K, int in_dtype, const void *x, uint8_t *q, float *scales,
+                          void *stream);
+
+/* Quantize a matrix w [R, C] (in_dtype) in 128x128 tiles: q [R, C] uint8,
+ * scales [R/128, C/128] (row-major over tiles).  R and C multiples of 128.  For
+ * stacked expert weights [E, R, C] pass E*R rows.  Needs no workspace. */
+int moe_quantize_fp8_blocks(int R, int C, int in_dtype, const void *w, uint8_t *q,
+                            float *scales, void *stream);
+
+/* FP8 Linear-1 with the activation and the FP8 cast fused: for every expert e and
+ * dispatch row r in [expert_offsets[e], expert_offsets[e+1]),
+ *   h = SiLU(W1_e x) (.) W3_e x in float32, x = the codes xq[sorted_token_ids[r]]
+ *   with their scales; hq[r], hs[r] = the 128-column-group quantization of h.
+ * xq [T, d], xs [T, d/128]; hq [T*k, d_ff] uint8; hs [T*k, d_ff/128]. */
+int moe_expert_up_fp8(const moe_config *cfg, const uint8_t *xq, const float *xs,
+                      const int32_t *sorted_token_ids, const int32_t *expert_offsets,
+                      const uint8_t *w13q, const float *w13s, uint8_t *hq, float *hs,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* FP8 Linear-2: expert_out[r] = W2_e h[r] for the same rows, bfloat16 rounded
+ * once from float32.  hq [T*k, d_ff], hs [T*k, d_ff/128]; expert_out [T*k, d]. */
+int moe_expert_down_fp8(const moe_config *cfg, const uint8_t *hq, const float *hs,
+                        const int32_t *expert_offsets, const uint8_t *w2q, const float *w2s,
+                        void *expert_out, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/* The whole layer with FP8 experts: route (bfloat16 router, as moe_forward),
+ * quantize the hidden rows, permute, FP8 grouped experts (routed and shared in
+ * the same launches), combine (float32 sum, bfloat16 out).  The four shared
+ * arguments are required when cfg->n_shared == 1. */
+int moe_forward_fp8(const moe_config *cfg, const void *hidden, const void *w_router,
+                    const float *logit_offset, const float *bias, const int32_t *token_ids,
+                    const int32_t *tid2eid, const uint8_t *w13q, const float *w13s,
+                    const uint8_t *w2q, const float *w2s, const uint8_t *w13q_shared,
+                    const float *w13s_shared, const uint8_t *w2q_shared,
+                    const float *w2s_shared, void *out, int32_t *topk_ids_out,
+                    float *topk_weights_out, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
 /* Static description of a status code. */
 const char *moe_strerror(int status);
 

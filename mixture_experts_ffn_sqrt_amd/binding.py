@@ -21,7 +21,9 @@ MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SQRTSOFTPLUS = 0, 1, 2
 MOE_ROUTE_LEARNED, MOE_ROUTE_HASH = 0, 1
 
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_up",
-           "moe_expert_down", "moe_combine", "moe_forward", "moe_strerror")
+           "moe_expert_down", "moe_combine", "moe_forward", "moe_quantize_fp8_rows",
+           "moe_quantize_fp8_blocks", "moe_expert_up_fp8", "moe_expert_down_fp8",
+           "moe_forward_fp8", "moe_strerror")
 
 
 class MoeError(RuntimeError):
@@ -70,6 +72,11 @@ def load_library(path: str = LIB_PATH):
     L.moe_expert_down.argtypes = [cfg, P, P, P, P, P, S, P]
     L.moe_combine.argtypes = [cfg, P, P, P, P, P, P]
     L.moe_forward.argtypes = [cfg, P, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
+    L.moe_quantize_fp8_rows.argtypes = [I, I, I, P, P, P, P]
+    L.moe_quantize_fp8_blocks.argtypes = [I, I, I, P, P, P, P]
+    L.moe_expert_up_fp8.argtypes = [cfg, P, P, P, P, P, P, P, P, P, S, P]
+    L.moe_expert_down_fp8.argtypes = [cfg, P, P, P, P, P, P, P, S, P]
+    L.moe_forward_fp8.argtypes = [cfg] + [P] * 18 + [S, P]
     L.moe_strerror.argtypes = [I]
     L.moe_strerror.restype = C.c_char_p
     for n in EXPORTS[:-1]:
@@ -239,6 +246,107 @@ def moe_forward(cfg, hidden, w_router, logit_offset, bias, token_ids, tid2eid, w
     _check("moe_forward", load_library().moe_forward(*args))
 
 
+_IN_DTYPES = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
+
+
+def moe_quantize_fp8_rows(x, q, scales, stream=None):
+    """x [n, K] float32/bfloat16 -> q [n, K] uint8 E4M3 codes, scales [n, K/128]."""
+    if x.dtype not in _IN_DTYPES:
+        raise ValueError("x must be float32 or bfloat16, got %s" % x.dtype)
+    n, K = x.shape
+    args = [n, K, _IN_DTYPES[x.dtype], _t("x", x, (n, K), x.dtype),
+            _t("q", q, (n, K), torch.uint8), _t("scales", scales, (n, K // 128), torch.float32),
+            _stream(stream)]
+    _check("moe_quantize_fp8_rows", load_library().moe_quantize_fp8_rows(*args))
+
+
+def moe_quantize_fp8_blocks(w, q, scales, stream=None):
+    """w [R, C] (or [E, R, C], quantized as E*R rows) -> codes of the same shape,
+    scales [R/128, C/128] (or [E, R/128, C/128])."""
+    if w.dtype not in _IN_DTYPES:
+        raise ValueError("w must be float32 or bfloat16, got %s" % w.dtype)
+    C_ = w.shape[-1]
+    R = w.numel() // C_ if C_ else 0
+    sshape = tuple(w.shape[:-2]) + (w.shape[-2] // 128, C_ // 128)
+    args = [R, C_, _IN_DTYPES[w.dtype], _t("w", w, tuple(w.shape), w.dtype),
+            _t("q", q, tuple(w.shape), torch.uint8), _t("scales", scales, sshape, torch.float32),
+            _stream(stream)]
+    _check("moe_quantize_fp8_blocks", load_library().moe_quantize_fp8_blocks(*args))
+
+
+def moe_expert_up_fp8(cfg, xq, xs, sorted_token_ids, expert_offsets, w13q, w13s, hq, hs,
+                      workspace, stream=None):
+    T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
+    u8, f32 = torch.uint8, torch.float32
+    args = [C.byref(cfg),
+            _t("xq", xq, (T, d), u8), _t("xs", xs, (T, d // 128), f32),
+            _t("sorted_token_ids", sorted_token_ids, (T * k,), torch.int32),
+            _t("expert_offsets", expert_offsets, (E + 1,), torch.int32),
+            _t("w13q", w13q, (E, 2 * F, d), u8), _t("w13s", w13s, (E, 2 * F // 128, d // 128), f32),
+            _t("hq", hq, (T * k, F), u8), _t("hs", hs, (T * k, F // 128), f32),
+            *_ws(cfg, workspace), _stream(stream)]
+    _check("moe_expert_up_fp8", load_library().moe_expert_up_fp8(*args))
+
+
+def moe_expert_down_fp8(cfg, hq, hs, expert_offsets, w2q, w2s, expert_out, workspace,
+                        stream=None):
+    T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
+    u8, f32 = torch.uint8, torch.float32
+    args = [C.byref(cfg),
+            _t("hq", hq, (T * k, F), u8), _t("hs", hs, (T * k, F // 128), f32),
+            _t("expert_offsets", expert_offsets, (E + 1,), torch.int32),
+            _t("w2q", w2q, (E, d, F), u8), _t("w2s", w2s, (E, d // 128, F // 128), f32),
+            _t("expert_out", expert_out, (T * k, d), torch.bfloat16),
+            *_ws(cfg, workspace), _stream(stream)]
+    _check("moe_expert_down_fp8", load_library().moe_expert_down_fp8(*args))
+
+
+def moe_forward_fp8(cfg, hidden, w_router, logit_offset, bias, token_ids, tid2eid, w13q, w13s,
+                    w2q, w2s, w13q_shared, w13s_shared, w2q_shared, w2s_shared, out,
+                    topk_ids_out, topk_weights_out, workspace, stream=None):
+    T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
+    bf, u8, f32 = torch.bfloat16, torch.uint8, torch.float32
+    hsh = cfg.route_mode == MOE_ROUTE_HASH
+    sh = bool(cfg.n_shared)
+    args = [C.byref(cfg),
+            _t("hidden", hidden, (T, d), bf), _t("w_router", w_router, (E, d), bf),
+            _t("logit_offset", logit_offset, (E,), f32, False),
+            _t("bias", bias, (E,), f32, False),
+            _t("token_ids", token_ids, (T,), torch.int32, hsh),
+            _t("tid2eid", tid2eid, (cfg.vocab, k), torch.int32, hsh),
+            _t("w13q", w13q, (E, 2 * F, d), u8), _t("w13s", w13s, (E, 2 * F // 128, d // 128), f32),
+            _t("w2q", w2q, (E, d, F), u8), _t("w2s", w2s, (E, d // 128, F // 128), f32),
+            _t("w13q_shared", w13q_shared, (2 * F, d), u8, sh),
+            _t("w13s_shared", w13s_shared, (2 * F // 128, d // 128), f32, sh),
+            _t("w2q_shared", w2q_shared, (d, F), u8, sh),
+            _t("w2s_shared", w2s_shared, (d // 128, F // 128), f32, sh),
+            _t("out", out, (T, d), bf),
+            _t("topk_ids_out", topk_ids_out, (T, k), torch.int32, False),
+            _t("topk_weights_out", topk_weights_out, (T, k), f32, False),
+            *_ws(cfg, workspace), _stream(stream)]
+    _check("moe_forward_fp8", load_library().moe_forward_fp8(*args))
+
+
+def quantize_fp8_weights(inp, stream=None):
+    """FP8 copies of the expert weights of an input dict (w13, w2 and the shared
+    expert's), quantized on the GPU in 128x128 tiles: returns a dict with w13q,
+    w13s, w2q, w2s (and *_shared when present)."""
+    out = {}
+    for name in ("w13", "w2", "w13_shared", "w2_shared"):
+        w = inp.get(name)
+        if w is None:
+            continue
+        q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+        s = torch.empty(tuple(w.shape[:-2]) + (w.shape[-2] // 128, w.shape[-1] // 128),
+                        dtype=torch.float32, device=w.device)
+        moe_quantize_fp8_blocks(w, q, s, stream)
+        base = name.replace("_shared", "")
+        suffix = "_shared" if name.endswith("_shared") else ""
+        out[base + "q" + suffix] = q
+        out[base + "s" + suffix] = s
+    return out
+
+
 def moe_strerror(status: int) -> str:
     return load_library().moe_strerror(int(status)).decode()
 
@@ -259,4 +367,14 @@ class MoELayer:
         moe_forward(self.cfg, i["hidden"], i["w_router"], i.get("logit_offset"), i.get("bias"),
                     i.get("token_ids"), i.get("tid2eid"), i["w13"], i["w2"], i.get("w13_shared"),
                     i.get("w2_shared"), self.out, self.ids, self.gates, self.workspace, stream)
+        return self.out
+
+    def forward_fp8(self, fp8, stream=None):
+        """The layer with FP8 experts; fp8 = quantize_fp8_weights(inputs)."""
+        i = self.inp
+        moe_forward_fp8(self.cfg, i["hidden"], i["w_router"], i.get("logit_offset"), i.get("bias"),
+                        i.get("token_ids"), i.get("tid2eid"), fp8["w13q"], fp8["w13s"],
+                        fp8["w2q"], fp8["w2s"], fp8.get("w13q_shared"), fp8.get("w13s_shared"),
+                        fp8.get("w2q_shared"), fp8.get("w2s_shared"), self.out, self.ids,
+                        self.gates, self.workspace, stream)
         return self.out

@@ -31,8 +31,13 @@ Workspace workspace_layout(const moe_config& c) {
   w.sorted_tok = take(P * 4);
   w.sorted_w = take(R * 4);
   w.dispatch = take(R * 4);
-  w.H = take(P * c.d_ff * es);
+  // H holds the bf16/f32 intermediate, or the FP8 codes followed by their scales
+  const int64_t h_codes = align_up(P * c.d_ff, 256);
+  w.H = take(std::max(P * c.d_ff * es, h_codes + P * (c.d_ff / 128) * 4));
+  w.hs = w.H + h_codes;
   w.Y = take(P * c.d * es);
+  w.xq = take(T * c.d);
+  w.xs = take(T * (c.d / 128) * 4);
   w.total = off;
   return w;
 }
@@ -70,6 +75,21 @@ int check_cfg(const moe_config* c) {
 }
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// The FP8 entry points: bf16 activations, 128-multiples, and operands the
+// buffer-load kernels address with 31-bit offsets.
+int check_fp8(const moe_config* c) {
+  const int st = check_cfg(c);
+  if (st) return st;
+  if (c->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (c->d % 128 || c->d_ff % 128) return MOE_ERR_UNSUPPORTED;
+  const int64_t lim = int64_t(1) << 31;
+  const int64_t T = c->T, d = c->d, F = c->d_ff;
+  const int64_t P = T * (c->k + c->n_shared);
+  if (T * d >= lim || P * F >= lim || 2 * F * d >= lim || P * (F / 128) * 4 >= lim)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
 
 template <typename T>
 T* at(void* ws, int64_t off) {
@@ -285,6 +305,167 @@ int moe_forward(const moe_config* cfg, const void* hidden, const void* w_router,
   const int64_t es = c.dtype == MOE_F32 ? 4 : 2;
   const char* shared_rows = c.n_shared ? at<char>(workspace, w.Y) + (int64_t)R * c.d * es : nullptr;
   return hip_status(launch_combine(c, a.Y, dispatch, gates, shared_rows, out, s));
+}
+
+int moe_quantize_fp8_rows(int n, int K, int in_dtype, const void* x, uint8_t* q, float* scales,
+                          void* stream) {
+  if (n < 0 || K <= 0) return MOE_ERR_INVALID_ARG;
+  if (K % 128) return MOE_ERR_UNSUPPORTED;
+  if (in_dtype != MOE_F32 && in_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (n == 0) return MOE_OK;
+  if (!x || !q || !scales) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_quantize_rows(n, K, in_dtype, x, q, scales,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int moe_quantize_fp8_blocks(int R, int C, int in_dtype, const void* w, uint8_t* q, float* scales,
+                            void* stream) {
+  if (R < 0 || C < 0) return MOE_ERR_INVALID_ARG;
+  if (R % 128 || C % 128) return MOE_ERR_UNSUPPORTED;
+  if (in_dtype != MOE_F32 && in_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (R == 0 || C == 0) return MOE_OK;
+  if (!w || !q || !scales) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_quantize_blocks(R, C, in_dtype, w, q, scales,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+Fp8FfnArgs fp8_args_of(const ExpertFfnArgs& a) {
+  Fp8FfnArgs f{};
+  f.sorted_tok = a.sorted_tok;
+  f.g_begin = a.g_begin;
+  f.g_end = a.g_end;
+  f.tile_prefix = a.tile_prefix;
+  f.n_groups = a.n_groups;
+  f.rows_bound = a.rows_bound;
+  f.routed_groups = a.routed_groups;
+  return f;
+}
+}  // namespace
+
+int moe_expert_up_fp8(const moe_config* cfg, const uint8_t* xq, const float* xs,
+                      const int32_t* sorted_token_ids, const int32_t* expert_offsets,
+                      const uint8_t* w13q, const float* w13s, uint8_t* hq, float* hs,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_fp8(cfg);
+  if (st) return st;
+  const moe_config& c = *cfg;
+  if (!xq || !xs || !sorted_token_ids || !expert_offsets || !w13q || !w13s || !hq || !hs ||
+      !workspace)
+    return MOE_ERR_INVALID_ARG;
+  const Workspace w = workspace_layout(c);
+  if (workspace_bytes < static_cast<size_t>(w.total)) return MOE_ERR_WORKSPACE;
+  if (c.T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ExpertFfnArgs a;
+  if ((st = staged_groups(c, expert_offsets, workspace, w, s, &a))) return st;
+  a.sorted_tok = sorted_token_ids;
+  Fp8FfnArgs f = fp8_args_of(a);
+  f.xq = xq;
+  f.xs = xs;
+  f.w13q = w13q;
+  f.w13s = w13s;
+  f.hq = hq;
+  f.hs = hs;
+  return hip_status(launch_expert_up_fp8(c, f, s));
+}
+
+int moe_expert_down_fp8(const moe_config* cfg, const uint8_t* hq, const float* hs,
+                        const int32_t* expert_offsets, const uint8_t* w2q, const float* w2s,
+                        void* expert_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_fp8(cfg);
+  if (st) return st;
+  const moe_config& c = *cfg;
+  if (!hq || !hs || !expert_offsets || !w2q || !w2s || !expert_out || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  const Workspace w = workspace_layout(c);
+  if (workspace_bytes < static_cast<size_t>(w.total)) return MOE_ERR_WORKSPACE;
+  if (c.T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ExpertFfnArgs a;
+  if ((st = staged_groups(c, expert_offsets, workspace, w, s, &a))) return st;
+  Fp8FfnArgs f = fp8_args_of(a);
+  f.hq = const_cast<uint8_t*>(hq);
+  f.hs = const_cast<float*>(hs);
+  f.w2q = w2q;
+  f.w2s = w2s;
+  f.Y = expert_out;
+  return hip_status(launch_expert_down_fp8(c, f, s));
+}
+
+int moe_forward_fp8(const moe_config* cfg, const void* hidden, const void* w_router,
+                    const float* logit_offset, const float* bias, const int32_t* token_ids,
+                    const int32_t* tid2eid, const uint8_t* w13q, const float* w13s,
+                    const uint8_t* w2q, const float* w2s, const uint8_t* w13q_shared,
+                    const float* w13s_shared, const uint8_t* w2q_shared, const float* w2s_shared,
+                    void* out, int32_t* topk_ids_out, float* topk_weights_out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int st = check_fp8(cfg);
+  if (st) return st;
+  const moe_config& c = *cfg;
+  if (!hidden || !w_router || !w13q || !w13s || !w2q || !w2s || !out || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  if (c.n_shared && (!w13q_shared || !w13s_shared || !w2q_shared || !w2s_shared))
+    return MOE_ERR_INVALID_ARG;
+  if (c.route_mode == MOE_ROUTE_HASH && (!token_ids || !tid2eid)) return MOE_ERR_INVALID_ARG;
+  const Workspace w = workspace_layout(c);
+  if (workspace_bytes < static_cast<size_t>(w.total)) return MOE_ERR_WORKSPACE;
+  if (c.T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  moe_config rc = c;
+  rc.logits_given = 0;
+  const int R = c.T * c.k;
+  float* logits = at<float>(workspace, w.logits);
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(workspace, w.ids);
+  float* gates = topk_weights_out ? topk_weights_out : at<float>(workspace, w.weights);
+  int32_t* sorted_tok = at<int32_t>(workspace, w.sorted_tok);
+  int32_t* dispatch = at<int32_t>(workspace, w.dispatch);
+  int32_t* offsets = at<int32_t>(workspace, w.offsets);
+  int32_t* groups = at<int32_t>(workspace, w.groups);
+  int32_t* tiles = at<int32_t>(workspace, w.tile_prefix);
+  uint8_t* xq = at<uint8_t>(workspace, w.xq);
+  float* xs = at<float>(workspace, w.xs);
+  const int G = c.E + c.n_shared;
+  const int splits = router_splits(rc);
+  if ((st = hip_status(launch_router_gemm(rc, hidden, w_router, logit_offset, logits, splits, s))))
+    return st;
+  if ((st = hip_status(launch_topk(rc, splits > 1 ? nullptr : logits, splits > 1 ? logits : nullptr,
+                                   splits > 1 ? splits : 0, logit_offset, bias, token_ids, tid2eid,
+                                   ids, gates, nullptr, s))))
+    return st;
+  if ((st = hip_status(launch_quantize_rows(c.T, c.d, MOE_BF16, hidden, xq, xs, s)))) return st;
+  if ((st = hip_status(launch_permute(rc, ids, gates, at<int32_t>(workspace, w.blockcnt),
+                                      at<int32_t>(workspace, w.counts), offsets, sorted_tok,
+                                      at<float>(workspace, w.sorted_w), dispatch, s))))
+    return st;
+  if ((st = hip_status(launch_build_tiles(offsets, c.E, R, R, c.n_shared ? c.T : 0, groups,
+                                          tiles, sorted_tok, s))))
+    return st;
+  Fp8FfnArgs f{};
+  f.xq = xq;
+  f.xs = xs;
+  f.sorted_tok = sorted_tok;
+  f.g_begin = groups;
+  f.g_end = groups + G;
+  f.tile_prefix = tiles;
+  f.n_groups = G;
+  f.rows_bound = R + c.n_shared * c.T;
+  f.routed_groups = c.E;
+  f.w13q = w13q;
+  f.w13s = w13s;
+  f.w2q = w2q;
+  f.w2s = w2s;
+  f.w13q_last = c.n_shared ? w13q_shared : nullptr;
+  f.w13s_last = c.n_shared ? w13s_shared : nullptr;
+  f.w2q_last = c.n_shared ? w2q_shared : nullptr;
+  f.w2s_last = c.n_shared ? w2s_shared : nullptr;
+  f.hq = at<uint8_t>(workspace, w.H);
+  f.hs = at<float>(workspace, w.hs);
+  f.Y = at<char>(workspace, w.Y);
+  if ((st = hip_status(launch_expert_up_fp8(c, f, s)))) return st;
+  if ((st = hip_status(launch_expert_down_fp8(c, f, s)))) return st;
+  const char* shared_rows = c.n_shared ? at<char>(workspace, w.Y) + (int64_t)R * c.d * 2 : nullptr;
+  return hip_status(launch_combine(c, f.Y, dispatch, gates, shared_rows, out, s));
 }
 
 const char* moe_strerror(int status) {

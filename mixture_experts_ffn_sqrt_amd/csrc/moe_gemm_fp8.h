@@ -1,0 +1,314 @@
+// Grouped GEMM with FP8 (E4M3) operands and block scales, for the FP8 experts.
+// Instantiated by moe_fp8.hip.
+//
+// What it computes ("MoE 架构与路由策略": E4M3, one scale per 128x128 weight
+// tile, table dsv4-moe-stages: activation + FP8 cast between Linear-1 and
+// Linear-2; "MoE 的算量与通信" closing section: promotion to FP32 accumulation
+// every 128 elements): for an output (row r, column o),
+//   acc = sum_kb  sa[r, kb] * sb[o/128, kb] * sum_{k in block kb} A[r, k] * B[o, k]
+// with A and B E4M3 codes, sa the operand row's scale per 128 columns and sb
+// the weight tile's scale.  Each 128-element block is one LDS stage: two MFMA
+// 32x32x64 steps into a fresh float32 block sum, which is then scaled and
+// added to the float32 accumulator.
+//
+// Epilogues: EPI_SWIGLU8 (Linear-1): h = SiLU(g) * u in float32, then the FP8
+// cast of h in 1x128 groups -- a tile holds exactly one 128-column group of H
+// per row, so the group maximum is reduced across the tile's waves through
+// LDS and the codes and scales are written straight from the tile.
+// EPI_STORE (Linear-2): bfloat16 output rounded once.
+#pragma once
+
+#include "moe_gemm_kernels.h"
+
+namespace moe {
+namespace gemm {
+
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+enum { EPI_SWIGLU8 = 3 };
+
+struct Fp8Args {
+  GemmArgs g;                 // operands as codes (1 byte per element); C: H codes or Y (bf16)
+  const float* a_scale;       // [rows of A, K/128]: A row's scale per K block
+  const int32_t* a_scale_rows;  // A row -> scale row (nullptr: same as the A row map)
+  const float* b_scale;       // group 0's [N_w/128, K/128] tile scales (N_w = weight rows)
+  const float* b_scale_last;  // the last group's, when it is not in b_scale (shared expert)
+  int64_t b_scale_group;      // floats between groups' tile scales
+  float* c_scale;             // EPI_SWIGLU8: [rows, d_ff/128] scales of H
+  int ldcs;                   // floats between rows of c_scale
+  uint32_t as_bytes;          // bytes of a_scale (buffer range)
+};
+
+// E4M3 code of v (finite; saturated to +-448), nearest-even.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  v = fminf(fmaxf(v, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFFu;
+}
+
+// E4M3 MFMA 32x32x64 (no hardware block scale: scale exponents 127 = 2^0)
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// BM x BN tile, WM x WN waves (wave tile 32*FM x 32*FN), STAGES LDS buffers of
+// one 128-element K block each: A rows, B rows (128 bytes each, chunks
+// swizzled by (row >> 1) & 7), then the block's A-row scales.
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES>
+__global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
+  const GemmArgs& p = q.g;
+  constexpr int NT = 64 * WM * WN, NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr bool SW = EPI == EPI_SWIGLU8;
+  constexpr int ROWB = 128;                  // bytes (= K elements) of a row per stage
+  constexpr int RPL = 1024 / ROWB;           // rows filled by one wavefront load
+  constexpr int SAB = (BM > 64 ? BM : 64) * 4;  // A-row scale bytes per stage
+  constexpr int STAGE = (BM + BN) * ROWB + SAB;
+  constexpr int LA = BM / RPL / NW, LB = BN / RPL / NW;
+  constexpr int NSA = (BM + 63) / 64;        // scale loads per stage (one per wave < NSA)
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "whole 32x32 fragments");
+  static_assert(LA * NW * RPL == BM && LB * NW * RPL == BN, "loads must split evenly");
+  static_assert(!SW || BN == 256, "SwiGLU8: one 128-column group of H per tile");
+  static_assert(!SW || FN % 2 == 0, "SwiGLU waves hold gate and up fragments in pairs");
+  static_assert(NSA <= NW, "one scale load per wave at most");
+  static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024, "LDS budget");
+  extern __shared__ __align__(16) char smem[];
+
+  TileCoord tc;
+  if (!decode_tile<BM>(p, tc)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const bool last = p.B_last && tc.grp == p.G - 1;
+  const char* Bg = last ? p.B_last : p.B + (int64_t)tc.grp * p.b_group;
+  const float* Sb = last ? q.b_scale_last : q.b_scale + (int64_t)tc.grp * q.b_scale_group;
+  constexpr uint32_t kOut = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t a_rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.A), 0, (int)p.a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t b_rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Bg), 0, (int)p.b_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(q.a_scale), 0, (int)q.as_bytes, 0x00020000);
+  const int KB = p.K / 128;  // K blocks (= stages of the loop)
+
+  // operand rows: lane l of load j fills slot l % 8 of tile row RPL*(wave+NW*j) + l/8
+  const int lr = lane / 8, lq = lane % 8;
+  uint32_t a_off[LA], b_off[LB];
+#pragma unroll
+  for (int j = 0; j < LA; ++j) {
+    const int row = RPL * (wave + NW * j) + lr;
+    const int ch = lq ^ ((row >> 1) & 7);
+    if (row < tc.nrows) {
+      const int arow = p.a_rows ? p.a_rows[tc.row0 + row] : tc.row0 + row;
+      a_off[j] = (uint32_t)arow * (uint32_t)p.lda + ch * 16;
+    } else {
+      a_off[j] = kOut;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < LB; ++j) {
+    const int row = RPL * (wave + NW * j) + lr;
+    const int ch = lq ^ ((row >> 1) & 7);
+    int brow;
+    bool ok = true;
+    if (SW) {
+      brow = (RPL * (wave + NW * j) < BN / 2) ? tc.nt * (BN / 2) + row
+                                              : p.up_row + tc.nt * (BN / 2) + (row - BN / 2);
+    } else {
+      brow = tc.nt * BN + row;
+      ok = brow < p.N;
+    }
+    b_off[j] = ok ? (uint32_t)brow * (uint32_t)p.ldb + ch * 16 : kOut;
+  }
+  // A-row scales: wave w < NSA loads rows 64 w .. 64 w + 63 (4 bytes per lane)
+  uint32_t s_off = kOut;
+  {
+    const int row = 64 * wave + lane;
+    if (wave < NSA && row < tc.nrows) {
+      const int arow = p.a_rows ? p.a_rows[tc.row0 + row] : tc.row0 + row;
+      const int srow = q.a_scale_rows ? q.a_scale_rows[tc.row0 + row] : arow;
+      s_off = (uint32_t)srow * (uint32_t)(KB * 4);
+    }
+  }
+#define MOE_FP8_ISSUE(kt_)                                                                 \
+  do {                                                                                     \
+    const int kc_ = (kt_) < KB ? (kt_) : KB - 1;                                           \
+    char* buf_ = smem + ((kt_) % STAGES) * STAGE;                                          \
+    _Pragma("unroll") for (int j = 0; j < LA; ++j)                                          \
+        load_lds16(a_rs, buf_ + (RPL * (wave + NW * j)) * ROWB, a_off[j] + kc_ * ROWB);     \
+    _Pragma("unroll") for (int j = 0; j < LB; ++j)                                          \
+        load_lds16(b_rs, buf_ + BM * ROWB + (RPL * (wave + NW * j)) * ROWB,                 \
+                   b_off[j] + kc_ * ROWB);                                                 \
+    if (wave < NSA)                                                                        \
+      load_lds4(s_rs, buf_ + (BM + BN) * ROWB + 256 * wave, s_off + kc_ * 4);              \
+  } while (0)
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
+
+  // fragment reads: row lane % 32, 16-byte chunks 4 kk + 2 (lane / 32) and the next
+  const int fr = lane & 31, fh = lane >> 5, fs = (fr >> 1) & 7;
+  int rd0[2], rd1[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    rd0[kk] = fr * ROWB + (((4 * kk + 2 * fh) ^ fs) << 4);
+    rd1[kk] = fr * ROWB + (((4 * kk + 2 * fh + 1) ^ fs) << 4);
+  }
+  int b_row[FN];
+#pragma unroll
+  for (int f = 0; f < FN; ++f)
+    b_row[f] = SW ? ((f < FN / 2) ? wn * (WTN / 2) + 32 * f : BN / 2 + wn * (WTN / 2) + 32 * (f - FN / 2))
+                  : wn * WTN + 32 * f;
+  // weight tile (128-row block) of fragment f, as a row of the group's scale table
+  // (a fragment wholly past the last weight row reads zeros and is never stored;
+  // its scale row is clamped into the table)
+  int b_blk[FN];
+#pragma unroll
+  for (int f = 0; f < FN; ++f) {
+    const int r0 = b_row[f];
+    b_blk[f] = SW ? ((r0 < BN / 2) ? tc.nt : p.up_row / 128 + tc.nt)
+                  : min((tc.nt * BN + r0) / 128, (p.N + 127) / 128 - 1);
+  }
+  // scale rows of this lane's output rows: fragment i, register group g holds
+  // rows wm*WTM + 32 i + 8 g + 4 (lane / 32) + 0..3
+  const int sa_rd = (BM + BN) * ROWB + 4 * (wm * WTM + 4 * fh);
+
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) MOE_FP8_ISSUE(s);
+
+  const int live = min(FM, max(0, (tc.nrows - wm * WTM + 31) / 32));
+  for (int kt = 0; kt < KB; ++kt) {
+    static_assert((STAGES - 2) * (LA + LB + 1) <= 63, "vmcnt range");
+    // at most (STAGES-2) later stages' loads may still be in flight; waves that
+    // issue no scale load have fewer loads per stage, so wait for the smaller count
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * (LA + LB)));
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    lds_barrier();
+    MOE_FP8_ISSUE(kt + STAGES - 1);
+    const char* cur = smem + (kt % STAGES) * STAGE;
+    float sb[FN];
+#pragma unroll
+    for (int f = 0; f < FN; ++f) sb[f] = Sb[(int64_t)b_blk[f] * KB + kt];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if (i >= live) continue;
+      i32x8 a[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(cur + rd0[kk] + (wm * WTM + 32 * i) * ROWB);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(cur + rd1[kk] + (wm * WTM + 32 * i) * ROWB);
+        a[kk] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+      float sa[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(cur + sa_rd + 4 * (32 * i + 8 * g));
+        sa[4 * g + 0] = v[0];
+        sa[4 * g + 1] = v[1];
+        sa[4 * g + 2] = v[2];
+        sa[4 * g + 3] = v[3];
+      }
+#pragma unroll
+      for (int f = 0; f < FN; ++f) {
+        i32x8 b[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(cur + BM * ROWB + rd0[kk] + b_row[f] * ROWB);
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(cur + BM * ROWB + rd1[kk] + b_row[f] * ROWB);
+          b[kk] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+        f32x16 t = {};
+        t = mfma_fp8(a[0], b[0], t);
+        t = mfma_fp8(a[1], b[1], t);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][f][r] = fmaf(t[r], sa[r] * sb[f], acc[i][f][r]);
+      }
+    }
+  }
+#undef MOE_FP8_ISSUE
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no LDS load may still be in flight
+
+  const int ccol = lane & 31, crow = (lane >> 5) * 4;
+  if constexpr (SW) {
+    // h = SiLU(g) * u; the row maximum of |h| over this wave's columns, then over
+    // the WN waves through LDS; scale = max / 448; codes E4M3(h / scale)
+    constexpr int HF = FN / 2;
+    float h[FM][HF][16];
+    float pmax[FM][16];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float m = 0.0f;
+#pragma unroll
+        for (int f = 0; f < HF; ++f) {
+          const float g = acc[i][f][r], u = acc[i][f + HF][r];
+          h[i][f][r] = g / (1.0f + expf(-g)) * u;
+          m = fmaxf(m, fabsf(h[i][f][r]));
+        }
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 32));
+        pmax[i][r] = m;
+      }
+    // all waves are past the main loop (their last LDS reads returned) before
+    // the stage buffers are reused for the partial maxima
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    lds_barrier();
+    float* part = reinterpret_cast<float*>(smem);  // [WN][BM]
+    if (ccol == 0) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          part[wn * BM + wm * WTM + 32 * i + 8 * (r >> 2) + crow + (r & 3)] = pmax[i][r];
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lrw = wm * WTM + 32 * i + 8 * (r >> 2) + crow + (r & 3);
+        float m = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WN; ++w) m = fmaxf(m, part[w * BM + lrw]);
+        if (lrw >= tc.nrows) continue;
+        const float sc = m / 448.0f;
+        const int64_t row = tc.row0 + lrw;
+        uint8_t* crow_ptr = reinterpret_cast<uint8_t*>(p.C) + row * p.ldc;
+#pragma unroll
+        for (int f = 0; f < HF; ++f) {
+          const int col = tc.nt * (BN / 2) + wn * (WTN / 2) + 32 * f + ccol;
+          crow_ptr[col] = sc == 0.0f ? 0 : (uint8_t)e4m3_code(h[i][f][r] / sc);
+        }
+        if (wn == 0 && ccol == 0) q.c_scale[row * q.ldcs + tc.nt] = sc;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lrw = wm * WTM + 32 * i + 8 * (r >> 2) + crow + (r & 3);
+        if (lrw >= tc.nrows) continue;
+        char* crow_ptr = p.C + (int64_t)(tc.row0 + lrw) * p.ldc;
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          const int col = tc.nt * BN + wn * WTN + 32 * f + ccol;
+          if (col >= p.N) continue;
+          *reinterpret_cast<uint16_t*>(crow_ptr + (int64_t)col * 2) = f32_to_bf16(acc[i][f][r]);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace gemm
+}  // namespace moe

@@ -361,6 +361,11 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, char* dst,
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)dst, 16, voff, 0, 0, 0);
 }
 
+// one 4-byte-per-lane buffer load straight into LDS at `dst` (+4 * lane)
+__device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t rs, char* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)dst, 4, voff, 0, 0, 0);
+}
+
 // Swizzle of the 16-byte chunks of an LDS row, from the row index modulo 32:
 // SWZ 0 = none, 1 = (r>>1 ^ r>>3), 2 = r, 3 = r>>1, 4 = r>>2 (masked to the
 // chunk count).

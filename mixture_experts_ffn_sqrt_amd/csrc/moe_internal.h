@@ -63,6 +63,8 @@ struct Workspace {
   int64_t sorted_tok, sorted_w;        // [P] i32, [R] f32
   int64_t dispatch;                    // [R] i32
   int64_t H, Y;                        // [P*d_ff], [P*d] elements of the layer dtype
+  int64_t hs;                          // FP8 experts: H scales [P, d_ff/128] f32 (codes at H)
+  int64_t xq, xs;                      // FP8 experts: hidden codes [T*d] u8, scales [T, d/128]
   int64_t total;
 };
 
@@ -122,6 +124,35 @@ struct ExpertFfnArgs {
 // GEMM 1 + SiLU(gate) * up -> H, and GEMM 2 -> Y
 hipError_t launch_expert_up(const moe_config& c, const ExpertFfnArgs& a, hipStream_t s);
 hipError_t launch_expert_down(const moe_config& c, const ExpertFfnArgs& a, hipStream_t s);
+
+// FP8 experts: E4M3 codes with float32 block scales (see include/moe.h)
+struct Fp8FfnArgs {
+  const uint8_t* xq;           // [T, d] codes of the hidden rows
+  const float* xs;             // [T, d/128]
+  const int32_t* sorted_tok;   // [rows]
+  const int32_t* g_begin;      // [G]
+  const int32_t* g_end;        // [G]
+  const int32_t* tile_prefix;  // [kNumTileHeights][G+1]
+  int n_groups, rows_bound, routed_groups;
+  const uint8_t* w13q;         // [E, 2*d_ff, d]
+  const float* w13s;           // [E, 2*d_ff/128, d/128]
+  const uint8_t* w2q;          // [E, d, d_ff]
+  const float* w2s;            // [E, d/128, d_ff/128]
+  const uint8_t* w13q_last;    // group E (shared) or nullptr
+  const float* w13s_last;
+  const uint8_t* w2q_last;
+  const float* w2s_last;
+  uint8_t* hq;                 // [rows, d_ff]
+  float* hs;                   // [rows, d_ff/128]
+  void* Y;                     // [rows, d] bfloat16
+};
+hipError_t launch_expert_up_fp8(const moe_config& c, const Fp8FfnArgs& a, hipStream_t s);
+hipError_t launch_expert_down_fp8(const moe_config& c, const Fp8FfnArgs& a, hipStream_t s);
+// 1x128 row quantization (in_dtype MOE_F32 / MOE_BF16) and 128x128 tile quantization
+hipError_t launch_quantize_rows(int n, int K, int in_dtype, const void* x, uint8_t* q,
+                                float* scales, hipStream_t s);
+hipError_t launch_quantize_blocks(int R, int C, int in_dtype, const void* w, uint8_t* q,
+                                  float* scales, hipStream_t s);
 
 hipError_t launch_combine(const moe_config& c, const void* expert_out, const int32_t* dispatch,
                           const float* weights, const void* shared_out, void* out,

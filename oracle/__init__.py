@@ -53,6 +53,8 @@ def lib():
         L.oracle_quantize_blocks.argtypes = [I, I, P, I, P, P]
         L.oracle_quantize_blocks.restype = None
         L.oracle_expert_ffn_fp8.argtypes = [I, I, P, P, P, P, P, P, P]
+        L.oracle_expert_up_fp8.argtypes = [I, I, P, P, P, P, P, P]
+        L.oracle_expert_up_fp8.restype = None
         L.oracle_expert_ffn_fp8.restype = None
         L.oracle_layer_fp8.argtypes = [I, P, I, I, I, I, I, I, I, I, I, I, I,
                                        P, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P, P, P, P]
@@ -282,6 +284,18 @@ def expert_ffn_fp8(xq, xs, w13q, w13s, w2q, w2s):
     lib().oracle_expert_ffn_fp8(d, d_ff, _p(xq), _p(xs), _p(w13q), _p(w13s), _p(w2q), _p(w2s),
                                 _p(y))
     return y
+
+
+def expert_up_fp8(xq, xs, w13q, w13s):
+    """The up half of an FP8 expert on one quantized row: (hq [d_ff] codes, hs [d_ff/128])."""
+    xq, xs = _c(xq, np.uint8), _c(xs, np.float32)
+    w13q, w13s = _c(w13q, np.uint8), _c(w13s, np.float32)
+    d = xq.shape[0]
+    d_ff = w13q.shape[0] // 2
+    hq = np.zeros(d_ff, np.uint8)
+    hs = np.zeros(d_ff // 128, np.float32)
+    lib().oracle_expert_up_fp8(d, d_ff, _p(xq), _p(xs), _p(w13q), _p(w13s), _p(hq), _p(hs))
+    return hq, hs
 
 
 def layer_fp8(hidden, w_router, w13q, w13s, w2q, w2s, k, scoring, rows=None, bias=None,

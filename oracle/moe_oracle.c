@@ -530,6 +530,7 @@ void oracle_quantize_rows(int n, int K, const float *x, uint8_t *q, float *s)
 void oracle_quantize_blocks(int R, int C, const void *w, int dtype, uint8_t *q, float *s)
 {
     int GC = C / 128;
+#pragma omp parallel for collapse(2) schedule(static)
     for (int br = 0; br < R / 128; ++br)
         for (int bc = 0; bc < GC; ++bc) {
             float amax = 0.0f;
@@ -553,11 +554,13 @@ void oracle_quantize_blocks(int R, int C, const void *w, int dtype, uint8_t *q, 
 static double dot_fp8(int K, const uint8_t *a, const float *sa, const uint8_t *b,
                       const float *sb)
 {
-    double acc = 0.0;
+    double val[256], acc = 0.0;
+    for (int c = 0; c < 256; ++c)
+        val[c] = oracle_e4m3_decode((uint8_t)c);
     for (int kb = 0; kb < K / 128; ++kb) {
         double part = 0.0;
         for (int i = kb * 128; i < kb * 128 + 128; ++i)
-            part += oracle_e4m3_decode(a[i]) * oracle_e4m3_decode(b[i]);
+            part += val[a[i]] * val[b[i]];
         acc += (double)sa[kb] * (double)sb[kb] * part;
     }
     return acc;
@@ -569,15 +572,14 @@ static double dot_fp8(int K, const uint8_t *a, const float *sa, const uint8_t *b
  * [d, d_ff] with w2s [d/128, d_ff/128].  h = SiLU(g) * u is rounded to float,
  * quantized in 1x128 groups, and the down projection reads those codes.
  * ------------------------------------------------------------------------- */
-void oracle_expert_ffn_fp8(int d, int d_ff, const uint8_t *xq, const float *xs,
-                           const uint8_t *w13q, const float *w13s, const uint8_t *w2q,
-                           const float *w2s, double *y)
+/* The up half: h = SiLU(g) * u rounded to float, then its 1x128 quantization
+   (hq [d_ff] codes, hs [d_ff/128] scales). */
+void oracle_expert_up_fp8(int d, int d_ff, const uint8_t *xq, const float *xs,
+                          const uint8_t *w13q, const float *w13s, uint8_t *hq, float *hs)
 {
-    int Gd = d / 128, Gf = d_ff / 128;
+    int Gd = d / 128;
     float *h = malloc(sizeof(float) * d_ff);
-    uint8_t *hq = malloc(d_ff);
-    float *hs = malloc(sizeof(float) * Gf);
-    float *sb = malloc(sizeof(float) * (Gd > Gf ? Gd : Gf));
+    float *sb = malloc(sizeof(float) * Gd);
     for (int f = 0; f < d_ff; ++f) {
         for (int kb = 0; kb < Gd; ++kb)
             sb[kb] = w13s[(size_t)(f / 128) * Gd + kb];
@@ -588,12 +590,24 @@ void oracle_expert_ffn_fp8(int d, int d_ff, const uint8_t *xq, const float *xs,
         h[f] = (float)(g / (1.0 + exp(-g)) * u);
     }
     oracle_quantize_rows(1, d_ff, h, hq, hs);
+    free(h);
+    free(sb);
+}
+
+void oracle_expert_ffn_fp8(int d, int d_ff, const uint8_t *xq, const float *xs,
+                           const uint8_t *w13q, const float *w13s, const uint8_t *w2q,
+                           const float *w2s, double *y)
+{
+    int Gd = d / 128, Gf = d_ff / 128;
+    uint8_t *hq = malloc(d_ff);
+    float *hs = malloc(sizeof(float) * Gf);
+    float *sb = malloc(sizeof(float) * (Gd > Gf ? Gd : Gf));
+    oracle_expert_up_fp8(d, d_ff, xq, xs, w13q, w13s, hq, hs);
     for (int o = 0; o < d; ++o) {
         for (int kb = 0; kb < Gf; ++kb)
             sb[kb] = w2s[(size_t)(o / 128) * Gf + kb];
         y[o] = dot_fp8(d_ff, hq, hs, w2q + (size_t)o * d_ff, sb);
     }
-    free(h);
     free(hq);
     free(hs);
     free(sb);

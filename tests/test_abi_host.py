@@ -109,3 +109,30 @@ def test_empty_batch_queues_nothing():
     assert L.moe_route(C.byref(c), bogus, bogus, None, None, None, None, bogus, bogus, bogus,
                        None) == 0
     assert L.moe_combine(C.byref(c), bogus, bogus, bogus, None, bogus, None) == 0
+
+
+def test_fp8_entry_points_check_on_host():
+    L = moe.load_library()
+    z = None
+    bogus = C.c_void_p(0x1000)
+    # quantizers: sizes and dtype first, then pointers
+    assert L.moe_quantize_fp8_rows(4, 192, 1, bogus, bogus, bogus, z) == -2   # K % 128
+    assert L.moe_quantize_fp8_rows(-1, 128, 1, bogus, bogus, bogus, z) == -1
+    assert L.moe_quantize_fp8_rows(4, 128, 7, bogus, bogus, bogus, z) == -1   # dtype
+    assert L.moe_quantize_fp8_rows(4, 128, 1, z, bogus, bogus, z) == -1
+    assert L.moe_quantize_fp8_rows(0, 128, 1, z, z, z, z) == 0               # nothing to do
+    assert L.moe_quantize_fp8_blocks(128, 200, 1, bogus, bogus, bogus, z) == -2
+    assert L.moe_quantize_fp8_blocks(128, 128, 0, bogus, z, bogus, z) == -1
+    # the FP8 layer needs bf16 activations and d, d_ff multiples of 128
+    fwd = [bogus] * 2 + [z] * 4 + [bogus] * 4 + [z] * 4 + [bogus] + [z] * 2 + [bogus]
+    c = cfg(d=256, d_ff=256, dtype="bf16")
+    assert L.moe_forward_fp8(C.byref(c), *fwd, 16, z) == -3                   # workspace
+    assert L.moe_forward_fp8(C.byref(cfg(d=192, d_ff=256, dtype="bf16")), *fwd, 1 << 40, z) == -2
+    assert L.moe_forward_fp8(C.byref(cfg(d=256, d_ff=256, dtype="f32")), *fwd, 1 << 40, z) == -2
+    assert L.moe_forward_fp8(C.byref(cfg(d=256, d_ff=256, dtype="bf16", n_shared=1)), *fwd,
+                             1 << 40, z) == -1
+    missing = list(fwd)
+    missing[8] = z                                                            # w2q
+    assert L.moe_forward_fp8(C.byref(c), *missing, 1 << 40, z) == -1
+    assert L.moe_expert_up_fp8(C.byref(c), *([bogus] * 8), z, 1 << 40, z) == -1  # workspace null
+    assert L.moe_expert_down_fp8(C.byref(c), *([bogus] * 6), bogus, 16, z) == -3
