@@ -22,7 +22,7 @@ METRIC = "MoE-layer tokens/s + grouped-GEMM % bf16 MFMA peak (prefill), % HBM BW
 DEFAULT_WORKLOAD = "mixtral_prefill"  # T=4096, d=4096, E=8, top-2, d_ff=14336, bf16
 
 # MI355X published peaks
-PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8": 5000.0}  # dense MFMA
 PEAK_HBM_GBS = 8000.0
 
 
@@ -39,6 +39,8 @@ def parse():
                     help="after the workload, copy 1 GiB three times (counter calibration)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the vendor-library bf16 GEMM and copy reference points")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the FP8-expert measurements reported beside the bf16 ones")
     return ap.parse_args()
 
 
@@ -112,7 +114,21 @@ def time_gpu(fn, steps, warmup, stream):
     return ev0.elapsed_time(ev1) / steps, wall
 
 
-def run_workload(name, steps, warmup, with_cpu, cpu_seconds):
+def fp8_accounting(lc, counts):
+    """Algorithmic work of the FP8 expert GEMM 1 (routed rows): the same FLOPs as
+    bf16; bytes = E4M3 codes (1 byte) of every active expert's w13 and its
+    128x128 tile scales, the gathered rows' codes and scales, H codes and scales."""
+    import numpy as np
+    d, F, T, k = lc.d, lc.d_ff, lc.T, lc.k
+    act = int((np.asarray(counts) > 0).sum())
+    rows = T * k
+    flops = 4 * d * F * rows
+    nbytes = (act * (2 * F * d + (2 * F // 128) * (d // 128) * 4)
+              + rows * (d + d // 128 * 4) + rows * (F + F // 128 * 4))
+    return flops, nbytes
+
+
+def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True):
     import numpy as np
     import torch
 
@@ -185,11 +201,59 @@ def run_workload(name, steps, warmup, with_cpu, cpu_seconds):
         routing=dict(active_experts=acct["active_experts"], max_rows=int(counts.max()),
                      mean_rows=float(counts.mean()), empty_experts=int((counts == 0).sum())),
     )
+    if with_fp8 and lc.dtype == "bf16" and lc.d % 128 == 0 and lc.d_ff % 128 == 0:
+        res["fp8"] = run_fp8(lc, c, layer, inp, perm, ws, Y, counts, decode, steps, warmup,
+                             stream)
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(lc, inp, cpu_seconds)
     del layer, inp, H, Y, perm
     torch.cuda.empty_cache()
     return res
+
+
+def run_fp8(lc, c, layer, inp, perm, ws, Y, counts, decode, steps, warmup, stream):
+    """The same step with FP8 (E4M3) experts (moe_forward_fp8), and its two
+    grouped GEMMs on their own; weights quantized once on the GPU beforehand."""
+    import torch
+
+    import mixture_experts_ffn_sqrt_amd as moe
+    T, k, d, F = lc.T, lc.k, lc.d, lc.d_ff
+    fp8 = moe.quantize_fp8_weights(inp)
+    ms_step, _ = time_gpu(lambda: layer.forward_fp8(fp8), steps, warmup, stream)
+    print("[bench] %s fp8: %.3f ms/step" % (lc.name, ms_step), file=sys.stderr, flush=True)
+    xq = torch.empty((T, d), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((T, d // 128), dtype=torch.float32, device="cuda")
+    moe.moe_quantize_fp8_rows(inp["hidden"], xq, xs)
+    hq = torch.empty((T * k, F), dtype=torch.uint8, device="cuda")
+    hs = torch.empty((T * k, F // 128), dtype=torch.float32, device="cuda")
+
+    def up():
+        moe.moe_expert_up_fp8(c, xq, xs, perm["tok"], perm["offsets"], fp8["w13q"], fp8["w13s"],
+                              hq, hs, ws)
+
+    def down():
+        moe.moe_expert_down_fp8(c, hq, hs, perm["offsets"], fp8["w2q"], fp8["w2s"], Y, ws)
+
+    ms_up, _ = time_gpu(up, steps, warmup, stream)
+    ms_down, _ = time_gpu(down, steps, warmup, stream)
+    flops, nbytes = fp8_accounting(lc, counts)
+    if decode:
+        ach = nbytes / (ms_up * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(ach / PEAK_HBM_GBS, 4), traffic=None)
+    else:
+        ach = flops / (ms_up * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(ach, 1), peak=PEAK_TFLOPS["fp8"],
+                    unit="TFLOP/s", frac=round(ach / PEAK_TFLOPS["fp8"], 4), traffic=None)
+    roof["kernel"] = "FP8 grouped GEMM 1 + SwiGLU + FP8 cast (moe_expert_up_fp8, routed rows)"
+    roof["kernel_ms"] = round(ms_up, 4)
+    gemm_tflops = 6 * d * F * T * k / ((ms_up + ms_down) * 1e-3) / 1e12
+    del fp8, xq, xs, hq, hs
+    return dict(ms_per_step=round(ms_step, 4), tokens_per_s=round(T / (ms_step * 1e-3), 1),
+                roofline=roof,
+                grouped_gemm=dict(ms_up=round(ms_up, 4), ms_down=round(ms_down, 4),
+                                  tflops=round(gemm_tflops, 1),
+                                  frac_fp8_peak=round(gemm_tflops / PEAK_TFLOPS["fp8"], 4)))
 
 
 def peaks():
@@ -272,7 +336,8 @@ def main():
     import mixture_experts_ffn_sqrt_amd as moe
     moe.load_library()
 
-    head = run_workload(args.workload, args.steps, args.warmup, not args.no_cpu, args.cpu_seconds)
+    head = run_workload(args.workload, args.steps, args.warmup, not args.no_cpu, args.cpu_seconds,
+                        not args.no_fp8)
     from mixture_experts_ffn_sqrt_amd.synth import CONFIGS
     lc = CONFIGS[args.workload]
     line = {
@@ -297,15 +362,16 @@ def main():
         "grouped_gemm": head["grouped_gemm"],
         "layer": head["layer"],
         "routing": head["routing"],
+        "fp8": head.get("fp8"),
     }
     if args.all:
         others = {}
         for name in CONFIGS:
             if name == args.workload:
                 continue
-            r = run_workload(name, args.steps, args.warmup, False, 0)
-            others[name] = {kk: r[kk] for kk in ("ms_per_step", "tokens_per_s", "roofline",
-                                                  "grouped_gemm", "layer", "routing")}
+            r = run_workload(name, args.steps, args.warmup, False, 0, not args.no_fp8)
+            others[name] = {kk: r.get(kk) for kk in ("ms_per_step", "tokens_per_s", "roofline",
+                                                      "grouped_gemm", "layer", "routing", "fp8")}
         line["workloads"] = others
     if not args.no_peaks:
         line["context"] = peaks()

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(int R, int C, cons
 template <int BM, int BN, int WM, int WN, int EPI, int ST>
 hipError_t launch_fp8(const Fp8Args& q, int m_tiles_bound, hipStream_t s) {
   constexpr int NT = 64 * WM * WN;
-  constexpr int LDS = ST * ((BM + BN) * 128 + (BM > 64 ? BM : 64) * 4);
+  constexpr int LDS = ST * ((BM + BN) * 128 + (BM > 64 ? BM : 64) * 4 + 256);
   const int grid = m_tiles_bound * q.g.n_tiles;
   if (grid <= 0) return hipSuccess;
   auto kern = grouped_gemm_fp8<BM, BN, WM, WN, EPI, ST>;
@@ -160,7 +160,7 @@ hipError_t launch_expert_up_fp8(const moe_config& c, const Fp8FfnArgs& a, hipStr
   q.as_bytes = (uint32_t)((int64_t)c.T * (d / 128) * 4);
   if (small_rows(a)) {
     g.tile_prefix = a.tile_prefix + tile_height_index(32) * (a.n_groups + 1);
-    return launch_fp8<32, 256, 1, 2, EPI_SWIGLU8, 4>(q, tile_bound8(a.rows_bound, a.n_groups, 32), s);
+    return launch_fp8<32, 256, 1, 4, EPI_SWIGLU8, 4>(q, tile_bound8(a.rows_bound, a.n_groups, 32), s);
   }
   g.tile_prefix = a.tile_prefix + tile_height_index(256) * (a.n_groups + 1);
   return launch_fp8<256, 256, 4, 2, EPI_SWIGLU8, 2>(q, tile_bound8(a.rows_bound, a.n_groups, 256), s);
@@ -194,7 +194,7 @@ hipError_t launch_expert_down_fp8(const moe_config& c, const Fp8FfnArgs& a, hipS
   if (small_rows(a)) {
     g.n_tiles = ceil_div(c.d, 128);
     g.tile_prefix = a.tile_prefix + tile_height_index(32) * (a.n_groups + 1);
-    return launch_fp8<32, 128, 1, 2, EPI_STORE, 4>(q, tile_bound8(a.rows_bound, a.n_groups, 32), s);
+    return launch_fp8<32, 128, 1, 4, EPI_STORE, 4>(q, tile_bound8(a.rows_bound, a.n_groups, 32), s);
   }
   g.n_tiles = ceil_div(c.d, 256);
   g.tile_prefix = a.tile_prefix + tile_height_index(256) * (a.n_groups + 1);

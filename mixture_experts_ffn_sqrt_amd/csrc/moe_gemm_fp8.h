@@ -52,7 +52,9 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
 
 // BM x BN tile, WM x WN waves (wave tile 32*FM x 32*FN), STAGES LDS buffers of
 // one 128-element K block each: A rows, B rows (128 bytes each, chunks
-// swizzled by (row >> 1) & 7), then the block's A-row scales.
+// swizzled by (row >> 1) & 7), the block's A-row scales, and the block's scales
+// of the tile's (at most two) 128-row weight blocks.  Everything a stage needs
+// arrives through the same direct-to-LDS loads, issued STAGES-1 stages ahead.
 template <int BM, int BN, int WM, int WN, int EPI, int STAGES>
 __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
   const GemmArgs& p = q.g;
@@ -63,7 +65,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
   constexpr int ROWB = 128;                  // bytes (= K elements) of a row per stage
   constexpr int RPL = 1024 / ROWB;           // rows filled by one wavefront load
   constexpr int SAB = (BM > 64 ? BM : 64) * 4;  // A-row scale bytes per stage
-  constexpr int STAGE = (BM + BN) * ROWB + SAB;
+  constexpr int SBB = 256;                   // weight-block scale bytes per stage
+  constexpr int STAGE = (BM + BN) * ROWB + SAB + SBB;
+  constexpr int NSB = BN / 128;              // weight blocks per tile (<= 2)
   constexpr int LA = BM / RPL / NW, LB = BN / RPL / NW;
   constexpr int NSA = (BM + 63) / 64;        // scale loads per stage (one per wave < NSA)
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "whole 32x32 fragments");
@@ -71,6 +75,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
   static_assert(!SW || BN == 256, "SwiGLU8: one 128-column group of H per tile");
   static_assert(!SW || FN % 2 == 0, "SwiGLU waves hold gate and up fragments in pairs");
   static_assert(NSA <= NW, "one scale load per wave at most");
+  static_assert(NSB >= 1 && NSB <= 2, "one or two weight blocks per tile");
   static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024, "LDS budget");
   extern __shared__ __align__(16) char smem[];
 
@@ -89,6 +94,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Bg), 0, (int)p.b_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(q.a_scale), 0, (int)q.as_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t sb_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(Sb), 0, (int)(q.b_scale_group * 4), 0x00020000);
   const int KB = p.K / 128;  // K blocks (= stages of the loop)
 
   // operand rows: lane l of load j fills slot l % 8 of tile row RPL*(wave+NW*j) + l/8
@@ -130,6 +137,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
       s_off = (uint32_t)srow * (uint32_t)(KB * 4);
     }
   }
+  // weight-block scales: lane j < NSB of the last wave loads block j of the tile
+  // (for SwiGLU: the gate block, then the up block); blocks past the weight
+  // rows read zeros
+  uint32_t sb_off = kOut;
+  if (lane < NSB) {
+    const int blk = SW ? (lane == 0 ? tc.nt : p.up_row / 128 + tc.nt) : tc.nt * NSB + lane;
+    if (SW || blk * 128 < p.N) sb_off = (uint32_t)blk * (uint32_t)(KB * 4);
+  }
 #define MOE_FP8_ISSUE(kt_)                                                                 \
   do {                                                                                     \
     const int kc_ = (kt_) < KB ? (kt_) : KB - 1;                                           \
@@ -141,6 +156,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
                    b_off[j] + kc_ * ROWB);                                                 \
     if (wave < NSA)                                                                        \
       load_lds4(s_rs, buf_ + (BM + BN) * ROWB + 256 * wave, s_off + kc_ * 4);              \
+    if (wave == NW - 1)                                                                    \
+      load_lds4(sb_rs, buf_ + (BM + BN) * ROWB + SAB, sb_off + kc_ * 4);                   \
   } while (0)
 
   f32x16 acc[FM][FN];
@@ -165,15 +182,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
     b_row[f] = SW ? ((f < FN / 2) ? wn * (WTN / 2) + 32 * f : BN / 2 + wn * (WTN / 2) + 32 * (f - FN / 2))
                   : wn * WTN + 32 * f;
   // weight tile (128-row block) of fragment f, as a row of the group's scale table
-  // (a fragment wholly past the last weight row reads zeros and is never stored;
-  // its scale row is clamped into the table)
-  int b_blk[FN];
+  // slot of fragment f's weight block among the stage's weight-block scales
+  int sb_slot[FN];
 #pragma unroll
-  for (int f = 0; f < FN; ++f) {
-    const int r0 = b_row[f];
-    b_blk[f] = SW ? ((r0 < BN / 2) ? tc.nt : p.up_row / 128 + tc.nt)
-                  : min((tc.nt * BN + r0) / 128, (p.N + 127) / 128 - 1);
-  }
+  for (int f = 0; f < FN; ++f) sb_slot[f] = SW ? (f < FN / 2 ? 0 : 1) : b_row[f] / 128;
   // scale rows of this lane's output rows: fragment i, register group g holds
   // rows wm*WTM + 32 i + 8 g + 4 (lane / 32) + 0..3
   const int sa_rd = (BM + BN) * ROWB + 4 * (wm * WTM + 4 * fh);
@@ -183,9 +195,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
 
   const int live = min(FM, max(0, (tc.nrows - wm * WTM + 31) / 32));
   for (int kt = 0; kt < KB; ++kt) {
-    static_assert((STAGES - 2) * (LA + LB + 1) <= 63, "vmcnt range");
+    static_assert((STAGES - 2) * (LA + LB + 2) <= 63, "vmcnt range");
     // at most (STAGES-2) later stages' loads may still be in flight; waves that
-    // issue no scale load have fewer loads per stage, so wait for the smaller count
+    // also issue scale loads have more loads per stage, so waiting for the count
+    // of a wave without them is conservative for every wave
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * (LA + LB)));
     __builtin_amdgcn_s_waitcnt(0xC07F);
     lds_barrier();
@@ -193,7 +206,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
     const char* cur = smem + (kt % STAGES) * STAGE;
     float sb[FN];
 #pragma unroll
-    for (int f = 0; f < FN; ++f) sb[f] = Sb[(int64_t)b_blk[f] * KB + kt];
+    for (int f = 0; f < FN; ++f)
+      sb[f] = *reinterpret_cast<const float*>(cur + (BM + BN) * ROWB + SAB + 4 * sb_slot[f]);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       if (i >= live) continue;
