@@ -182,10 +182,14 @@ int moe_forward(const moe_config *cfg, const void *hidden, const void *w_router,
  *            128x128 tile (row-major over tiles).  Shared expert: one expert's worth.
  *   Activations (hidden rows before Linear-1, h after the activation): one scale
  *            per row per 128 columns: codes [rows, K], scales [rows, K/128].
- *   A group's scale is max |x| / 448 in float32 and its codes are E4M3(x / scale)
- *   (float32 division, nearest-even, saturated to +-448); an all-zero group has
- *   scale 0 and zero codes.  A dot product sums each 128-element K block, scales
- *   the block sum by the two block scales and accumulates in float32.
+ *   A group's scale is a power of two, 2^e: the smallest with max |x| <= 448 * 2^e
+ *   (e >= -126; an all-zero group has scale 1); its codes are E4M3(x * 2^-e),
+ *   nearest-even, saturated to +-448.  Power-of-two tile scales keep FP4 (E2M1)
+ *   weights with their finer scales exactly representable after the cast to
+ *   FP8 (the FP4 QAT section's lossless dequantization), and they are the
+ *   scales gfx950's block-scaled matrix cores apply.  A dot product sums each
+ *   128-element K block, scales the block sum by the two block scales and
+ *   accumulates in float32.
  * The FP8 entry points need cfg->dtype == MOE_BF16 (hidden, router weight,
  * expert_out and out are bfloat16; the router stays bfloat16) and d, d_ff
  * multiples of 128 (else MOE_ERR_UNSUPPORTED), and every operand smaller than

@@ -4,9 +4,9 @@
 // dsv4-moe-stages: the FP8 cast after the activation; "MoE 的算量与通信" 五.2:
 // FP8 dispatch of the hidden rows).
 //
-// A group of values x gets the scale s = max |x| / 448 (float) and the codes
-// E4M3(x / s) (division in float, nearest-even, saturated to +-448); an
-// all-zero group gets s = 0 and zero codes.
+// A group of values x gets the power-of-two scale s = 2^e, the smallest with
+// max |x| <= 448 s (e >= -126; s = 1 for an all-zero group), and the codes
+// E4M3(x / s), nearest-even (the division by s is exact).
 #include "moe_gemm_fp8.h"
 
 namespace moe {
@@ -40,11 +40,11 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(int n, int K, const 
   const int g = (int)(job - row * G);
   const int64_t base = row * K + g * 128 + 2 * lane;
   const float v0 = load_in(x, base), v1 = load_in(x, base + 1);
-  const float sc = wave_max64(fmaxf(fabsf(v0), fabsf(v1))) / 448.0f;
-  const uint32_t c0 = sc == 0.0f ? 0u : e4m3_code(v0 / sc);
-  const uint32_t c1 = sc == 0.0f ? 0u : e4m3_code(v1 / sc);
+  const int e = fp8_scale_exp(wave_max64(fmaxf(fabsf(v0), fabsf(v1))));
+  const float inv = ldexpf(1.0f, -e);
+  const uint32_t c0 = e4m3_code(v0 * inv), c1 = e4m3_code(v1 * inv);
   *reinterpret_cast<uint16_t*>(q + base) = (uint16_t)(c0 | (c1 << 8));
-  if (lane == 0) scales[row * G + g] = sc;
+  if (lane == 0) scales[row * G + g] = ldexpf(1.0f, e);
 }
 
 // One block of 256 threads per 128x128 tile: thread t covers 64 consecutive
@@ -62,17 +62,15 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(int R, int C, cons
   m = wave_max64(m);
   if ((t & 63) == 0) wmax[t >> 6] = m;
   __syncthreads();
-  const float sc = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])) / 448.0f;
+  const int e = fp8_scale_exp(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
+  const float inv = ldexpf(1.0f, -e);
   for (int i = 0; i < 64; i += 4) {
     uint32_t word = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t c = sc == 0.0f ? 0u : e4m3_code(load_in(w, base + i + j) / sc);
-      word |= c << (8 * j);
-    }
+    for (int j = 0; j < 4; ++j) word |= e4m3_code(load_in(w, base + i + j) * inv) << (8 * j);
     *reinterpret_cast<uint32_t*>(q + base + i) = word;
   }
-  if (t == 0) scales[(int64_t)br * GC + bc] = sc;
+  if (t == 0) scales[(int64_t)br * GC + bc] = ldexpf(1.0f, e);
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, int ST>
@@ -163,7 +161,7 @@ hipError_t launch_expert_up_fp8(const moe_config& c, const Fp8FfnArgs& a, hipStr
     return launch_fp8<32, 256, 1, 4, EPI_SWIGLU8, 4>(q, tile_bound8(a.rows_bound, a.n_groups, 32), s);
   }
   g.tile_prefix = a.tile_prefix + tile_height_index(256) * (a.n_groups + 1);
-  return launch_fp8<256, 256, 4, 2, EPI_SWIGLU8, 2>(q, tile_bound8(a.rows_bound, a.n_groups, 256), s);
+  return launch_fp8<256, 256, 4, 4, EPI_SWIGLU8, 2>(q, tile_bound8(a.rows_bound, a.n_groups, 256), s);
 }
 
 hipError_t launch_expert_down_fp8(const moe_config& c, const Fp8FfnArgs& a, hipStream_t s) {
@@ -198,7 +196,7 @@ hipError_t launch_expert_down_fp8(const moe_config& c, const Fp8FfnArgs& a, hipS
   }
   g.n_tiles = ceil_div(c.d, 256);
   g.tile_prefix = a.tile_prefix + tile_height_index(256) * (a.n_groups + 1);
-  return launch_fp8<256, 256, 4, 2, EPI_STORE, 2>(q, tile_bound8(a.rows_bound, a.n_groups, 256), s);
+  return launch_fp8<256, 256, 4, 4, EPI_STORE, 2>(q, tile_bound8(a.rows_bound, a.n_groups, 256), s);
 }
 
 }  // namespace moe

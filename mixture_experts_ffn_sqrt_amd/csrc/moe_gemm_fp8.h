@@ -7,9 +7,11 @@
 // every 128 elements): for an output (row r, column o),
 //   acc = sum_kb  sa[r, kb] * sb[o/128, kb] * sum_{k in block kb} A[r, k] * B[o, k]
 // with A and B E4M3 codes, sa the operand row's scale per 128 columns and sb
-// the weight tile's scale.  Each 128-element block is one LDS stage: two MFMA
-// 32x32x64 steps into a fresh float32 block sum, which is then scaled and
-// added to the float32 accumulator.
+// the weight tile's scale, all scales powers of two.  gfx950's scaled MFMA
+// 32x32x64 takes a power-of-two (E8M0) scale per row of A and per column of B
+// for each 32-element K sub-block and accumulates in float32, so each
+// 128-element block (one LDS stage) is two scaled MFMA steps straight into the
+// accumulator: the per-block promotion costs no vector instruction.
 //
 // Epilogues: EPI_SWIGLU8 (Linear-1): h = SiLU(g) * u in float32, then the FP8
 // cast of h in 1x128 groups -- a tile holds exactly one 128-column group of H
@@ -45,9 +47,25 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFFu;
 }
 
-// E4M3 MFMA 32x32x64 (no hardware block scale: scale exponents 127 = 2^0)
-__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+// Exponent of a group's scale: the smallest e with amax <= 448 * 2^e.  With
+// amax = m * 2^k, m in [0.5, 1), and 448 = 0.875 * 2^9: e = k - 9 if m <= 0.875,
+// else k - 8; at least -126 (a normal float); 0 for an all-zero group.
+__device__ __forceinline__ int fp8_scale_exp(float amax) {
+  if (amax == 0.0f) return 0;
+  int k;
+  const float m = frexpf(amax, &k);
+  const int e = k - 9 + (m > 0.875f ? 1 : 0);
+  return e < -126 ? -126 : e;
+}
+
+// E8M0 form of a power-of-two float scale: its biased exponent
+__device__ __forceinline__ int e8m0_of(float s) { return (int)((__float_as_uint(s) >> 23) & 0xFFu); }
+
+// E4M3 MFMA 32x32x64 with E8M0 scales: lane l's sa scales A row l % 32 and
+// K half l / 32, lane l's sb scales B column l % 32 and K half l / 32
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c,
+                                           int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
 // BM x BN tile, WM x WN waves (wave tile 32*FM x 32*FN), STAGES LDS buffers of
@@ -186,9 +204,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
   int sb_slot[FN];
 #pragma unroll
   for (int f = 0; f < FN; ++f) sb_slot[f] = SW ? (f < FN / 2 ? 0 : 1) : b_row[f] / 128;
-  // scale rows of this lane's output rows: fragment i, register group g holds
-  // rows wm*WTM + 32 i + 8 g + 4 (lane / 32) + 0..3
-  const int sa_rd = (BM + BN) * ROWB + 4 * (wm * WTM + 4 * fh);
 
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) MOE_FP8_ISSUE(s);
@@ -204,45 +219,39 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
     lds_barrier();
     MOE_FP8_ISSUE(kt + STAGES - 1);
     const char* cur = smem + (kt % STAGES) * STAGE;
-    float sb[FN];
+    int sbe[FN];
 #pragma unroll
     for (int f = 0; f < FN; ++f)
-      sb[f] = *reinterpret_cast<const float*>(cur + (BM + BN) * ROWB + SAB + 4 * sb_slot[f]);
+      sbe[f] = e8m0_of(*reinterpret_cast<const float*>(cur + (BM + BN) * ROWB + SAB + 4 * sb_slot[f]));
+    int sae[FM];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      if (i >= live) continue;
-      i32x8 a[2];
+    for (int i = 0; i < FM; ++i)
+      sae[i] = e8m0_of(*reinterpret_cast<const float*>(cur + (BM + BN) * ROWB +
+                                                       4 * (wm * WTM + 32 * i + fr)));
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(cur + rd0[kk] + (wm * WTM + 32 * i) * ROWB);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(cur + rd1[kk] + (wm * WTM + 32 * i) * ROWB);
-        a[kk] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      }
-      float sa[16];
+    for (int kk = 0; kk < 2; ++kk) {
+      i32x8 a[FM], b[FN];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(cur + sa_rd + 4 * (32 * i + 8 * g));
-        sa[4 * g + 0] = v[0];
-        sa[4 * g + 1] = v[1];
-        sa[4 * g + 2] = v[2];
-        sa[4 * g + 3] = v[3];
+      for (int i = 0; i < FM; ++i) {
+        const char* src = cur + (wm * WTM + 32 * i) * ROWB;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(src + rd0[kk]);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(src + rd1[kk]);
+        a[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       }
 #pragma unroll
       for (int f = 0; f < FN; ++f) {
-        i32x8 b[2];
+        const char* src = cur + BM * ROWB + b_row[f] * ROWB;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(src + rd0[kk]);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(src + rd1[kk]);
+        b[f] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(cur + BM * ROWB + rd0[kk] + b_row[f] * ROWB);
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(cur + BM * ROWB + rd1[kk] + b_row[f] * ROWB);
-          b[kk] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        }
-        f32x16 t = {};
-        t = mfma_fp8(a[0], b[0], t);
-        t = mfma_fp8(a[1], b[1], t);
+      for (int i = 0; i < FM; ++i) {
+        if (i >= live) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][f][r] = fmaf(t[r], sa[r] * sb[f], acc[i][f][r]);
+        for (int f = 0; f < FN; ++f) acc[i][f] = mfma_fp8(a[i], b[f], acc[i][f], sae[i], sbe[f]);
       }
     }
   }
@@ -252,7 +261,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
   const int ccol = lane & 31, crow = (lane >> 5) * 4;
   if constexpr (SW) {
     // h = SiLU(g) * u; the row maximum of |h| over this wave's columns, then over
-    // the WN waves through LDS; scale = max / 448; codes E4M3(h / scale)
+    // the WN waves through LDS; scale 2^e = the smallest power of two with
+    // max <= 448 * 2^e; codes E4M3(h * 2^-e)
     constexpr int HF = FN / 2;
     float h[FM][HF][16];
     float pmax[FM][16];
@@ -294,15 +304,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
 #pragma unroll
         for (int w = 0; w < WN; ++w) m = fmaxf(m, part[w * BM + lrw]);
         if (lrw >= tc.nrows) continue;
-        const float sc = m / 448.0f;
+        const int e = fp8_scale_exp(m);
+        const float inv = ldexpf(1.0f, -e);  // exact: codes = E4M3(h * 2^-e)
         const int64_t row = tc.row0 + lrw;
         uint8_t* crow_ptr = reinterpret_cast<uint8_t*>(p.C) + row * p.ldc;
 #pragma unroll
         for (int f = 0; f < HF; ++f) {
           const int col = tc.nt * (BN / 2) + wn * (WTN / 2) + 32 * f + ccol;
-          crow_ptr[col] = sc == 0.0f ? 0 : (uint8_t)e4m3_code(h[i][f][r] / sc);
+          crow_ptr[col] = (uint8_t)e4m3_code(h[i][f][r] * inv);
         }
-        if (wn == 0 && ccol == 0) q.c_scale[row * q.ldcs + tc.nt] = sc;
+        if (wn == 0 && ccol == 0) q.c_scale[row * q.ldcs + tc.nt] = ldexpf(1.0f, e);
       }
     }
   } else {

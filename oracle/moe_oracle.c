@@ -48,13 +48,15 @@
  *    then FP8 cast between Linear-1 and Linear-2; [P3] 五.2: FP8 dispatch; [P3]
  *    closing section: promotion to FP32 accumulation every 128 elements).  The
  *    pages fix the weight tile; activations are read as one scale per token per
- *    128 channels (1x128, the K blocks of the weight tiles).  A scale is the
- *    group's max |x| / 448 in float, a code is E4M3 of x / scale rounded to
- *    nearest-even with the division in float (the precision the GPU decides
- *    in), saturated to +-448; an all-zero group has scale 0 and zero codes.
- *    Products are summed per 128-element K block and each block sum is scaled
- *    by the two block scales (in double here).  h = SiLU(g)*u is rounded to
- *    float before it is quantized.
+ *    128 channels (1x128, the K blocks of the weight tiles).  Scales are powers
+ *    of two: [P2]'s FP4 QAT section calls FP4 -> FP8 dequantization lossless
+ *    when each FP8 tile's FP4 sub-block scales span no more than the FP8
+ *    exponent range, which holds only if the FP8 tile scale is a power of two.
+ *    A group's scale is the smallest 2^e with max |x| <= 448 * 2^e (e >= -126;
+ *    1 for an all-zero group) and a code is E4M3 of x * 2^-e (exact scaling),
+ *    rounded to nearest-even.  Products are summed per 128-element K block and
+ *    each block sum is scaled by the two block scales (in double here).
+ *    h = SiLU(g)*u is rounded to float before it is quantized.
  *
  * Pins: the tests check this file against the pages' worked examples (router
  * example, two-token toy, dispatch/combine toy, EP4 per-expert counts), closed
@@ -498,17 +500,29 @@ uint8_t oracle_e4m3_encode(float v)
     return sign | (uint8_t)(code > 0x7E ? 0x7E : code);
 }
 
-static uint8_t quantize_one(float x, float scale)
+/* Exponent of a group's scale: the smallest e with amax <= 448 * 2^e.  With
+   amax = m * 2^k, m in [0.5, 1) and 448 = 0.875 * 2^9: e = k - 9 if m <= 0.875,
+   else k - 8.  Clamped to e >= -126 (the scale stays a normal float); an
+   all-zero group gets e = 0. */
+static int scale_exp(float amax)
 {
-    if (scale == 0.0f)
+    if (amax == 0.0f)
         return 0;
-    float v = x / scale;
+    int k;
+    float m = frexpf(amax, &k);
+    int e = k - 9 + (m > 0.875f ? 1 : 0);
+    return e < -126 ? -126 : e;
+}
+
+static uint8_t quantize_one(float x, int e)
+{
+    float v = ldexpf(x, -e); /* exact: a power-of-two scaling */
     v = v > 448.0f ? 448.0f : (v < -448.0f ? -448.0f : v);
     return oracle_e4m3_encode(v);
 }
 
 /* Rows of a float [n, K] matrix in groups of 128 columns (the 1x128 reading for
-   activations): s[r, g] = max |x| / 448 over the group, q = E4M3(x / s). */
+   activations): s[r, g] = 2^e with e = scale_exp(max |x|), q = E4M3(x / s). */
 void oracle_quantize_rows(int n, int K, const float *x, uint8_t *q, float *s)
 {
     int G = K / 128;
@@ -518,15 +532,16 @@ void oracle_quantize_rows(int n, int K, const float *x, uint8_t *q, float *s)
             float amax = 0.0f;
             for (int i = 0; i < 128; ++i)
                 amax = fmaxf(amax, fabsf(xr[i]));
-            float sc = amax / 448.0f;
-            s[(size_t)r * G + g] = sc;
+            int e = scale_exp(amax);
+            s[(size_t)r * G + g] = ldexpf(1.0f, e);
             for (int i = 0; i < 128; ++i)
-                q[(size_t)r * K + (size_t)g * 128 + i] = quantize_one(xr[i], sc);
+                q[(size_t)r * K + (size_t)g * 128 + i] = quantize_one(xr[i], e);
         }
 }
 
-/* A [R, C] weight matrix (float or bf16) in 128x128 tiles, one scale per tile
-   ([P2] FP4 QAT section: FP8 quantized per 128x128 tile): s[R/128, C/128]. */
+/* A [R, C] weight matrix (float or bf16) in 128x128 tiles, one power-of-two
+   scale per tile ([P2] FP4 QAT section: FP8 quantized per 128x128 tile):
+   s[R/128, C/128]. */
 void oracle_quantize_blocks(int R, int C, const void *w, int dtype, uint8_t *q, float *s)
 {
     int GC = C / 128;
@@ -539,12 +554,12 @@ void oracle_quantize_blocks(int R, int C, const void *w, int dtype, uint8_t *q, 
                     size_t at = (size_t)(br * 128 + i) * C + (size_t)bc * 128 + j;
                     amax = fmaxf(amax, fabsf((float)elem(w, at, dtype)));
                 }
-            float sc = amax / 448.0f;
-            s[(size_t)br * GC + bc] = sc;
+            int e = scale_exp(amax);
+            s[(size_t)br * GC + bc] = ldexpf(1.0f, e);
             for (int i = 0; i < 128; ++i)
                 for (int j = 0; j < 128; ++j) {
                     size_t at = (size_t)(br * 128 + i) * C + (size_t)bc * 128 + j;
-                    q[at] = quantize_one((float)elem(w, at, dtype), sc);
+                    q[at] = quantize_one((float)elem(w, at, dtype), e);
                 }
         }
 }

@@ -69,19 +69,35 @@ def _dequant_rows(q, s):
     return O.e4m3_decode(q) * np.repeat(s.astype(np.float64), 128, axis=1)
 
 
+def _scale_of(amax):
+    """The smallest power of two 2^e with amax <= 448 * 2^e (e >= -126), by search."""
+    out = np.ones_like(amax, dtype=np.float64)
+    for idx, a in np.ndenumerate(amax):
+        if a == 0:
+            continue
+        e = -126
+        while a > 448.0 * 2.0 ** e:
+            e += 1
+        out[idx] = 2.0 ** e
+    return out.astype(np.float32)
+
+
 def test_quantize_rows_bounds_and_extremes():
     rng = np.random.default_rng(3)
     x = (rng.standard_normal((64, 512)) * rng.uniform(1e-3, 1e3, (64, 1))).astype(np.float32)
     x[5, 128:256] = 0.0                                # an all-zero group
+    x[6, 0:128] = np.float32(448.0) * np.float32(2.0 ** -3)   # amax exactly 448 * 2^-3
     q, s = O.quantize_rows(x)
     g = x.reshape(64, 4, 128)
     amax = np.abs(g).max(axis=2)
-    assert np.array_equal(s, (amax / np.float32(448)).astype(np.float32))
-    assert s[5, 1] == 0 and not q[5, 128:256].any()
-    # the largest element of every non-zero group lands on +-448
+    assert np.array_equal(s, _scale_of(amax))
+    assert s[6, 0] == 2.0 ** -3
+    assert s[5, 1] == 1.0 and not q[5, 128:256].any()
+    # the largest element of every non-zero group lands in the top binade (224, 448]
     idx = np.abs(g).argmax(axis=2)
     top = np.take_along_axis(q.reshape(64, 4, 128), idx[..., None], 2)[..., 0]
-    assert np.all((top[amax > 0] & 0x7F) == 0x7E)
+    tv = np.abs(O.e4m3_decode(top[amax > 0]))
+    assert np.all((tv >= 224) & (tv <= 448))
     # error bound: half a step of E4M3 (2^-4 relative for normals, 2^-10 * s absolute below)
     err = np.abs(_dequant_rows(q, s) - x)
     bound = np.maximum(np.abs(x) * 2.0 ** -4, np.repeat(s, 128, axis=1) * 2.0 ** -10)
@@ -89,6 +105,8 @@ def test_quantize_rows_bounds_and_extremes():
 
 
 def test_quantize_rows_power_of_two_invariance():
+    """Scales are powers of two: scaling the input by 8 scales the scale by 8
+    and leaves every code unchanged."""
     rng = np.random.default_rng(4)
     x = rng.standard_normal((8, 256)).astype(np.float32)
     q1, s1 = O.quantize_rows(x)
@@ -105,11 +123,24 @@ def test_quantize_blocks_against_torch_formulation():
     for br in range(2):
         for bc in range(3):
             blk = w[br * 128:(br + 1) * 128, bc * 128:(bc + 1) * 128]
-            sc = np.float32(np.abs(blk).max()) / np.float32(448)
-            v = np.clip(blk / sc, -448, 448).astype(np.float32)
+            sc = _scale_of(np.array([np.abs(blk).max()]))[0]
+            v = (blk / sc).astype(np.float32)          # exact: sc is a power of two
             ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
             assert s[br, bc] == sc
             assert np.array_equal(q[br * 128:(br + 1) * 128, bc * 128:(bc + 1) * 128], ref)
+
+
+def test_fp4_to_fp8_tile_dequantization_is_lossless():
+    """The page's claim: MXFP4 weights (E2M1 values with a power-of-two scale per
+    1x32 sub-block) re-quantized to FP8 128x128 tiles lose nothing as long as the
+    sub-block scales of a tile span little enough of the FP8 exponent range."""
+    rng = np.random.default_rng(13)
+    e2m1 = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    vals = rng.choice(e2m1, (256, 256)) * rng.choice([-1, 1], (256, 256))
+    sub = 2.0 ** rng.integers(-3, 4, (256, 256 // 32))          # a 2^6 spread per tile
+    w = (vals * np.repeat(sub, 32, axis=1)).astype(np.float32)
+    q, s = O.quantize_blocks(w)
+    assert np.array_equal(_dequant_blocks(q, s), w.astype(np.float64))
 
 
 def _dequant_blocks(q, s):
@@ -147,7 +178,7 @@ def test_expert_ffn_fp8_exact_on_small_integers():
     ints = np.array([-3, -2, -1, 0, 1, 2, 3], np.float32)
     w13 = rng.choice(ints, (2 * d_ff, d))
     w2 = rng.choice(ints, (d, d_ff))
-    w13[0, 0] = w13[d_ff, 0] = w2[0, 0] = 448.0    # every tile: scale amax / 448 = 1
+    w13[0, 0] = w13[d_ff, 0] = w2[0, 0] = 448.0    # every tile: max 448, scale 1
     x = rng.choice(ints, (1, d))
     x[0, 0] = 448.0
     w13q, w13s = O.quantize_blocks(w13)
@@ -187,7 +218,7 @@ def test_layer_fp8_close_to_bf16_layer():
 
 
 @pytest.mark.parametrize("which", ["rows", "blocks"])
-def test_quantizers_reject_nothing_on_zeros(which):
+def test_quantizers_on_zeros(which):
     z = np.zeros((128, 256), np.float32)
     q, s = O.quantize_rows(z) if which == "rows" else O.quantize_blocks(z)
-    assert not q.any() and not s.any()
+    assert not q.any() and np.all(s == 1.0)
