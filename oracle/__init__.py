@@ -59,6 +59,18 @@ def lib():
         L.oracle_layer_fp8.argtypes = [I, P, I, I, I, I, I, I, I, I, I, I, I,
                                        P, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P, P, P, P]
         L.oracle_layer_fp8.restype = I
+        L.oracle_e2m1_decode.argtypes = [C.c_uint8]
+        L.oracle_e2m1_decode.restype = C.c_double
+        L.oracle_e2m1_encode.argtypes = [F]
+        L.oracle_e2m1_encode.restype = C.c_uint8
+        L.oracle_quantize_mxfp4.argtypes = [I, I, P, I, P, P]
+        L.oracle_quantize_mxfp4.restype = None
+        L.oracle_expert_up_mxfp4.argtypes = [I, I, P, P, P, P, P, P]
+        L.oracle_expert_up_mxfp4.restype = None
+        L.oracle_expert_ffn_mxfp4.argtypes = [I, I, P, P, P, P, P, P, P]
+        L.oracle_expert_ffn_mxfp4.restype = None
+        L.oracle_layer_mxfp4.argtypes = L.oracle_layer_fp8.argtypes
+        L.oracle_layer_mxfp4.restype = I
         for name in ("oracle_route", "oracle_hash_route", "oracle_permute",
                      "oracle_layer", "oracle_num_threads"):
             getattr(L, name).restype = I
@@ -298,12 +310,17 @@ def expert_up_fp8(xq, xs, w13q, w13s):
     return hq, hs
 
 
-def layer_fp8(hidden, w_router, w13q, w13s, w2q, w2s, k, scoring, rows=None, bias=None,
-              logit_offset=None, n_group=1, topk_group=1, group_topk=0, shared=None,
-              route_mode=LEARNED, token_ids=None, tid2eid=None):
+def layer_fp8(hidden, w_router, w13q, w13s, w2q, w2s, k, scoring, **kw):
     """The layer with FP8 experts for the listed token rows.  w13q/w13s/w2q/w2s:
-    sequences over experts of per-expert arrays (None where not needed); shared:
-    None or a tuple (w13q, w13s, w2q, w2s).  Returns dict(out, ids, gates, margin)."""
+    sequences over experts of per-expert arrays (None where not needed); keyword
+    arguments as for layer_mxfp4.  Returns dict(out, ids, gates, margin)."""
+    return _layer_lowp("oracle_layer_fp8", np.float32, hidden, w_router, w13q, w13s, w2q, w2s,
+                       k, scoring, **kw)
+
+
+def _layer_lowp(fn, scale_dtype, hidden, w_router, w13q, w13s, w2q, w2s, k, scoring, rows=None,
+                bias=None, logit_offset=None, n_group=1, topk_group=1, group_topk=0, shared=None,
+                route_mode=LEARNED, token_ids=None, tid2eid=None, d_ff=None):
     h, dt = _tensor(hidden)
     wr, _ = _tensor(w_router)
     T, d = h.shape
@@ -321,14 +338,15 @@ def layer_fp8(hidden, w_router, w13q, w13s, w2q, w2s, k, scoring, rows=None, bia
                 arr[e] = a.ctypes.data
         return arr
 
-    pq13, ps13 = ptrs(w13q, np.uint8), ptrs(w13s, np.float32)
-    pq2, ps2 = ptrs(w2q, np.uint8), ptrs(w2s, np.float32)
-    first = next(w for w in w13q if w is not None)
-    d_ff = np.asarray(first).shape[0] // 2
+    pq13, ps13 = ptrs(w13q, np.uint8), ptrs(w13s, scale_dtype)
+    pq2, ps2 = ptrs(w2q, np.uint8), ptrs(w2s, scale_dtype)
+    if d_ff is None:
+        first = next(w for w in w13q if w is not None)
+        d_ff = np.asarray(first).shape[0] // 2
     sh = [None] * 4
     if shared is not None:
-        sh = [_c(shared[0], np.uint8), _c(shared[1], np.float32), _c(shared[2], np.uint8),
-              _c(shared[3], np.float32)]
+        sh = [_c(shared[0], np.uint8), _c(shared[1], scale_dtype), _c(shared[2], np.uint8),
+              _c(shared[3], scale_dtype)]
     r = np.arange(T, dtype=np.int32) if rows is None else _c(rows, np.int32)
     n = len(r)
     out = np.zeros((n, d), np.float64)
@@ -340,13 +358,84 @@ def layer_fp8(hidden, w_router, w13q, w13s, w2q, w2s, k, scoring, rows=None, bia
     tok = None if token_ids is None else _c(token_ids, np.int32)
     tab = None if tid2eid is None else _c(tid2eid, np.int32)
     vocab = 0 if tab is None else tab.shape[0]
-    rc = lib().oracle_layer_fp8(n, _p(r), d, E, k, d_ff, 0 if shared is None else 1, dt,
-                                scoring, route_mode, n_group, topk_group, group_topk, _p(h),
-                                _p(wr), _p(b), _p(off), _p(tok), _p(tab), vocab,
-                                C.cast(pq13, C.c_void_p), C.cast(ps13, C.c_void_p),
-                                C.cast(pq2, C.c_void_p), C.cast(ps2, C.c_void_p),
-                                _p(sh[0]), _p(sh[1]), _p(sh[2]), _p(sh[3]),
-                                _p(out), _p(ids), _p(gates), _p(margin))
+    rc = getattr(lib(), fn)(n, _p(r), d, E, k, d_ff, 0 if shared is None else 1, dt,
+                            scoring, route_mode, n_group, topk_group, group_topk, _p(h),
+                            _p(wr), _p(b), _p(off), _p(tok), _p(tab), vocab,
+                            C.cast(pq13, C.c_void_p), C.cast(ps13, C.c_void_p),
+                            C.cast(pq2, C.c_void_p), C.cast(ps2, C.c_void_p),
+                            _p(sh[0]), _p(sh[1]), _p(sh[2]), _p(sh[3]),
+                            _p(out), _p(ids), _p(gates), _p(margin))
     if rc:
-        raise ValueError("oracle_layer_fp8 rejected its arguments (missing expert weights?)")
+        raise ValueError("%s rejected its arguments (missing expert weights?)" % fn)
     return dict(out=out, ids=ids, gates=gates, margin=margin)
+
+
+# ----------------------------------------------------------------------------
+# MXFP4 (E2M1, 1x32 E8M0 scales) expert weights
+# ----------------------------------------------------------------------------
+def e2m1_decode(codes):
+    """E2M1 codes (0..15, uint8 array or int) -> float64 values."""
+    c = np.asarray(codes, np.uint8)
+    f = np.vectorize(lambda v: lib().oracle_e2m1_decode(int(v)), otypes=[np.float64])
+    return f(c)
+
+
+def e2m1_encode(values):
+    """float32 values -> nearest E2M1 codes (ties to even, saturated to +-6)."""
+    v = np.asarray(values, np.float32)
+    f = np.vectorize(lambda x: lib().oracle_e2m1_encode(float(x)), otypes=[np.uint8])
+    return f(v)
+
+
+def quantize_mxfp4(w):
+    """[R, C] float32 or bf16 bits (C a multiple of 32) -> (packed codes uint8
+    [R, C/2], element 2j in the low nibble; E8M0 scale bytes uint8 [R, C/32])."""
+    w, dt = _tensor(w)
+    R, Cc = w.shape
+    q = np.zeros((R, Cc // 2), np.uint8)
+    s = np.zeros((R, Cc // 32), np.uint8)
+    lib().oracle_quantize_mxfp4(R, Cc, _p(w), dt, _p(q), _p(s))
+    return q, s
+
+
+def mxfp4_dequantize(q, s):
+    """(packed codes [R, C/2], E8M0 bytes [R, C/32]) -> float64 [R, C]."""
+    q, s = np.asarray(q, np.uint8), np.asarray(s, np.uint8)
+    R = q.shape[0]
+    codes = np.stack([q & 15, q >> 4], axis=-1).reshape(R, -1)
+    scale = np.ldexp(1.0, s.astype(np.int64) - 127)
+    return e2m1_decode(codes) * np.repeat(scale, 32, axis=1)
+
+
+def expert_up_mxfp4(xq, xs, w13q, w13s):
+    """The up half of an MXFP4 expert on one FP8 row: (hq [d_ff] codes, hs [d_ff/128])."""
+    xq, xs = _c(xq, np.uint8), _c(xs, np.float32)
+    w13q, w13s = _c(w13q, np.uint8), _c(w13s, np.uint8)
+    d = xq.shape[0]
+    d_ff = w13q.shape[0] // 2
+    hq = np.zeros(d_ff, np.uint8)
+    hs = np.zeros(d_ff // 128, np.float32)
+    lib().oracle_expert_up_mxfp4(d, d_ff, _p(xq), _p(xs), _p(w13q), _p(w13s), _p(hq), _p(hs))
+    return hq, hs
+
+
+def expert_ffn_mxfp4(xq, xs, w13q, w13s, w2q, w2s):
+    """One SwiGLU expert with MXFP4 weights on one FP8 row (codes xq [d], scales xs [d/128])."""
+    xq, xs = _c(xq, np.uint8), _c(xs, np.float32)
+    w13q, w13s, w2q, w2s = (_c(w13q, np.uint8), _c(w13s, np.uint8), _c(w2q, np.uint8),
+                            _c(w2s, np.uint8))
+    d = xq.shape[0]
+    d_ff = w13q.shape[0] // 2
+    y = np.zeros(d, np.float64)
+    lib().oracle_expert_ffn_mxfp4(d, d_ff, _p(xq), _p(xs), _p(w13q), _p(w13s), _p(w2q),
+                                  _p(w2s), _p(y))
+    return y
+
+
+def layer_mxfp4(hidden, w_router, w13q, w13s, w2q, w2s, k, scoring, **kw):
+    """The layer with MXFP4 expert weights for the listed token rows (keyword
+    arguments: rows, bias, logit_offset, n_group, topk_group, group_topk, shared =
+    (w13q, w13s, w2q, w2s), route_mode, token_ids, tid2eid).  Returns
+    dict(out, ids, gates, margin)."""
+    return _layer_lowp("oracle_layer_mxfp4", np.uint8, hidden, w_router, w13q, w13s, w2q, w2s,
+                       k, scoring, **kw)

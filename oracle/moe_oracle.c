@@ -57,6 +57,12 @@
  *    rounded to nearest-even.  Products are summed per 128-element K block and
  *    each block sum is scaled by the two block scales (in double here).
  *    h = SiLU(g)*u is rounded to float before it is quantized.
+ *  - MXFP4 expert weights ([P2] FP4 QAT section: E2M1 with one scale per 1x32
+ *    sub-block, used directly at inference; FP4 x FP8 products): a weight row's
+ *    32-element blocks get power-of-two scales (E8M0 bytes) by the FP8 rule with
+ *    6 in place of 448, codes rounded to nearest-even; activations and h stay
+ *    E4M3 1x128 as above.  Products are summed per 32-element block and scaled
+ *    by the block's weight scale and the activation's 1x128 scale.
  *
  * Pins: the tests check this file against the pages' worked examples (router
  * example, two-token toy, dispatch/combine toy, EP4 per-expert counts), closed
@@ -500,19 +506,23 @@ uint8_t oracle_e4m3_encode(float v)
     return sign | (uint8_t)(code > 0x7E ? 0x7E : code);
 }
 
-/* Exponent of a group's scale: the smallest e with amax <= 448 * 2^e.  With
-   amax = m * 2^k, m in [0.5, 1) and 448 = 0.875 * 2^9: e = k - 9 if m <= 0.875,
-   else k - 8.  Clamped to e >= -126 (the scale stays a normal float); an
-   all-zero group gets e = 0. */
-static int scale_exp(float amax)
+/* Exponent of a group's scale: the smallest e with amax <= top * 2^e, where top
+   is the format's largest magnitude (448 for E4M3, 6 for E2M1).  With
+   amax = m * 2^k and top = tm * 2^tk (m, tm in [0.5, 1)): e = k - tk if m <= tm,
+   else k - tk + 1 (448 = 0.875 * 2^9, 6 = 0.75 * 2^3).  Clamped to e >= -126
+   (the scale stays a normal float); an all-zero group gets e = 0. */
+static int scale_exp_top(float amax, float top)
 {
     if (amax == 0.0f)
         return 0;
-    int k;
+    int k, tk;
     float m = frexpf(amax, &k);
-    int e = k - 9 + (m > 0.875f ? 1 : 0);
+    float tm = frexpf(top, &tk);
+    int e = k - tk + (m > tm ? 1 : 0);
     return e < -126 ? -126 : e;
 }
+
+static int scale_exp(float amax) { return scale_exp_top(amax, 448.0f); }
 
 static uint8_t quantize_one(float x, int e)
 {
@@ -633,19 +643,33 @@ void oracle_expert_ffn_fp8(int d, int d_ff, const uint8_t *xq, const float *xs,
  * float hidden states and router weight); each listed token's hidden row is
  * quantized (1x128, [P3] 五.2 FP8 dispatch) and goes through the FP8 experts;
  * the gated sum is formed in double.  w13q/w13s/w2q/w2s: per-expert pointers
- * (NULL for experts no listed token selects); shared expert likewise.
+ * (NULL for experts no listed token selects); shared expert likewise.  The
+ * weight scales are float32 tile scales (FP8) or E8M0 bytes (MXFP4): the
+ * expert function given reads them.
  * ------------------------------------------------------------------------- */
-int oracle_layer_fp8(int n, const int32_t *rows, int d, int E, int k, int d_ff,
-                     int n_shared, int dtype, int scoring, int route_mode, int n_group,
-                     int topk_group, int group_topk, const void *hidden,
-                     const void *w_router, const float *bias, const float *logit_offset,
-                     const int32_t *token_ids, const int32_t *tid2eid, int vocab,
-                     const uint8_t *const *w13q, const float *const *w13s,
-                     const uint8_t *const *w2q, const float *const *w2s,
-                     const uint8_t *w13q_sh, const float *w13s_sh, const uint8_t *w2q_sh,
-                     const float *w2s_sh, double *out, int32_t *ids_out, float *gates_out,
-                     float *margin_out)
+typedef void (*lowp_ffn_fn)(int d, int d_ff, const uint8_t *xq, const float *xs,
+                            const uint8_t *w13q, const void *w13s, const uint8_t *w2q,
+                            const void *w2s, double *y);
+
+static void ffn_fp8_any(int d, int d_ff, const uint8_t *xq, const float *xs,
+                        const uint8_t *w13q, const void *w13s, const uint8_t *w2q,
+                        const void *w2s, double *y)
 {
+    oracle_expert_ffn_fp8(d, d_ff, xq, xs, w13q, (const float *)w13s, w2q, (const float *)w2s, y);
+}
+
+static int layer_lowp(lowp_ffn_fn ffn, int n, const int32_t *rows, int d, int E, int k, int d_ff,
+                      int n_shared, int dtype, int scoring, int route_mode, int n_group,
+                      int topk_group, int group_topk, const void *hidden,
+                      const void *w_router, const float *bias, const float *logit_offset,
+                      const int32_t *token_ids, const int32_t *tid2eid, int vocab,
+                      const uint8_t *const *w13q, const void *const *w13s,
+                      const uint8_t *const *w2q, const void *const *w2s,
+                      const uint8_t *w13q_sh, const void *w13s_sh, const uint8_t *w2q_sh,
+                      const void *w2s_sh, double *out, int32_t *ids_out, float *gates_out,
+                      float *margin_out)
+{
+
     int bad = 0;
     if (k < 1 || k > 64 || k > E || n_shared < 0 || n_shared > 1 || d % 128 || d_ff % 128)
         return -1;
@@ -673,12 +697,12 @@ int oracle_layer_fp8(int n, const int32_t *rows, int d, int E, int k, int d_ff,
                 rc = -1;
                 break;
             }
-            oracle_expert_ffn_fp8(d, d_ff, xq, xs, w13q[e], w13s[e], w2q[e], w2s[e], y);
+            ffn(d, d_ff, xq, xs, w13q[e], w13s[e], w2q[e], w2s[e], y);
             for (int i = 0; i < d; ++i)
                 o[i] += (double)gates[j] * y[i];
         }
         if (!rc && n_shared == 1) {
-            oracle_expert_ffn_fp8(d, d_ff, xq, xs, w13q_sh, w13s_sh, w2q_sh, w2s_sh, y);
+            ffn(d, d_ff, xq, xs, w13q_sh, w13s_sh, w2q_sh, w2s_sh, y);
             for (int i = 0; i < d; ++i)
                 o[i] += y[i];
         }
@@ -698,6 +722,164 @@ int oracle_layer_fp8(int n, const int32_t *rows, int d, int E, int k, int d_ff,
         free(y);
     }
     return bad ? -1 : 0;
+}
+
+
+int oracle_layer_fp8(int n, const int32_t *rows, int d, int E, int k, int d_ff,
+                     int n_shared, int dtype, int scoring, int route_mode, int n_group,
+                     int topk_group, int group_topk, const void *hidden,
+                     const void *w_router, const float *bias, const float *logit_offset,
+                     const int32_t *token_ids, const int32_t *tid2eid, int vocab,
+                     const uint8_t *const *w13q, const float *const *w13s,
+                     const uint8_t *const *w2q, const float *const *w2s,
+                     const uint8_t *w13q_sh, const float *w13s_sh, const uint8_t *w2q_sh,
+                     const float *w2s_sh, double *out, int32_t *ids_out, float *gates_out,
+                     float *margin_out)
+{
+    return layer_lowp(ffn_fp8_any, n, rows, d, E, k, d_ff, n_shared, dtype, scoring, route_mode,
+                      n_group, topk_group, group_topk, hidden, w_router, bias, logit_offset,
+                      token_ids, tid2eid, vocab, w13q, (const void *const *)w13s, w2q,
+                      (const void *const *)w2s, w13q_sh, w13s_sh, w2q_sh, w2s_sh, out, ids_out,
+                      gates_out, margin_out);
+}
+
+/* ---------------------------------------------------------------------------
+ * MXFP4 E2M1 ([P2] FP4 QAT section and table dsv4-moe-fp4-vs-fp8: 2 exponent
+ * bits and 1 mantissa bit, one shared scale per 1x32 sub-block; [P2]: inference
+ * uses the FP4 weights directly, and FP4 x FP8 products are what hardware with
+ * native support multiplies).  Code layout (the OCP MX E2M1 element): sign bit 3,
+ * exponent field E (bits 2..1, bias 1), mantissa bit m.  E = 0: m / 2; E = 1..3:
+ * (1 + m/2) * 2^(E-1).  No infinities or NaN: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ * Weights only: one scale per 32 consecutive elements of a weight row (the K
+ * direction of the dot products), a power of two stored as an E8M0 byte
+ * (scale = 2^(byte - 127)), chosen as for FP8 with 6 in place of 448.  Two codes
+ * per byte, element 2j in the low nibble.  Activations (the hidden rows and h)
+ * stay E4M3 with 1x128 scales.
+ * ------------------------------------------------------------------------- */
+double oracle_e2m1_decode(uint8_t c)
+{
+    int E = (c >> 1) & 3, m = c & 1;
+    double v = E == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, E - 1);
+    return (c & 8) ? -v : v;
+}
+
+/* nearest of the eight magnitudes (searched in order); on a tie the code whose
+   mantissa bit is 0; past 6 it stays 6 */
+uint8_t oracle_e2m1_encode(float v)
+{
+    uint8_t sign = signbit(v) ? 8 : 0;
+    double a = fabs((double)v);
+    if (a >= 6.0) /* saturate (far past 6 the distances below would tie) */
+        return sign | 7;
+    int best = 0;
+    for (int c = 1; c < 8; ++c) {
+        double dc = fabs(oracle_e2m1_decode((uint8_t)c) - a);
+        double db = fabs(oracle_e2m1_decode((uint8_t)best) - a);
+        if (dc < db || (dc == db && (c & 1) == 0))
+            best = c;
+    }
+    return sign | (uint8_t)best;
+}
+
+/* A [R, C] weight matrix (float or bf16, C a multiple of 32) in 1x32 blocks:
+   q [R, C/2] (two codes per byte), s [R, C/32] E8M0 scale bytes. */
+void oracle_quantize_mxfp4(int R, int C, const void *w, int dtype, uint8_t *q, uint8_t *s)
+{
+    int G = C / 32;
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < R; ++r)
+        for (int g = 0; g < G; ++g) {
+            size_t at = (size_t)r * C + (size_t)g * 32;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i)
+                amax = fmaxf(amax, fabsf((float)elem(w, at + i, dtype)));
+            int e = scale_exp_top(amax, 6.0f);
+            s[(size_t)r * G + g] = (uint8_t)(e + 127);
+            for (int i = 0; i < 32; i += 2) {
+                uint8_t lo = oracle_e2m1_encode(ldexpf((float)elem(w, at + i, dtype), -e));
+                uint8_t hi = oracle_e2m1_encode(ldexpf((float)elem(w, at + i + 1, dtype), -e));
+                q[(at + i) / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+}
+
+/* sum over 32-element blocks b of sa[b / 4] * 2^(sb[b] - 127) * sum_{k in b}
+   dec8(a_k) dec4(w_k), in double: an FP8 vector (1x128 scales) against an MXFP4
+   weight row */
+static double dot_mx(int K, const uint8_t *a, const float *sa, const uint8_t *wq,
+                     const uint8_t *sb)
+{
+    double v8[256], v4[16], acc = 0.0;
+    for (int c = 0; c < 256; ++c)
+        v8[c] = oracle_e4m3_decode((uint8_t)c);
+    for (int c = 0; c < 16; ++c)
+        v4[c] = oracle_e2m1_decode((uint8_t)c);
+    for (int b = 0; b < K / 32; ++b) {
+        double part = 0.0;
+        for (int i = b * 32; i < b * 32 + 32; ++i) {
+            uint8_t code = (i & 1) ? (uint8_t)(wq[i / 2] >> 4) : (uint8_t)(wq[i / 2] & 15);
+            part += v8[a[i]] * v4[code];
+        }
+        acc += (double)sa[b / 4] * ldexp(1.0, (int)sb[b] - 127) * part;
+    }
+    return acc;
+}
+
+/* One SwiGLU expert with MXFP4 weights: w13q [2 d_ff, d/2] with w13s [2 d_ff,
+   d/32]; w2q [d, d_ff/2] with w2s [d, d_ff/32].  x and h as for FP8. */
+void oracle_expert_up_mxfp4(int d, int d_ff, const uint8_t *xq, const float *xs,
+                            const uint8_t *w13q, const uint8_t *w13s, uint8_t *hq, float *hs)
+{
+    float *h = malloc(sizeof(float) * d_ff);
+    for (int f = 0; f < d_ff; ++f) {
+        double g = dot_mx(d, xq, xs, w13q + (size_t)f * (d / 2), w13s + (size_t)f * (d / 32));
+        double u = dot_mx(d, xq, xs, w13q + (size_t)(d_ff + f) * (d / 2),
+                          w13s + (size_t)(d_ff + f) * (d / 32));
+        h[f] = (float)(g / (1.0 + exp(-g)) * u);
+    }
+    oracle_quantize_rows(1, d_ff, h, hq, hs);
+    free(h);
+}
+
+void oracle_expert_ffn_mxfp4(int d, int d_ff, const uint8_t *xq, const float *xs,
+                             const uint8_t *w13q, const uint8_t *w13s, const uint8_t *w2q,
+                             const uint8_t *w2s, double *y)
+{
+    uint8_t *hq = malloc(d_ff);
+    float *hs = malloc(sizeof(float) * (d_ff / 128));
+    oracle_expert_up_mxfp4(d, d_ff, xq, xs, w13q, w13s, hq, hs);
+    for (int o = 0; o < d; ++o)
+        y[o] = dot_mx(d_ff, hq, hs, w2q + (size_t)o * (d_ff / 2), w2s + (size_t)o * (d_ff / 32));
+    free(hq);
+    free(hs);
+}
+
+static void ffn_mxfp4_any(int d, int d_ff, const uint8_t *xq, const float *xs,
+                          const uint8_t *w13q, const void *w13s, const uint8_t *w2q,
+                          const void *w2s, double *y)
+{
+    oracle_expert_ffn_mxfp4(d, d_ff, xq, xs, w13q, (const uint8_t *)w13s, w2q,
+                            (const uint8_t *)w2s, y);
+}
+
+/* The layer with MXFP4 expert weights (the FP8 layer's steps; weight scales are
+   E8M0 bytes) */
+int oracle_layer_mxfp4(int n, const int32_t *rows, int d, int E, int k, int d_ff,
+                       int n_shared, int dtype, int scoring, int route_mode, int n_group,
+                       int topk_group, int group_topk, const void *hidden,
+                       const void *w_router, const float *bias, const float *logit_offset,
+                       const int32_t *token_ids, const int32_t *tid2eid, int vocab,
+                       const uint8_t *const *w13q, const uint8_t *const *w13s,
+                       const uint8_t *const *w2q, const uint8_t *const *w2s,
+                       const uint8_t *w13q_sh, const uint8_t *w13s_sh, const uint8_t *w2q_sh,
+                       const uint8_t *w2s_sh, double *out, int32_t *ids_out, float *gates_out,
+                       float *margin_out)
+{
+    return layer_lowp(ffn_mxfp4_any, n, rows, d, E, k, d_ff, n_shared, dtype, scoring,
+                      route_mode, n_group, topk_group, group_topk, hidden, w_router, bias,
+                      logit_offset, token_ids, tid2eid, vocab, w13q, (const void *const *)w13s,
+                      w2q, (const void *const *)w2s, w13q_sh, w13s_sh, w2q_sh, w2s_sh, out,
+                      ids_out, gates_out, margin_out);
 }
 
 /* number of OpenMP threads the layer loop runs on (reported with timings) */
