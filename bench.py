@@ -44,30 +44,36 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCES = ("mixture_experts_ffn_sqrt_amd/csrc/moe_gemm_kernels.h",
-                  "mixture_experts_ffn_sqrt_amd/csrc/moe_gemm.hip")
+KERNEL_SOURCES = {
+    "bf16": ("mixture_experts_ffn_sqrt_amd/csrc/moe_gemm_kernels.h",
+             "mixture_experts_ffn_sqrt_amd/csrc/moe_gemm.hip"),
+    "fp8": ("mixture_experts_ffn_sqrt_amd/csrc/moe_gemm_kernels.h",
+            "mixture_experts_ffn_sqrt_amd/csrc/moe_gemm_fp8.h",
+            "mixture_experts_ffn_sqrt_amd/csrc/moe_fp8.hip"),
+}
 
 
-def kernel_source_sha():
+def kernel_source_sha(kind="bf16"):
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, kind="bf16"):
     """HBM bytes per launch of the dominant kernel from the committed counter
-    summary (profiles/traffic.json), or None when it is absent or was taken on
-    different kernel sources."""
+    summary (profiles/traffic.json, keyed "<workload>" for bf16 and
+    "<workload>_fp8"), or None when it is absent or was taken on different
+    kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         tab = json.load(f)
-    ent = tab.get(workload)
-    if not ent or ent.get("kernel_source_sha") != kernel_source_sha():
+    ent = tab.get(workload if kind == "bf16" else workload + "_" + kind)
+    if not ent or ent.get("kernel_source_sha") != kernel_source_sha(kind):
         return None
     return int(ent["fetch_bytes_per_launch"] + ent["write_bytes_per_launch"])
 
@@ -240,11 +246,12 @@ def run_fp8(lc, c, layer, inp, perm, ws, Y, counts, decode, steps, warmup, strea
     if decode:
         ach = nbytes / (ms_up * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(ach / PEAK_HBM_GBS, 4), traffic=None)
+                    frac=round(ach / PEAK_HBM_GBS, 4), traffic=measured_traffic(lc.name, "fp8"))
     else:
         ach = flops / (ms_up * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(ach, 1), peak=PEAK_TFLOPS["fp8"],
-                    unit="TFLOP/s", frac=round(ach / PEAK_TFLOPS["fp8"], 4), traffic=None)
+                    unit="TFLOP/s", frac=round(ach / PEAK_TFLOPS["fp8"], 4),
+                    traffic=measured_traffic(lc.name, "fp8"))
     roof["kernel"] = "FP8 grouped GEMM 1 + SwiGLU + FP8 cast (moe_expert_up_fp8, routed rows)"
     roof["kernel_ms"] = round(ms_up, 4)
     gemm_tflops = 6 * d * F * T * k / ((ms_up + ms_down) * 1e-3) / 1e12
