@@ -41,6 +41,8 @@ def parse():
                     help="skip the vendor-library bf16 GEMM and copy reference points")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the FP8-expert measurements reported beside the bf16 ones")
+    ap.add_argument("--no-mxfp4", action="store_true",
+                    help="skip the MXFP4-weight measurements reported beside the bf16 ones")
     return ap.parse_args()
 
 
@@ -51,6 +53,7 @@ KERNEL_SOURCES = {
             "mixture_experts_ffn_sqrt_amd/csrc/moe_gemm_fp8.h",
             "mixture_experts_ffn_sqrt_amd/csrc/moe_fp8.hip"),
 }
+KERNEL_SOURCES["mxfp4"] = KERNEL_SOURCES["fp8"]
 
 
 def kernel_source_sha(kind="bf16"):
@@ -120,21 +123,26 @@ def time_gpu(fn, steps, warmup, stream):
     return ev0.elapsed_time(ev1) / steps, wall
 
 
-def fp8_accounting(lc, counts):
-    """Algorithmic work of the FP8 expert GEMM 1 (routed rows): the same FLOPs as
-    bf16; bytes = E4M3 codes (1 byte) of every active expert's w13 and its
-    128x128 tile scales, the gathered rows' codes and scales, H codes and scales."""
+def lowp_accounting(lc, counts, kind):
+    """Algorithmic work of the low-precision expert GEMM 1 (routed rows): the same
+    FLOPs as bf16; bytes = every active expert's w13 codes and scales (FP8: 1
+    byte per weight and a float per 128x128 tile; MXFP4: half a byte per weight
+    and a byte per 32), the gathered rows' E4M3 codes and 1x128 scales, and H's
+    codes and scales."""
     import numpy as np
     d, F, T, k = lc.d, lc.d_ff, lc.T, lc.k
     act = int((np.asarray(counts) > 0).sum())
     rows = T * k
     flops = 4 * d * F * rows
-    nbytes = (act * (2 * F * d + (2 * F // 128) * (d // 128) * 4)
-              + rows * (d + d // 128 * 4) + rows * (F + F // 128 * 4))
+    if kind == "mxfp4":
+        wbytes = 2 * F * d // 2 + 2 * F * (d // 32)
+    else:
+        wbytes = 2 * F * d + (2 * F // 128) * (d // 128) * 4
+    nbytes = act * wbytes + rows * (d + d // 128 * 4) + rows * (F + F // 128 * 4)
     return flops, nbytes
 
 
-def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True):
+def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True, with_mx=True):
     import numpy as np
     import torch
 
@@ -207,9 +215,11 @@ def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True):
         routing=dict(active_experts=acct["active_experts"], max_rows=int(counts.max()),
                      mean_rows=float(counts.mean()), empty_experts=int((counts == 0).sum())),
     )
-    if with_fp8 and lc.dtype == "bf16" and lc.d % 128 == 0 and lc.d_ff % 128 == 0:
-        res["fp8"] = run_fp8(lc, c, layer, inp, perm, ws, Y, counts, decode, steps, warmup,
-                             stream)
+    lowp_ok = lc.dtype == "bf16" and lc.d % 128 == 0 and lc.d_ff % 128 == 0
+    for kind, on in (("fp8", with_fp8), ("mxfp4", with_mx)):
+        if on and lowp_ok:
+            res[kind] = run_lowp(kind, lc, c, layer, inp, perm, ws, Y, counts, decode, steps,
+                                 warmup, stream)
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(lc, inp, cpu_seconds)
     del layer, inp, H, Y, perm
@@ -217,45 +227,52 @@ def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True):
     return res
 
 
-def run_fp8(lc, c, layer, inp, perm, ws, Y, counts, decode, steps, warmup, stream):
-    """The same step with FP8 (E4M3) experts (moe_forward_fp8), and its two
-    grouped GEMMs on their own; weights quantized once on the GPU beforehand."""
+def run_lowp(kind, lc, c, layer, inp, perm, ws, Y, counts, decode, steps, warmup, stream):
+    """The same step with FP8 activations and FP8 (E4M3, kind "fp8") or MXFP4
+    (kind "mxfp4") expert weights (moe_forward_fp8 / moe_forward_mxfp4), and its
+    two grouped GEMMs on their own; weights quantized once on the GPU beforehand.
+    The peak is the FP8 matrix rate in both cases: the activations are E4M3, so
+    every MFMA has an FP8 operand."""
     import torch
 
     import mixture_experts_ffn_sqrt_amd as moe
     T, k, d, F = lc.T, lc.k, lc.d, lc.d_ff
-    fp8 = moe.quantize_fp8_weights(inp)
-    ms_step, _ = time_gpu(lambda: layer.forward_fp8(fp8), steps, warmup, stream)
-    print("[bench] %s fp8: %.3f ms/step" % (lc.name, ms_step), file=sys.stderr, flush=True)
+    mx = kind == "mxfp4"
+    wq = moe.quantize_mxfp4_weights(inp) if mx else moe.quantize_fp8_weights(inp)
+    fwd = layer.forward_mxfp4 if mx else layer.forward_fp8
+    ms_step, _ = time_gpu(lambda: fwd(wq), steps, warmup, stream)
+    print("[bench] %s %s: %.3f ms/step" % (lc.name, kind, ms_step), file=sys.stderr, flush=True)
     xq = torch.empty((T, d), dtype=torch.uint8, device="cuda")
     xs = torch.empty((T, d // 128), dtype=torch.float32, device="cuda")
     moe.moe_quantize_fp8_rows(inp["hidden"], xq, xs)
     hq = torch.empty((T * k, F), dtype=torch.uint8, device="cuda")
     hs = torch.empty((T * k, F // 128), dtype=torch.float32, device="cuda")
+    up_fn = moe.moe_expert_up_mxfp4 if mx else moe.moe_expert_up_fp8
+    down_fn = moe.moe_expert_down_mxfp4 if mx else moe.moe_expert_down_fp8
 
     def up():
-        moe.moe_expert_up_fp8(c, xq, xs, perm["tok"], perm["offsets"], fp8["w13q"], fp8["w13s"],
-                              hq, hs, ws)
+        up_fn(c, xq, xs, perm["tok"], perm["offsets"], wq["w13q"], wq["w13s"], hq, hs, ws)
 
     def down():
-        moe.moe_expert_down_fp8(c, hq, hs, perm["offsets"], fp8["w2q"], fp8["w2s"], Y, ws)
+        down_fn(c, hq, hs, perm["offsets"], wq["w2q"], wq["w2s"], Y, ws)
 
     ms_up, _ = time_gpu(up, steps, warmup, stream)
     ms_down, _ = time_gpu(down, steps, warmup, stream)
-    flops, nbytes = fp8_accounting(lc, counts)
+    flops, nbytes = lowp_accounting(lc, counts, kind)
     if decode:
         ach = nbytes / (ms_up * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(ach / PEAK_HBM_GBS, 4), traffic=measured_traffic(lc.name, "fp8"))
+                    frac=round(ach / PEAK_HBM_GBS, 4), traffic=measured_traffic(lc.name, kind))
     else:
         ach = flops / (ms_up * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(ach, 1), peak=PEAK_TFLOPS["fp8"],
                     unit="TFLOP/s", frac=round(ach / PEAK_TFLOPS["fp8"], 4),
-                    traffic=measured_traffic(lc.name, "fp8"))
-    roof["kernel"] = "FP8 grouped GEMM 1 + SwiGLU + FP8 cast (moe_expert_up_fp8, routed rows)"
+                    traffic=measured_traffic(lc.name, kind))
+    roof["kernel"] = "%s grouped GEMM 1 + SwiGLU + FP8 cast (%s, routed rows)" % (
+        "MXFP4-weight" if mx else "FP8", up_fn.__name__)
     roof["kernel_ms"] = round(ms_up, 4)
     gemm_tflops = 6 * d * F * T * k / ((ms_up + ms_down) * 1e-3) / 1e12
-    del fp8, xq, xs, hq, hs
+    del wq, xq, xs, hq, hs
     return dict(ms_per_step=round(ms_step, 4), tokens_per_s=round(T / (ms_step * 1e-3), 1),
                 roofline=roof,
                 grouped_gemm=dict(ms_up=round(ms_up, 4), ms_down=round(ms_down, 4),
@@ -344,7 +361,7 @@ def main():
     moe.load_library()
 
     head = run_workload(args.workload, args.steps, args.warmup, not args.no_cpu, args.cpu_seconds,
-                        not args.no_fp8)
+                        not args.no_fp8, not args.no_mxfp4)
     from mixture_experts_ffn_sqrt_amd.synth import CONFIGS
     lc = CONFIGS[args.workload]
     line = {
@@ -370,15 +387,18 @@ def main():
         "layer": head["layer"],
         "routing": head["routing"],
         "fp8": head.get("fp8"),
+        "mxfp4": head.get("mxfp4"),
     }
     if args.all:
         others = {}
         for name in CONFIGS:
             if name == args.workload:
                 continue
-            r = run_workload(name, args.steps, args.warmup, False, 0, not args.no_fp8)
+            r = run_workload(name, args.steps, args.warmup, False, 0, not args.no_fp8,
+                             not args.no_mxfp4)
             others[name] = {kk: r.get(kk) for kk in ("ms_per_step", "tokens_per_s", "roofline",
-                                                      "grouped_gemm", "layer", "routing", "fp8")}
+                                                      "grouped_gemm", "layer", "routing", "fp8",
+                                                      "mxfp4")}
         line["workloads"] = others
     if not args.no_peaks:
         line["context"] = peaks()

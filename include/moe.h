@@ -237,6 +237,62 @@ int moe_forward_fp8(const moe_config *cfg, const void *hidden, const void *w_rou
                     float *topk_weights_out, void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/* ---------------------------------------------------------------------------
+ * MXFP4 expert weights ("MoE 架构与路由策略", FP4 QAT section and table
+ * dsv4-moe-fp4-vs-fp8: E2M1 codes with one shared scale per 1x32 sub-block;
+ * inference uses the FP4 weights directly; FP4 x FP8 products on hardware that
+ * multiplies them natively, as gfx950's matrix cores do).  Activations (hidden
+ * rows, h) are E4M3 with 1x128 power-of-two scales exactly as for the FP8
+ * experts; only the weights change.
+ *   Codes: E2M1 (sign, 2 exponent bits with bias 1, 1 mantissa bit; magnitudes
+ *   0, 0.5, 1, 1.5, 2, 3, 4, 6; no infinities or NaN), two per byte, element 2j
+ *   in the low nibble.  Scales: one E8M0 byte per 32 consecutive elements of a
+ *   weight row (value 2^(byte - 127)), the smallest power of two with
+ *   max |x| <= 6 * scale (>= 2^-126; 2^0 for an all-zero block); codes are
+ *   E2M1(x / scale), nearest-even, saturated to +-6.
+ *   Scale layout: for a weight matrix [R, C] the scales are stored
+ *   K-block-major, [C/128, R, 4]: for each 128-column block j, each row r's four
+ *   bytes (its blocks 4j .. 4j+3).  The matrix cores' loads then read one K
+ *   block's scales of consecutive rows as contiguous words.
+ *   Weights: w13q [E, 2*d_ff, d/2] uint8 with w13s [E, d/128, 2*d_ff, 4] uint8,
+ *            w2q [E, d, d_ff/2] with w2s [E, d_ff/128, d, 4].  Shared expert: one
+ *            expert's worth.
+ * A dot product sums each 32-element block, scales the block sum by the
+ * weight block's scale and the activation's 1x128 scale, and accumulates in
+ * float32.  Requirements, workspace and errors as for the FP8 entry points. */
+
+/* Quantize n_mat matrices w [n_mat, R, C] (in_dtype MOE_F32 or MOE_BF16) in 1x32
+ * blocks: q [n_mat, R, C/2] packed codes, scales [n_mat, C/128, R, 4] E8M0 bytes
+ * (the layout above).  C a multiple of 128 (else MOE_ERR_UNSUPPORTED).  Needs no
+ * workspace; n_mat, R or C == 0 queues nothing. */
+int moe_quantize_mxfp4(int n_mat, int R, int C, int in_dtype, const void *w, uint8_t *q,
+                       uint8_t *scales, void *stream);
+
+/* Linear-1 + SwiGLU + FP8 cast of h with MXFP4 weights; arguments as for
+ * moe_expert_up_fp8 except w13q [E, 2*d_ff, d/2] and w13s [E, d/128, 2*d_ff, 4]. */
+int moe_expert_up_mxfp4(const moe_config *cfg, const uint8_t *xq, const float *xs,
+                        const int32_t *sorted_token_ids, const int32_t *expert_offsets,
+                        const uint8_t *w13q, const uint8_t *w13s, uint8_t *hq, float *hs,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Linear-2 with MXFP4 weights; arguments as for moe_expert_down_fp8 except w2q
+ * [E, d, d_ff/2] and w2s [E, d_ff/128, d, 4]. */
+int moe_expert_down_mxfp4(const moe_config *cfg, const uint8_t *hq, const float *hs,
+                          const int32_t *expert_offsets, const uint8_t *w2q, const uint8_t *w2s,
+                          void *expert_out, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* The whole layer with MXFP4 expert weights: the steps of moe_forward_fp8 with
+ * the weights above (the shared expert's likewise). */
+int moe_forward_mxfp4(const moe_config *cfg, const void *hidden, const void *w_router,
+                      const float *logit_offset, const float *bias, const int32_t *token_ids,
+                      const int32_t *tid2eid, const uint8_t *w13q, const uint8_t *w13s,
+                      const uint8_t *w2q, const uint8_t *w2s, const uint8_t *w13q_shared,
+                      const uint8_t *w13s_shared, const uint8_t *w2q_shared,
+                      const uint8_t *w2s_shared, void *out, int32_t *topk_ids_out,
+                      float *topk_weights_out, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
 /* Static description of a status code. */
 const char *moe_strerror(int status);
 

@@ -23,7 +23,8 @@ MOE_ROUTE_LEARNED, MOE_ROUTE_HASH = 0, 1
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_up",
            "moe_expert_down", "moe_combine", "moe_forward", "moe_quantize_fp8_rows",
            "moe_quantize_fp8_blocks", "moe_expert_up_fp8", "moe_expert_down_fp8",
-           "moe_forward_fp8", "moe_strerror")
+           "moe_forward_fp8", "moe_quantize_mxfp4", "moe_expert_up_mxfp4",
+           "moe_expert_down_mxfp4", "moe_forward_mxfp4", "moe_strerror")
 
 
 class MoeError(RuntimeError):
@@ -77,6 +78,10 @@ def load_library(path: str = LIB_PATH):
     L.moe_expert_up_fp8.argtypes = [cfg, P, P, P, P, P, P, P, P, P, S, P]
     L.moe_expert_down_fp8.argtypes = [cfg, P, P, P, P, P, P, P, S, P]
     L.moe_forward_fp8.argtypes = [cfg] + [P] * 18 + [S, P]
+    L.moe_quantize_mxfp4.argtypes = [I, I, I, I, P, P, P, P]
+    L.moe_expert_up_mxfp4.argtypes = [cfg, P, P, P, P, P, P, P, P, P, S, P]
+    L.moe_expert_down_mxfp4.argtypes = [cfg, P, P, P, P, P, P, P, S, P]
+    L.moe_forward_mxfp4.argtypes = [cfg] + [P] * 18 + [S, P]
     L.moe_strerror.argtypes = [I]
     L.moe_strerror.restype = C.c_char_p
     for n in EXPORTS[:-1]:
@@ -347,6 +352,97 @@ def quantize_fp8_weights(inp, stream=None):
     return out
 
 
+def moe_quantize_mxfp4(w, q, scales, stream=None):
+    """w [R, C] or [n, R, C] float32/bfloat16 (C a multiple of 128) -> q [..., R,
+    C/2] uint8 packed E2M1, scales [..., C/128, R, 4] uint8 E8M0 (K-block-major)."""
+    if w.dtype not in _IN_DTYPES:
+        raise ValueError("w must be float32 or bfloat16, got %s" % w.dtype)
+    if w.dim() not in (2, 3):
+        raise ValueError("w must be [R, C] or [n, R, C]")
+    R, C_ = w.shape[-2], w.shape[-1]
+    n = w.shape[0] if w.dim() == 3 else 1
+    lead = tuple(w.shape[:-2])
+    args = [n, R, C_, _IN_DTYPES[w.dtype], _t("w", w, tuple(w.shape), w.dtype),
+            _t("q", q, lead + (R, C_ // 2), torch.uint8),
+            _t("scales", scales, lead + (C_ // 128, R, 4), torch.uint8), _stream(stream)]
+    _check("moe_quantize_mxfp4", load_library().moe_quantize_mxfp4(*args))
+
+
+def moe_expert_up_mxfp4(cfg, xq, xs, sorted_token_ids, expert_offsets, w13q, w13s, hq, hs,
+                        workspace, stream=None):
+    T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
+    u8, f32 = torch.uint8, torch.float32
+    args = [C.byref(cfg),
+            _t("xq", xq, (T, d), u8), _t("xs", xs, (T, d // 128), f32),
+            _t("sorted_token_ids", sorted_token_ids, (T * k,), torch.int32),
+            _t("expert_offsets", expert_offsets, (E + 1,), torch.int32),
+            _t("w13q", w13q, (E, 2 * F, d // 2), u8),
+            _t("w13s", w13s, (E, d // 128, 2 * F, 4), u8),
+            _t("hq", hq, (T * k, F), u8), _t("hs", hs, (T * k, F // 128), f32),
+            *_ws(cfg, workspace), _stream(stream)]
+    _check("moe_expert_up_mxfp4", load_library().moe_expert_up_mxfp4(*args))
+
+
+def moe_expert_down_mxfp4(cfg, hq, hs, expert_offsets, w2q, w2s, expert_out, workspace,
+                          stream=None):
+    T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
+    u8, f32 = torch.uint8, torch.float32
+    args = [C.byref(cfg),
+            _t("hq", hq, (T * k, F), u8), _t("hs", hs, (T * k, F // 128), f32),
+            _t("expert_offsets", expert_offsets, (E + 1,), torch.int32),
+            _t("w2q", w2q, (E, d, F // 2), u8), _t("w2s", w2s, (E, F // 128, d, 4), u8),
+            _t("expert_out", expert_out, (T * k, d), torch.bfloat16),
+            *_ws(cfg, workspace), _stream(stream)]
+    _check("moe_expert_down_mxfp4", load_library().moe_expert_down_mxfp4(*args))
+
+
+def moe_forward_mxfp4(cfg, hidden, w_router, logit_offset, bias, token_ids, tid2eid, w13q, w13s,
+                      w2q, w2s, w13q_shared, w13s_shared, w2q_shared, w2s_shared, out,
+                      topk_ids_out, topk_weights_out, workspace, stream=None):
+    T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
+    bf, u8, f32 = torch.bfloat16, torch.uint8, torch.float32
+    hsh = cfg.route_mode == MOE_ROUTE_HASH
+    sh = bool(cfg.n_shared)
+    args = [C.byref(cfg),
+            _t("hidden", hidden, (T, d), bf), _t("w_router", w_router, (E, d), bf),
+            _t("logit_offset", logit_offset, (E,), f32, False),
+            _t("bias", bias, (E,), f32, False),
+            _t("token_ids", token_ids, (T,), torch.int32, hsh),
+            _t("tid2eid", tid2eid, (cfg.vocab, k), torch.int32, hsh),
+            _t("w13q", w13q, (E, 2 * F, d // 2), u8),
+            _t("w13s", w13s, (E, d // 128, 2 * F, 4), u8),
+            _t("w2q", w2q, (E, d, F // 2), u8), _t("w2s", w2s, (E, F // 128, d, 4), u8),
+            _t("w13q_shared", w13q_shared, (2 * F, d // 2), u8, sh),
+            _t("w13s_shared", w13s_shared, (d // 128, 2 * F, 4), u8, sh),
+            _t("w2q_shared", w2q_shared, (d, F // 2), u8, sh),
+            _t("w2s_shared", w2s_shared, (F // 128, d, 4), u8, sh),
+            _t("out", out, (T, d), bf),
+            _t("topk_ids_out", topk_ids_out, (T, k), torch.int32, False),
+            _t("topk_weights_out", topk_weights_out, (T, k), f32, False),
+            *_ws(cfg, workspace), _stream(stream)]
+    _check("moe_forward_mxfp4", load_library().moe_forward_mxfp4(*args))
+
+
+def quantize_mxfp4_weights(inp, stream=None):
+    """MXFP4 copies of the expert weights of an input dict (w13, w2 and the
+    shared expert's), quantized on the GPU in 1x32 blocks: returns a dict with
+    w13q, w13s, w2q, w2s (and *_shared when present)."""
+    out = {}
+    for name in ("w13", "w2", "w13_shared", "w2_shared"):
+        w = inp.get(name)
+        if w is None:
+            continue
+        lead, R, C_ = tuple(w.shape[:-2]), w.shape[-2], w.shape[-1]
+        q = torch.empty(lead + (R, C_ // 2), dtype=torch.uint8, device=w.device)
+        s = torch.empty(lead + (C_ // 128, R, 4), dtype=torch.uint8, device=w.device)
+        moe_quantize_mxfp4(w, q, s, stream)
+        base = name.replace("_shared", "")
+        suffix = "_shared" if name.endswith("_shared") else ""
+        out[base + "q" + suffix] = q
+        out[base + "s" + suffix] = s
+    return out
+
+
 def moe_strerror(status: int) -> str:
     return load_library().moe_strerror(int(status)).decode()
 
@@ -377,4 +473,14 @@ class MoELayer:
                         fp8["w2q"], fp8["w2s"], fp8.get("w13q_shared"), fp8.get("w13s_shared"),
                         fp8.get("w2q_shared"), fp8.get("w2s_shared"), self.out, self.ids,
                         self.gates, self.workspace, stream)
+        return self.out
+
+    def forward_mxfp4(self, mx, stream=None):
+        """The layer with MXFP4 expert weights; mx = quantize_mxfp4_weights(inputs)."""
+        i = self.inp
+        moe_forward_mxfp4(self.cfg, i["hidden"], i["w_router"], i.get("logit_offset"),
+                          i.get("bias"), i.get("token_ids"), i.get("tid2eid"), mx["w13q"],
+                          mx["w13s"], mx["w2q"], mx["w2s"], mx.get("w13q_shared"),
+                          mx.get("w13s_shared"), mx.get("w2q_shared"), mx.get("w2s_shared"),
+                          self.out, self.ids, self.gates, self.workspace, stream)
         return self.out

@@ -343,10 +343,11 @@ Fp8FfnArgs fp8_args_of(const ExpertFfnArgs& a) {
 }
 }  // namespace
 
-int moe_expert_up_fp8(const moe_config* cfg, const uint8_t* xq, const float* xs,
-                      const int32_t* sorted_token_ids, const int32_t* expert_offsets,
-                      const uint8_t* w13q, const float* w13s, uint8_t* hq, float* hs,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+int expert_up_lowp(const moe_config* cfg, int wfmt, const uint8_t* xq, const float* xs,
+                   const int32_t* sorted_token_ids, const int32_t* expert_offsets,
+                   const uint8_t* w13q, const void* w13s, uint8_t* hq, float* hs,
+                   void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_fp8(cfg);
   if (st) return st;
   const moe_config& c = *cfg;
@@ -361,6 +362,7 @@ int moe_expert_up_fp8(const moe_config* cfg, const uint8_t* xq, const float* xs,
   if ((st = staged_groups(c, expert_offsets, workspace, w, s, &a))) return st;
   a.sorted_tok = sorted_token_ids;
   Fp8FfnArgs f = fp8_args_of(a);
+  f.wfmt = wfmt;
   f.xq = xq;
   f.xs = xs;
   f.w13q = w13q;
@@ -370,9 +372,9 @@ int moe_expert_up_fp8(const moe_config* cfg, const uint8_t* xq, const float* xs,
   return hip_status(launch_expert_up_fp8(c, f, s));
 }
 
-int moe_expert_down_fp8(const moe_config* cfg, const uint8_t* hq, const float* hs,
-                        const int32_t* expert_offsets, const uint8_t* w2q, const float* w2s,
-                        void* expert_out, void* workspace, size_t workspace_bytes, void* stream) {
+int expert_down_lowp(const moe_config* cfg, int wfmt, const uint8_t* hq, const float* hs,
+                     const int32_t* expert_offsets, const uint8_t* w2q, const void* w2s,
+                     void* expert_out, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_fp8(cfg);
   if (st) return st;
   const moe_config& c = *cfg;
@@ -385,6 +387,7 @@ int moe_expert_down_fp8(const moe_config* cfg, const uint8_t* hq, const float* h
   ExpertFfnArgs a;
   if ((st = staged_groups(c, expert_offsets, workspace, w, s, &a))) return st;
   Fp8FfnArgs f = fp8_args_of(a);
+  f.wfmt = wfmt;
   f.hq = const_cast<uint8_t*>(hq);
   f.hs = const_cast<float*>(hs);
   f.w2q = w2q;
@@ -393,13 +396,15 @@ int moe_expert_down_fp8(const moe_config* cfg, const uint8_t* hq, const float* h
   return hip_status(launch_expert_down_fp8(c, f, s));
 }
 
-int moe_forward_fp8(const moe_config* cfg, const void* hidden, const void* w_router,
-                    const float* logit_offset, const float* bias, const int32_t* token_ids,
-                    const int32_t* tid2eid, const uint8_t* w13q, const float* w13s,
-                    const uint8_t* w2q, const float* w2s, const uint8_t* w13q_shared,
-                    const float* w13s_shared, const uint8_t* w2q_shared, const float* w2s_shared,
-                    void* out, int32_t* topk_ids_out, float* topk_weights_out, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+// router -> top-k -> FP8 cast of the hidden rows -> permute -> tiles -> GEMM 1
+// (+ SwiGLU + FP8 cast of H) -> GEMM 2 -> combine, for either weight format
+int forward_lowp(const moe_config* cfg, int wfmt, const void* hidden, const void* w_router,
+                 const float* logit_offset, const float* bias, const int32_t* token_ids,
+                 const int32_t* tid2eid, const uint8_t* w13q, const void* w13s,
+                 const uint8_t* w2q, const void* w2s, const uint8_t* w13q_shared,
+                 const void* w13s_shared, const uint8_t* w2q_shared, const void* w2s_shared,
+                 void* out, int32_t* topk_ids_out, float* topk_weights_out, void* workspace,
+                 size_t workspace_bytes, void* stream) {
   int st = check_fp8(cfg);
   if (st) return st;
   const moe_config& c = *cfg;
@@ -442,6 +447,7 @@ int moe_forward_fp8(const moe_config* cfg, const void* hidden, const void* w_rou
                                           tiles, sorted_tok, s))))
     return st;
   Fp8FfnArgs f{};
+  f.wfmt = wfmt;
   f.xq = xq;
   f.xs = xs;
   f.sorted_tok = sorted_tok;
@@ -466,6 +472,74 @@ int moe_forward_fp8(const moe_config* cfg, const void* hidden, const void* w_rou
   if ((st = hip_status(launch_expert_down_fp8(c, f, s)))) return st;
   const char* shared_rows = c.n_shared ? at<char>(workspace, w.Y) + (int64_t)R * c.d * 2 : nullptr;
   return hip_status(launch_combine(c, f.Y, dispatch, gates, shared_rows, out, s));
+}
+}  // namespace
+
+int moe_expert_up_fp8(const moe_config* cfg, const uint8_t* xq, const float* xs,
+                      const int32_t* sorted_token_ids, const int32_t* expert_offsets,
+                      const uint8_t* w13q, const float* w13s, uint8_t* hq, float* hs,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return expert_up_lowp(cfg, kWeightE4M3, xq, xs, sorted_token_ids, expert_offsets, w13q, w13s,
+                        hq, hs, workspace, workspace_bytes, stream);
+}
+
+int moe_expert_down_fp8(const moe_config* cfg, const uint8_t* hq, const float* hs,
+                        const int32_t* expert_offsets, const uint8_t* w2q, const float* w2s,
+                        void* expert_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return expert_down_lowp(cfg, kWeightE4M3, hq, hs, expert_offsets, w2q, w2s, expert_out,
+                          workspace, workspace_bytes, stream);
+}
+
+int moe_forward_fp8(const moe_config* cfg, const void* hidden, const void* w_router,
+                    const float* logit_offset, const float* bias, const int32_t* token_ids,
+                    const int32_t* tid2eid, const uint8_t* w13q, const float* w13s,
+                    const uint8_t* w2q, const float* w2s, const uint8_t* w13q_shared,
+                    const float* w13s_shared, const uint8_t* w2q_shared, const float* w2s_shared,
+                    void* out, int32_t* topk_ids_out, float* topk_weights_out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return forward_lowp(cfg, kWeightE4M3, hidden, w_router, logit_offset, bias, token_ids, tid2eid,
+                      w13q, w13s, w2q, w2s, w13q_shared, w13s_shared, w2q_shared, w2s_shared, out,
+                      topk_ids_out, topk_weights_out, workspace, workspace_bytes, stream);
+}
+
+int moe_quantize_mxfp4(int n_mat, int R, int C, int in_dtype, const void* w, uint8_t* q,
+                       uint8_t* scales, void* stream) {
+  if (n_mat < 0 || R < 0 || C < 0) return MOE_ERR_INVALID_ARG;
+  if (C % 128) return MOE_ERR_UNSUPPORTED;
+  if (in_dtype != MOE_F32 && in_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (n_mat == 0 || R == 0 || C == 0) return MOE_OK;
+  if (!w || !q || !scales) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_quantize_mxfp4(n_mat, R, C, in_dtype, w, q, scales,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int moe_expert_up_mxfp4(const moe_config* cfg, const uint8_t* xq, const float* xs,
+                        const int32_t* sorted_token_ids, const int32_t* expert_offsets,
+                        const uint8_t* w13q, const uint8_t* w13s, uint8_t* hq, float* hs,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return expert_up_lowp(cfg, kWeightMxfp4, xq, xs, sorted_token_ids, expert_offsets, w13q, w13s,
+                        hq, hs, workspace, workspace_bytes, stream);
+}
+
+int moe_expert_down_mxfp4(const moe_config* cfg, const uint8_t* hq, const float* hs,
+                          const int32_t* expert_offsets, const uint8_t* w2q, const uint8_t* w2s,
+                          void* expert_out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return expert_down_lowp(cfg, kWeightMxfp4, hq, hs, expert_offsets, w2q, w2s, expert_out,
+                          workspace, workspace_bytes, stream);
+}
+
+int moe_forward_mxfp4(const moe_config* cfg, const void* hidden, const void* w_router,
+                      const float* logit_offset, const float* bias, const int32_t* token_ids,
+                      const int32_t* tid2eid, const uint8_t* w13q, const uint8_t* w13s,
+                      const uint8_t* w2q, const uint8_t* w2s, const uint8_t* w13q_shared,
+                      const uint8_t* w13s_shared, const uint8_t* w2q_shared,
+                      const uint8_t* w2s_shared, void* out, int32_t* topk_ids_out,
+                      float* topk_weights_out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return forward_lowp(cfg, kWeightMxfp4, hidden, w_router, logit_offset, bias, token_ids, tid2eid,
+                      w13q, w13s, w2q, w2s, w13q_shared, w13s_shared, w2q_shared, w2s_shared, out,
+                      topk_ids_out, topk_weights_out, workspace, workspace_bytes, stream);
 }
 
 const char* moe_strerror(int status) {

@@ -7,6 +7,14 @@
 // A group of values x gets the power-of-two scale s = 2^e, the smallest with
 // max |x| <= 448 s (e >= -126; s = 1 for an all-zero group), and the codes
 // E4M3(x / s), nearest-even (the division by s is exact).
+//
+// MXFP4 weights (the same page's FP4 QAT section: E2M1 with one scale per 1x32
+// sub-block): each 32 consecutive elements of a weight row get s = 2^e, the
+// smallest with max |x| <= 6 s (e >= -126; 1 for an all-zero block), stored as
+// the E8M0 byte e + 127, and the codes E2M1(x / s), nearest-even, two per byte
+// with element 2j in the low nibble.  Scales are stored K-block-major
+// ([C/128, R, 4] per matrix) so that one K block's scales of consecutive rows
+// are contiguous for the GEMMs' loads.
 #include "moe_gemm_fp8.h"
 
 namespace moe {
@@ -47,6 +55,57 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(int n, int K, const 
   if (lane == 0) scales[row * G + g] = ldexpf(1.0f, e);
 }
 
+// E2M1 code of v, nearest with ties to the even mantissa, saturated to +-6: the
+// magnitudes are 0, .5, 1, 1.5, 2, 3, 4, 6, and the code counts the midpoints
+// below |v| (a midpoint that is a tie rounds to the even neighbour: strict
+// comparison where the lower neighbour is even, inclusive where it is odd)
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+                     (a >= 3.5f) + (a > 5.0f);
+  return c | (signbit(v) ? 8u : 0u);
+}
+
+// Exponent of an MXFP4 block scale: the smallest e with amax <= 6 * 2^e.  With
+// amax = m * 2^k, m in [0.5, 1), and 6 = 0.75 * 2^3: e = k - 3 if m <= 0.75,
+// else k - 2; at least -126; 0 for an all-zero block.
+__device__ __forceinline__ int mx_scale_exp(float amax) {
+  if (amax == 0.0f) return 0;
+  int k;
+  const float m = frexpf(amax, &k);
+  const int e = k - 3 + (m > 0.75f ? 1 : 0);
+  return e < -126 ? -126 : e;
+}
+
+// 16 lanes per 32-element block (two elements each, one output byte), four
+// blocks per wavefront, blocks numbered over the row-major [n_mat * R, C]
+// input (a row's C/32 blocks are consecutive).  Scale of block b of row r of
+// matrix m goes to scales[m][b / 4][r][b % 4].
+template <typename TIn>
+__global__ __launch_bounds__(256) void quantize_mxfp4_kernel(int64_t nblocks, int R, int C,
+                                                             const TIn* w, uint8_t* q,
+                                                             uint8_t* scales) {
+  const int lane = threadIdx.x & 63, sub = lane & 15;
+  const int64_t blk = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+  const bool ok = blk < nblocks;
+  const int64_t base = blk * 32 + 2 * sub;
+  const float v0 = ok ? load_in(w, base) : 0.0f, v1 = ok ? load_in(w, base + 1) : 0.0f;
+  float m = fmaxf(fabsf(v0), fabsf(v1));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+  if (!ok) return;
+  const int e = mx_scale_exp(m);
+  const float inv = ldexpf(1.0f, -e);
+  q[base / 2] = (uint8_t)(e2m1_code(v0 * inv) | (e2m1_code(v1 * inv) << 4));
+  if (sub == 0) {
+    const int GB = C / 32;
+    const int64_t row = blk / GB;  // over all matrices
+    const int b = (int)(blk - row * GB);
+    const int64_t m = row / R, r = row - m * R;
+    scales[((m * (C / 128) + b / 4) * R + r) * 4 + (b & 3)] = (uint8_t)(e + 127);
+  }
+}
+
 // One block of 256 threads per 128x128 tile: thread t covers 64 consecutive
 // elements of tile row t / 2.
 template <typename TIn>
@@ -73,13 +132,15 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(int R, int C, cons
   if (t == 0) scales[(int64_t)br * GC + bc] = ldexpf(1.0f, e);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int ST>
+template <int BM, int BN, int WM, int WN, int EPI, int ST, int WF = WF_E4M3>
 hipError_t launch_fp8(const Fp8Args& q, int m_tiles_bound, hipStream_t s) {
   constexpr int NT = 64 * WM * WN;
-  constexpr int LDS = ST * ((BM + BN) * 128 + (BM > 64 ? BM : 64) * 4 + 256);
+  constexpr bool MX = WF == WF_MXFP4;
+  constexpr int LDS = ST * (BM * 128 + BN * (MX ? 64 : 128) + (BM > 64 ? BM : 64) * 4 +
+                            (MX ? BN * 4 : 256));
   const int grid = m_tiles_bound * q.g.n_tiles;
   if (grid <= 0) return hipSuccess;
-  auto kern = grouped_gemm_fp8<BM, BN, WM, WN, EPI, ST>;
+  auto kern = grouped_gemm_fp8<BM, BN, WM, WN, EPI, ST, WF>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   if (e != hipSuccess) return e;
@@ -93,7 +154,10 @@ int tile_bound8(int64_t rows, int groups, int bm) {
 }
 
 // 32-row streaming tiles when experts have a few rows each (decode), else
-// 256x256 tiles (the same rule as the bf16 experts)
+// 256x256 tiles (the same rule as the bf16 experts).  The decode tiles keep
+// short LDS rings (2-3 stages, 40-80 KB) so that two to four blocks share a CU
+// and one block's pipeline fill and epilogue overlap another's streaming:
+// measured faster than one block per CU with a 4-12 stage ring.
 bool small_rows(const Fp8FfnArgs& a) {
   return a.rows_bound / (a.n_groups > 0 ? a.n_groups : 1) < 48;
 }
@@ -114,6 +178,20 @@ hipError_t launch_quantize_rows(int n, int K, int in_dtype, const void* x, uint8
   return hipGetLastError();
 }
 
+hipError_t launch_quantize_mxfp4(int n_mat, int R, int C, int in_dtype, const void* w, uint8_t* q,
+                                 uint8_t* scales, hipStream_t s) {
+  const int64_t nblocks = (int64_t)n_mat * R * (C / 32);
+  if (nblocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)((nblocks + 15) / 16));
+  if (in_dtype == MOE_F32)
+    hipLaunchKernelGGL(quantize_mxfp4_kernel<float>, grid, dim3(256), 0, s, nblocks, R, C,
+                       static_cast<const float*>(w), q, scales);
+  else
+    hipLaunchKernelGGL(quantize_mxfp4_kernel<uint16_t>, grid, dim3(256), 0, s, nblocks, R, C,
+                       static_cast<const uint16_t*>(w), q, scales);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_blocks(int R, int C, int in_dtype, const void* w, uint8_t* q,
                                   float* scales, hipStream_t s) {
   const int64_t tiles = (int64_t)(R / 128) * (C / 128);
@@ -129,6 +207,7 @@ hipError_t launch_quantize_blocks(int R, int C, int in_dtype, const void* w, uin
 
 hipError_t launch_expert_up_fp8(const moe_config& c, const Fp8FfnArgs& a, hipStream_t s) {
   const int64_t d = c.d, F = c.d_ff;
+  const bool mx = a.wfmt == kWeightMxfp4;
   Fp8Args q{};
   GemmArgs& g = q.g;
   g.A = reinterpret_cast<const char*>(a.xq);
@@ -136,8 +215,8 @@ hipError_t launch_expert_up_fp8(const moe_config& c, const Fp8FfnArgs& a, hipStr
   g.lda = d;
   g.B = reinterpret_cast<const char*>(a.w13q);
   g.B_last = reinterpret_cast<const char*>(a.w13q_last);
-  g.b_group = 2 * F * d;
-  g.ldb = d;
+  g.ldb = mx ? d / 2 : d;
+  g.b_group = 2 * F * g.ldb;
   g.N = c.d_ff;
   g.up_row = c.d_ff;
   g.K = c.d;
@@ -148,24 +227,30 @@ hipError_t launch_expert_up_fp8(const moe_config& c, const Fp8FfnArgs& a, hipStr
   g.ldc = F;
   g.n_tiles = c.d_ff / 128;
   g.a_bytes = (uint32_t)((int64_t)c.T * d);
-  g.b_bytes = (uint32_t)(2 * F * d);
+  g.b_bytes = (uint32_t)g.b_group;
   q.a_scale = a.xs;
   q.b_scale = a.w13s;
   q.b_scale_last = a.w13s_last;
-  q.b_scale_group = (2 * F / 128) * (d / 128);
+  q.b_scale_group = mx ? 2 * F * (d / 32) : (2 * F / 128) * (d / 128) * 4;
+  q.b_scale_kstride = mx ? (uint32_t)(2 * F * 4) : 4u;
   q.c_scale = a.hs;
   q.ldcs = c.d_ff / 128;
   q.as_bytes = (uint32_t)((int64_t)c.T * (d / 128) * 4);
   if (small_rows(a)) {
     g.tile_prefix = a.tile_prefix + tile_height_index(32) * (a.n_groups + 1);
-    return launch_fp8<32, 256, 1, 4, EPI_SWIGLU8, 4>(q, tile_bound8(a.rows_bound, a.n_groups, 32), s);
+    const int mt = tile_bound8(a.rows_bound, a.n_groups, 32);
+    return mx ? launch_fp8<32, 256, 1, 4, EPI_SWIGLU8, 3, WF_MXFP4>(q, mt, s)
+              : launch_fp8<32, 256, 1, 4, EPI_SWIGLU8, 2>(q, mt, s);
   }
   g.tile_prefix = a.tile_prefix + tile_height_index(256) * (a.n_groups + 1);
-  return launch_fp8<256, 256, 4, 4, EPI_SWIGLU8, 2>(q, tile_bound8(a.rows_bound, a.n_groups, 256), s);
+  const int mt = tile_bound8(a.rows_bound, a.n_groups, 256);
+  return mx ? launch_fp8<256, 256, 4, 4, EPI_SWIGLU8, 3, WF_MXFP4>(q, mt, s)
+            : launch_fp8<256, 256, 4, 4, EPI_SWIGLU8, 2>(q, mt, s);
 }
 
 hipError_t launch_expert_down_fp8(const moe_config& c, const Fp8FfnArgs& a, hipStream_t s) {
   const int64_t d = c.d, F = c.d_ff;
+  const bool mx = a.wfmt == kWeightMxfp4;
   Fp8Args q{};
   GemmArgs& g = q.g;
   g.A = reinterpret_cast<const char*>(a.hq);
@@ -173,8 +258,8 @@ hipError_t launch_expert_down_fp8(const moe_config& c, const Fp8FfnArgs& a, hipS
   g.lda = F;
   g.B = reinterpret_cast<const char*>(a.w2q);
   g.B_last = reinterpret_cast<const char*>(a.w2q_last);
-  g.b_group = d * F;
-  g.ldb = F;
+  g.ldb = mx ? F / 2 : F;
+  g.b_group = d * g.ldb;
   g.N = c.d;
   g.K = c.d_ff;
   g.g_begin = a.g_begin;
@@ -183,20 +268,25 @@ hipError_t launch_expert_down_fp8(const moe_config& c, const Fp8FfnArgs& a, hipS
   g.C = static_cast<char*>(a.Y);
   g.ldc = d * 2;
   g.a_bytes = (uint32_t)((int64_t)a.rows_bound * F);
-  g.b_bytes = (uint32_t)(d * F);
+  g.b_bytes = (uint32_t)g.b_group;
   q.a_scale = a.hs;
   q.b_scale = a.w2s;
   q.b_scale_last = a.w2s_last;
-  q.b_scale_group = (d / 128) * (F / 128);
+  q.b_scale_group = mx ? d * (F / 32) : (d / 128) * (F / 128) * 4;
+  q.b_scale_kstride = mx ? (uint32_t)(d * 4) : 4u;
   q.as_bytes = (uint32_t)((int64_t)a.rows_bound * (F / 128) * 4);
   if (small_rows(a)) {
     g.n_tiles = ceil_div(c.d, 128);
     g.tile_prefix = a.tile_prefix + tile_height_index(32) * (a.n_groups + 1);
-    return launch_fp8<32, 128, 1, 4, EPI_STORE, 4>(q, tile_bound8(a.rows_bound, a.n_groups, 32), s);
+    const int mt = tile_bound8(a.rows_bound, a.n_groups, 32);
+    return mx ? launch_fp8<32, 128, 1, 4, EPI_STORE, 3, WF_MXFP4>(q, mt, s)
+              : launch_fp8<32, 128, 1, 4, EPI_STORE, 3>(q, mt, s);
   }
   g.n_tiles = ceil_div(c.d, 256);
   g.tile_prefix = a.tile_prefix + tile_height_index(256) * (a.n_groups + 1);
-  return launch_fp8<256, 256, 4, 4, EPI_STORE, 2>(q, tile_bound8(a.rows_bound, a.n_groups, 256), s);
+  const int mt = tile_bound8(a.rows_bound, a.n_groups, 256);
+  return mx ? launch_fp8<256, 256, 4, 4, EPI_STORE, 3, WF_MXFP4>(q, mt, s)
+            : launch_fp8<256, 256, 4, 4, EPI_STORE, 2>(q, mt, s);
 }
 
 }  // namespace moe

@@ -13,6 +13,15 @@
 // 128-element block (one LDS stage) is two scaled MFMA steps straight into the
 // accumulator: the per-block promotion costs no vector instruction.
 //
+// MXFP4 weights (WF_MXFP4; the same page's FP4 QAT section: E2M1 with one
+// scale per 1x32 sub-block, native FP4 weights at inference, FP4 x FP8
+// products): B is packed E2M1 (two codes per byte) with an E8M0 scale byte per
+// weight row and 32-element K block, so
+//   acc = sum_b  sa[r, b/4] * sb[o, b] * sum_{k in block b} A[r, k] * B[o, k]
+// over 32-element blocks b.  The scaled MFMA takes FP8 A and FP4 B in one
+// instruction, and its per-lane B scale is exactly one such block (a lane's
+// column and K half), so the E8M0 bytes go to the matrix cores unchanged.
+//
 // Epilogues: EPI_SWIGLU8 (Linear-1): h = SiLU(g) * u in float32, then the FP8
 // cast of h in 1x128 groups -- a tile holds exactly one 128-column group of H
 // per row, so the group maximum is reduced across the tile's waves through
@@ -28,14 +37,19 @@ namespace gemm {
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 enum { EPI_SWIGLU8 = 3 };
+enum { WF_E4M3 = 0, WF_MXFP4 = 1 };  // weight formats
 
 struct Fp8Args {
   GemmArgs g;                 // operands as codes (1 byte per element); C: H codes or Y (bf16)
   const float* a_scale;       // [rows of A, K/128]: A row's scale per K block
   const int32_t* a_scale_rows;  // A row -> scale row (nullptr: same as the A row map)
-  const float* b_scale;       // group 0's [N_w/128, K/128] tile scales (N_w = weight rows)
-  const float* b_scale_last;  // the last group's, when it is not in b_scale (shared expert)
-  int64_t b_scale_group;      // floats between groups' tile scales
+  // weight scales of group 0: E4M3 weights: [N_w/128, K/128] float tile scales
+  // (N_w = weight rows); MXFP4: [K/128, N_w, 4] E8M0 bytes (per 128-column
+  // block of K, each row's four 32-element block scales)
+  const void* b_scale;
+  const void* b_scale_last;   // the last group's, when it is not in b_scale (shared expert)
+  int64_t b_scale_group;      // bytes between groups' weight scales (= one group's)
+  uint32_t b_scale_kstride;   // bytes between the scales of consecutive K blocks of a row
   float* c_scale;             // EPI_SWIGLU8: [rows, d_ff/128] scales of H
   int ldcs;                   // floats between rows of c_scale
   uint32_t as_bytes;          // bytes of a_scale (buffer range)
@@ -61,35 +75,49 @@ __device__ __forceinline__ int fp8_scale_exp(float amax) {
 // E8M0 form of a power-of-two float scale: its biased exponent
 __device__ __forceinline__ int e8m0_of(float s) { return (int)((__float_as_uint(s) >> 23) & 0xFFu); }
 
-// E4M3 MFMA 32x32x64 with E8M0 scales: lane l's sa scales A row l % 32 and
-// K half l / 32, lane l's sb scales B column l % 32 and K half l / 32
+// MFMA 32x32x64 with E8M0 scales, A in E4M3 and B in E4M3 (WF_E4M3) or E2M1
+// (WF_MXFP4: B's 32 codes per lane in the first four registers): lane l's sa
+// scales A row l % 32 and K half l / 32, lane l's sb scales B column l % 32 and
+// K half l / 32
+template <int WF>
 __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c,
                                            int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, WF == WF_MXFP4 ? 4 : 0, 0,
+                                                         sa, 0, sb);
 }
 
 // BM x BN tile, WM x WN waves (wave tile 32*FM x 32*FN), STAGES LDS buffers of
-// one 128-element K block each: A rows, B rows (128 bytes each, chunks
-// swizzled by (row >> 1) & 7), the block's A-row scales, and the block's scales
-// of the tile's (at most two) 128-row weight blocks.  Everything a stage needs
-// arrives through the same direct-to-LDS loads, issued STAGES-1 stages ahead.
-template <int BM, int BN, int WM, int WN, int EPI, int STAGES>
+// one 128-element K block each: A rows (128 bytes, chunks swizzled by
+// (row >> 1) & 7), B rows (E4M3: 128 bytes, swizzled likewise; MXFP4: 64 bytes,
+// chunks swizzled by (row >> 2) & 3), the block's A-row scales, and the
+// block's weight scales (E4M3: of the tile's at most two 128-row weight
+// blocks; MXFP4: one dword of four E8M0 bytes per B row).  Everything a stage
+// needs arrives through the same direct-to-LDS loads, issued STAGES-1 stages
+// ahead.
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int WF = WF_E4M3>
 __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
   const GemmArgs& p = q.g;
   constexpr int NT = 64 * WM * WN, NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr bool SW = EPI == EPI_SWIGLU8;
-  constexpr int ROWB = 128;                  // bytes (= K elements) of a row per stage
-  constexpr int RPL = 1024 / ROWB;           // rows filled by one wavefront load
+  constexpr bool MX = WF == WF_MXFP4;
+  constexpr int ROWB = 128;                  // bytes (= K elements) of an A row per stage
+  constexpr int BROWB = MX ? 64 : 128;       // bytes of a B row per stage
+  constexpr int RPL = 1024 / ROWB;           // A rows filled by one wavefront load
+  constexpr int RPLB = 1024 / BROWB;         // B rows filled by one wavefront load
+  constexpr int BCH = BROWB / 16;            // 16-byte chunks per B row
   constexpr int SAB = (BM > 64 ? BM : 64) * 4;  // A-row scale bytes per stage
-  constexpr int SBB = 256;                   // weight-block scale bytes per stage
-  constexpr int STAGE = (BM + BN) * ROWB + SAB + SBB;
-  constexpr int NSB = BN / 128;              // weight blocks per tile (<= 2)
-  constexpr int LA = BM / RPL / NW, LB = BN / RPL / NW;
+  constexpr int NSBL = MX ? BN / 64 : 1;     // weight-scale wavefront loads per stage
+  constexpr int SBB = 256 * NSBL;            // weight-scale bytes per stage
+  constexpr int OFF_B = BM * ROWB, OFF_SA = OFF_B + BN * BROWB, OFF_SB = OFF_SA + SAB;
+  constexpr int STAGE = OFF_SB + SBB;
+  constexpr int NSB = BN / 128;              // E4M3: weight blocks per tile (<= 2)
+  constexpr int LA = BM / RPL / NW, LB = BN / RPLB / NW;
   constexpr int NSA = (BM + 63) / 64;        // scale loads per stage (one per wave < NSA)
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "whole 32x32 fragments");
-  static_assert(LA * NW * RPL == BM && LB * NW * RPL == BN, "loads must split evenly");
+  static_assert(LA * NW * RPL == BM && LB * NW * RPLB == BN, "loads must split evenly");
+  static_assert(NSBL <= NW, "one weight-scale load per wave at most");
   static_assert(!SW || BN == 256, "SwiGLU8: one 128-column group of H per tile");
   static_assert(!SW || FN % 2 == 0, "SwiGLU waves hold gate and up fragments in pairs");
   static_assert(NSA <= NW, "one scale load per wave at most");
@@ -104,7 +132,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
   const int wm = wave / WN, wn = wave % WN;
   const bool last = p.B_last && tc.grp == p.G - 1;
   const char* Bg = last ? p.B_last : p.B + (int64_t)tc.grp * p.b_group;
-  const float* Sb = last ? q.b_scale_last : q.b_scale + (int64_t)tc.grp * q.b_scale_group;
+  const char* Sb = last ? static_cast<const char*>(q.b_scale_last)
+                        : static_cast<const char*>(q.b_scale) + tc.grp * q.b_scale_group;
   constexpr uint32_t kOut = 0x80000000u;
   const __amdgpu_buffer_rsrc_t a_rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.A), 0, (int)p.a_bytes, 0x00020000);
@@ -113,7 +142,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
   const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(q.a_scale), 0, (int)q.as_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t sb_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(Sb), 0, (int)(q.b_scale_group * 4), 0x00020000);
+      const_cast<char*>(Sb), 0, (int)q.b_scale_group, 0x00020000);
   const int KB = p.K / 128;  // K blocks (= stages of the loop)
 
   // operand rows: lane l of load j fills slot l % 8 of tile row RPL*(wave+NW*j) + l/8
@@ -130,20 +159,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
       a_off[j] = kOut;
     }
   }
+  // weight row of tile row `row` (-1: past the weight rows)
+  auto weight_row = [&](int row) -> int {
+    if (SW) return row < BN / 2 ? tc.nt * (BN / 2) + row : p.up_row + tc.nt * (BN / 2) + (row - BN / 2);
+    const int brow = tc.nt * BN + row;
+    return brow < p.N ? brow : -1;
+  };
 #pragma unroll
   for (int j = 0; j < LB; ++j) {
-    const int row = RPL * (wave + NW * j) + lr;
-    const int ch = lq ^ ((row >> 1) & 7);
-    int brow;
-    bool ok = true;
-    if (SW) {
-      brow = (RPL * (wave + NW * j) < BN / 2) ? tc.nt * (BN / 2) + row
-                                              : p.up_row + tc.nt * (BN / 2) + (row - BN / 2);
-    } else {
-      brow = tc.nt * BN + row;
-      ok = brow < p.N;
-    }
-    b_off[j] = ok ? (uint32_t)brow * (uint32_t)p.ldb + ch * 16 : kOut;
+    const int row = RPLB * (wave + NW * j) + lane / BCH;
+    const int ch = MX ? (lane % BCH) ^ ((row >> 2) & 3) : (lane % BCH) ^ ((row >> 1) & 7);
+    const int brow = weight_row(row);
+    b_off[j] = brow >= 0 ? (uint32_t)brow * (uint32_t)p.ldb + ch * 16 : kOut;
   }
   // A-row scales: wave w < NSA loads rows 64 w .. 64 w + 63 (4 bytes per lane)
   uint32_t s_off = kOut;
@@ -155,14 +182,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
       s_off = (uint32_t)srow * (uint32_t)(KB * 4);
     }
   }
-  // weight-block scales: lane j < NSB of the last wave loads block j of the tile
-  // (for SwiGLU: the gate block, then the up block); blocks past the weight
-  // rows read zeros
+  // weight scales, loaded by the last NSBL waves.  E4M3: lane j < NSB loads
+  // the scale row of the tile's weight block j (for SwiGLU: the gate block,
+  // then the up block).  MXFP4: lane l of load i loads tile row 64 i + l's four
+  // E8M0 bytes of the stage's K block (consecutive rows are consecutive words,
+  // so a load reads 256 contiguous bytes).  Rows past the weight rows read zeros.
   uint32_t sb_off = kOut;
-  if (lane < NSB) {
+  if constexpr (MX) {
+    const int brow = weight_row(64 * (wave - (NW - NSBL)) + lane);
+    if (wave >= NW - NSBL && brow >= 0) sb_off = (uint32_t)brow * 4u;
+  } else if (lane < NSB) {
     const int blk = SW ? (lane == 0 ? tc.nt : p.up_row / 128 + tc.nt) : tc.nt * NSB + lane;
     if (SW || blk * 128 < p.N) sb_off = (uint32_t)blk * (uint32_t)(KB * 4);
   }
+  const bool has_sa = wave < NSA, has_sb = wave >= NW - NSBL;  // scale loads of this wave
 #define MOE_FP8_ISSUE(kt_)                                                                 \
   do {                                                                                     \
     const int kc_ = (kt_) < KB ? (kt_) : KB - 1;                                           \
@@ -170,12 +203,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
     _Pragma("unroll") for (int j = 0; j < LA; ++j)                                          \
         load_lds16(a_rs, buf_ + (RPL * (wave + NW * j)) * ROWB, a_off[j] + kc_ * ROWB);     \
     _Pragma("unroll") for (int j = 0; j < LB; ++j)                                          \
-        load_lds16(b_rs, buf_ + BM * ROWB + (RPL * (wave + NW * j)) * ROWB,                 \
-                   b_off[j] + kc_ * ROWB);                                                 \
-    if (wave < NSA)                                                                        \
-      load_lds4(s_rs, buf_ + (BM + BN) * ROWB + 256 * wave, s_off + kc_ * 4);              \
-    if (wave == NW - 1)                                                                    \
-      load_lds4(sb_rs, buf_ + (BM + BN) * ROWB + SAB, sb_off + kc_ * 4);                   \
+        load_lds16(b_rs, buf_ + OFF_B + (RPLB * (wave + NW * j)) * BROWB,                   \
+                   b_off[j] + kc_ * BROWB);                                                \
+    if (has_sa)                                                                            \
+      load_lds4(s_rs, buf_ + OFF_SA + 256 * wave, s_off + kc_ * 4);                        \
+    if (has_sb)                                                                            \
+      load_lds4(sb_rs, buf_ + OFF_SB + 256 * (wave - (NW - NSBL)),                         \
+                sb_off + (uint32_t)kc_ * q.b_scale_kstride);                                \
   } while (0)
 
   f32x16 acc[FM][FN];
@@ -186,13 +220,23 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
 
-  // fragment reads: row lane % 32, 16-byte chunks 4 kk + 2 (lane / 32) and the next
+  // fragment reads: row lane % 32 of the K step kk (64 elements = four 16-byte
+  // chunks 4 kk .. 4 kk + 3 of an A row).  E4M3 x E4M3: lane half fh holds K
+  // 32 fh .. 32 fh + 31 of the step (chunks 2 fh, 2 fh + 1) on both sides.
+  // E4M3 x E2M1: a lane half's 32 FP4 codes meet the A elements at step
+  // positions 16 fh .. 16 fh + 15 and 32 + 16 fh .. 32 + 16 fh + 15, and its B
+  // scale covers exactly those; so B lanes take K 32 fh .. 32 fh + 31 (one
+  // 1x32 block, chunk 2 kk + fh of a 64-byte B row) and A lanes take chunks
+  // fh and fh + 2 of the step.
   const int fr = lane & 31, fh = lane >> 5, fs = (fr >> 1) & 7;
-  int rd0[2], rd1[2];
+  int rd0[2], rd1[2], rdb[2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
-    rd0[kk] = fr * ROWB + (((4 * kk + 2 * fh) ^ fs) << 4);
-    rd1[kk] = fr * ROWB + (((4 * kk + 2 * fh + 1) ^ fs) << 4);
+    const int c0 = MX ? 4 * kk + fh : 4 * kk + 2 * fh;
+    const int c1 = MX ? 4 * kk + fh + 2 : 4 * kk + 2 * fh + 1;
+    rd0[kk] = fr * ROWB + ((c0 ^ fs) << 4);
+    rd1[kk] = fr * ROWB + ((c1 ^ fs) << 4);
+    rdb[kk] = fr * BROWB + (((2 * kk + fh) ^ ((fr >> 2) & 3)) << 4);
   }
   int b_row[FN];
 #pragma unroll
@@ -211,23 +255,33 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
   const int live = min(FM, max(0, (tc.nrows - wm * WTM + 31) / 32));
   for (int kt = 0; kt < KB; ++kt) {
     static_assert((STAGES - 2) * (LA + LB + 2) <= 63, "vmcnt range");
-    // at most (STAGES-2) later stages' loads may still be in flight; waves that
-    // also issue scale loads have more loads per stage, so waiting for the count
-    // of a wave without them is conservative for every wave
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * (LA + LB)));
+    // at most (STAGES-2) later stages' loads may still be in flight: a wave's
+    // loads per stage are its operand loads plus one for each kind of scale it
+    // loads (wave-uniform branches, so each wave waits for its own count)
+    if (has_sa && has_sb)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * (LA + LB + 2)));
+    else if (has_sa || has_sb)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * (LA + LB + 1)));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * (LA + LB)));
     __builtin_amdgcn_s_waitcnt(0xC07F);
     lds_barrier();
     MOE_FP8_ISSUE(kt + STAGES - 1);
     const char* cur = smem + (kt % STAGES) * STAGE;
-    int sbe[FN];
+    // E4M3: the E8M0 form of the fragment's weight-block scale; MXFP4: the four
+    // E8M0 bytes of the lane's B column, shifted so byte 2 kk is its K half's
+    uint32_t sbw[FN];
 #pragma unroll
-    for (int f = 0; f < FN; ++f)
-      sbe[f] = e8m0_of(*reinterpret_cast<const float*>(cur + (BM + BN) * ROWB + SAB + 4 * sb_slot[f]));
+    for (int f = 0; f < FN; ++f) {
+      if constexpr (MX)
+        sbw[f] = *reinterpret_cast<const uint32_t*>(cur + OFF_SB + 4 * (b_row[f] + fr)) >> (8 * fh);
+      else
+        sbw[f] = e8m0_of(*reinterpret_cast<const float*>(cur + OFF_SB + 4 * sb_slot[f]));
+    }
     int sae[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      sae[i] = e8m0_of(*reinterpret_cast<const float*>(cur + (BM + BN) * ROWB +
-                                                       4 * (wm * WTM + 32 * i + fr)));
+      sae[i] = e8m0_of(*reinterpret_cast<const float*>(cur + OFF_SA + 4 * (wm * WTM + 32 * i + fr)));
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       i32x8 a[FM], b[FN];
@@ -241,17 +295,26 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
       }
 #pragma unroll
       for (int f = 0; f < FN; ++f) {
-        const char* src = cur + BM * ROWB + b_row[f] * ROWB;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(src + rd0[kk]);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(src + rd1[kk]);
-        b[f] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        const char* src = cur + OFF_B + b_row[f] * BROWB;
+        if constexpr (MX) {
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(src + rdb[kk]);
+          b[f] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
+        } else {
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(src + rd0[kk]);
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(src + rd1[kk]);
+          b[f] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
       }
+      int sbe[FN];
+#pragma unroll
+      for (int f = 0; f < FN; ++f) sbe[f] = MX ? (int)((sbw[f] >> (16 * kk)) & 0xFFu) : (int)sbw[f];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         if (i >= live) continue;
 #pragma unroll
-        for (int f = 0; f < FN; ++f) acc[i][f] = mfma_fp8(a[i], b[f], acc[i][f], sae[i], sbe[f]);
+        for (int f = 0; f < FN; ++f)
+          acc[i][f] = mfma_fp8<WF>(a[i], b[f], acc[i][f], sae[i], sbe[f]);
       }
     }
   }

@@ -126,7 +126,12 @@ hipError_t launch_expert_up(const moe_config& c, const ExpertFfnArgs& a, hipStre
 hipError_t launch_expert_down(const moe_config& c, const ExpertFfnArgs& a, hipStream_t s);
 
 // FP8 experts: E4M3 codes with float32 block scales (see include/moe.h)
+// The FP8 experts: E4M3 activations with 1x128 scales; weights in E4M3 with
+// 128x128 float tile scales (kWeightE4M3) or MXFP4 with 1x32 E8M0 scales
+// (kWeightMxfp4, codes packed two per byte)
+enum { kWeightE4M3 = 0, kWeightMxfp4 = 1 };
 struct Fp8FfnArgs {
+  int wfmt;                    // kWeightE4M3 or kWeightMxfp4
   const uint8_t* xq;           // [T, d] codes of the hidden rows
   const float* xs;             // [T, d/128]
   const int32_t* sorted_tok;   // [rows]
@@ -134,14 +139,14 @@ struct Fp8FfnArgs {
   const int32_t* g_end;        // [G]
   const int32_t* tile_prefix;  // [kNumTileHeights][G+1]
   int n_groups, rows_bound, routed_groups;
-  const uint8_t* w13q;         // [E, 2*d_ff, d]
-  const float* w13s;           // [E, 2*d_ff/128, d/128]
-  const uint8_t* w2q;          // [E, d, d_ff]
-  const float* w2s;            // [E, d/128, d_ff/128]
+  const uint8_t* w13q;         // E4M3: [E, 2*d_ff, d]; MXFP4: [E, 2*d_ff, d/2]
+  const void* w13s;            // E4M3: [E, 2*d_ff/128, d/128] float; MXFP4: [E, d/128, 2*d_ff, 4] bytes
+  const uint8_t* w2q;          // E4M3: [E, d, d_ff]; MXFP4: [E, d, d_ff/2]
+  const void* w2s;             // E4M3: [E, d/128, d_ff/128] float; MXFP4: [E, d_ff/128, d, 4] bytes
   const uint8_t* w13q_last;    // group E (shared) or nullptr
-  const float* w13s_last;
+  const void* w13s_last;
   const uint8_t* w2q_last;
-  const float* w2s_last;
+  const void* w2s_last;
   uint8_t* hq;                 // [rows, d_ff]
   float* hs;                   // [rows, d_ff/128]
   void* Y;                     // [rows, d] bfloat16
@@ -153,6 +158,10 @@ hipError_t launch_quantize_rows(int n, int K, int in_dtype, const void* x, uint8
                                 float* scales, hipStream_t s);
 hipError_t launch_quantize_blocks(int R, int C, int in_dtype, const void* w, uint8_t* q,
                                   float* scales, hipStream_t s);
+// MXFP4: n_mat matrices [R, C] in 1x32 blocks -> q [n_mat, R, C/2] packed E2M1,
+// scales [n_mat, C/128, R, 4] E8M0
+hipError_t launch_quantize_mxfp4(int n_mat, int R, int C, int in_dtype, const void* w, uint8_t* q,
+                                 uint8_t* scales, hipStream_t s);
 
 hipError_t launch_combine(const moe_config& c, const void* expert_out, const int32_t* dispatch,
                           const float* weights, const void* shared_out, void* out,

@@ -136,3 +136,28 @@ def test_fp8_entry_points_check_on_host():
     assert L.moe_forward_fp8(C.byref(c), *missing, 1 << 40, z) == -1
     assert L.moe_expert_up_fp8(C.byref(c), *([bogus] * 8), z, 1 << 40, z) == -1  # workspace null
     assert L.moe_expert_down_fp8(C.byref(c), *([bogus] * 6), bogus, 16, z) == -3
+
+
+def test_mxfp4_entry_points_check_on_host():
+    L = moe.load_library()
+    z = None
+    bogus = C.c_void_p(0x1000)
+    assert L.moe_quantize_mxfp4(1, 4, 96, 1, bogus, bogus, bogus, z) == -2    # C % 128
+    assert L.moe_quantize_mxfp4(1, -1, 128, 1, bogus, bogus, bogus, z) == -1
+    assert L.moe_quantize_mxfp4(-1, 4, 128, 1, bogus, bogus, bogus, z) == -1
+    assert L.moe_quantize_mxfp4(1, 4, 128, 5, bogus, bogus, bogus, z) == -1   # dtype
+    assert L.moe_quantize_mxfp4(1, 4, 128, 1, bogus, z, bogus, z) == -1
+    assert L.moe_quantize_mxfp4(0, 4, 128, 1, z, z, z, z) == 0               # nothing to do
+    assert L.moe_quantize_mxfp4(2, 0, 128, 1, z, z, z, z) == 0
+    fwd = [bogus] * 2 + [z] * 4 + [bogus] * 4 + [z] * 4 + [bogus] + [z] * 2 + [bogus]
+    c = cfg(d=256, d_ff=256, dtype="bf16")
+    assert L.moe_forward_mxfp4(C.byref(c), *fwd, 16, z) == -3                 # workspace
+    assert L.moe_forward_mxfp4(C.byref(cfg(d=256, d_ff=160, dtype="bf16")), *fwd, 1 << 40, z) == -2
+    assert L.moe_forward_mxfp4(C.byref(cfg(d=256, d_ff=256, dtype="f32")), *fwd, 1 << 40, z) == -2
+    assert L.moe_forward_mxfp4(C.byref(cfg(d=256, d_ff=256, dtype="bf16", n_shared=1)), *fwd,
+                               1 << 40, z) == -1                              # shared missing
+    missing = list(fwd)
+    missing[7] = z                                                            # w13s
+    assert L.moe_forward_mxfp4(C.byref(c), *missing, 1 << 40, z) == -1
+    assert L.moe_expert_up_mxfp4(C.byref(c), *([bogus] * 8), z, 1 << 40, z) == -1
+    assert L.moe_expert_down_mxfp4(C.byref(c), *([bogus] * 6), bogus, 16, z) == -3

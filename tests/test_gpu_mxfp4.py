@@ -1,0 +1,229 @@
+"""GPU parity of the MXFP4 expert weights (E2M1 codes, 1x32 E8M0 scales) against
+the oracle.
+
+The GPU quantizes the bf16 master weights with moe_quantize_mxfp4 and the hidden
+rows inside the layer; the oracle quantizes the same masters itself (pinned on
+the CPU), so no oracle input comes from the GPU.  Quantizer codes and scales
+must match bit for bit.  The expert stages and the layer then differ from the
+oracle only by float32 sums on the GPU against float64 in the oracle, which can
+flip an H code at a rounding boundary: the FP8 experts' bounds apply unchanged
+(decoded H within one E4M3 step or 4 subnormal steps, flips under 1%, a group
+scale one power of two away in at most 1% of groups; expert rows <= 2e-2; layer
+rows <= 5e-2 and median <= 1e-2).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_ffn_sqrt_amd as moe
+import oracle as O
+from mixture_experts_ffn_sqrt_amd.synth import CONFIGS, make_inputs, to_host_bits
+
+import parity_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+LAYER_TOL, LAYER_MEDIAN_TOL = 5e-2, 1e-2
+
+
+def gpu_mx(w):
+    lead, R, C_ = tuple(w.shape[:-2]), w.shape[-2], w.shape[-1]
+    q = torch.empty(lead + (R, C_ // 2), dtype=torch.uint8, device="cuda")
+    s = torch.empty(lead + (C_ // 128, R, 4), dtype=torch.uint8, device="cuda")
+    moe.moe_quantize_mxfp4(w, q, s)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+def kmajor(s):
+    """Oracle scales [R, C/32] -> the library's K-block-major layout [C/128, R, 4]."""
+    R, G = s.shape
+    return np.ascontiguousarray(s.reshape(R, G // 4, 4).transpose(1, 0, 2))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_quantize_mxfp4_bit_exact(dtype):
+    g = torch.Generator().manual_seed(41)
+    w = torch.randn((70, 384), generator=g) * torch.logspace(-5, 4, 70).unsqueeze(1)
+    w[3, 64:96] = 0.0                                    # an all-zero block
+    ties = torch.tensor([6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    w[4, :32] = ties.repeat(4)                           # exact ties, scale 1
+    w[5, :32] = -ties.repeat(4) * 2.0 ** -7              # the same at scale 2^-7
+    w[6, :] = 1e-30                                      # tiny blocks
+    w[7, 32:64] = 3.0e38 * torch.linspace(-1, 1, 32)     # near the float range
+    w = w.to(dtype)
+    q, s = gpu_mx(w.cuda())
+    rq, rs = O.quantize_mxfp4(to_host_bits(w))
+    assert np.array_equal(s, kmajor(rs)), np.argwhere(s != kmajor(rs))[:5]
+    assert np.array_equal(q, rq), np.argwhere(q != rq)[:5]
+
+
+def test_quantize_mxfp4_expert_stack_bit_exact():
+    g = torch.Generator().manual_seed(42)
+    w = (torch.randn((3, 256, 384), generator=g) * 0.02).to(torch.bfloat16)
+    w[1, :, 32:64] *= 50
+    q, s = gpu_mx(w.cuda())
+    for e in range(3):   # each matrix has its own scale table
+        rq, rs = O.quantize_mxfp4(to_host_bits(w[e]))
+        assert np.array_equal(s[e], kmajor(rs)), e
+        assert np.array_equal(q[e], rq), e
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+@pytest.mark.parametrize("T, d, E, k, d_ff", [
+    (40, 256, 16, 4, 256),      # a few rows per expert: 32-row streaming tiles
+    (700, 256, 4, 2, 384),      # 256x256 tiles, ragged rows per expert
+    (300, 384, 3, 3, 128),      # k = E, d not a multiple of 256 (partial column tile)
+    (1, 512, 8, 2, 256),        # one token
+])
+def test_expert_up_down_mxfp4(T, d, E, k, d_ff):
+    lc = CONFIGS["mixtral_prefill"].with_(T=T, d=d, E=E, k=k, d_ff=d_ff, seed=37)
+    inp = make_inputs(lc, "cuda")
+    rng = np.random.default_rng(T + 1)
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    perm = O.permute(ids, np.ones((T, k), np.float32), E)
+    c = H.cfg_of(lc)
+    ws = torch.empty(moe.moe_workspace_size(c), dtype=torch.uint8, device="cuda")
+    xq = torch.empty((T, d), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((T, d // 128), dtype=torch.float32, device="cuda")
+    moe.moe_quantize_fp8_rows(inp["hidden"], xq, xs)
+    mx = moe.quantize_mxfp4_weights(inp)
+    hq = torch.zeros((T * k, d_ff), dtype=torch.uint8, device="cuda")
+    hs = torch.zeros((T * k, d_ff // 128), dtype=torch.float32, device="cuda")
+    y = torch.zeros((T * k, d), dtype=torch.bfloat16, device="cuda")
+    st, off = _dev(perm["sorted_token_ids"]), _dev(perm["offsets"])
+    moe.moe_expert_up_mxfp4(c, xq, xs, st, off, mx["w13q"], mx["w13s"], hq, hs, ws)
+    moe.moe_expert_down_mxfp4(c, hq, hs, off, mx["w2q"], mx["w2s"], y, ws)
+    torch.cuda.synchronize()
+    x_f = inp["hidden"].float().cpu().numpy()
+    rxq, rxs = O.quantize_rows(x_f)
+    q13 = [O.quantize_mxfp4(to_host_bits(inp["w13"][e])) for e in range(E)]
+    q2 = [O.quantize_mxfp4(to_host_bits(inp["w2"][e])) for e in range(E)]
+    for e in range(E):   # the GPU's weight codes and scales are the oracle's
+        assert np.array_equal(mx["w13q"][e].cpu().numpy(), q13[e][0])
+        assert np.array_equal(mx["w13s"][e].cpu().numpy(), kmajor(q13[e][1]))
+        assert np.array_equal(mx["w2q"][e].cpu().numpy(), q2[e][0])
+        assert np.array_equal(mx["w2s"][e].cpu().numpy(), kmajor(q2[e][1]))
+    expert_of_row = np.repeat(np.arange(E), perm["counts"])
+    g_hq, g_hs = hq.cpu().numpy(), hs.cpu().numpy()
+    flips, scale_moves, ref_y = 0, 0, []
+    for r, (t, e) in enumerate(zip(perm["sorted_token_ids"], expert_of_row)):
+        rhq, rhs = O.expert_up_mxfp4(rxq[t], rxs[t], *q13[e])
+        ratio = g_hs[r] / rhs
+        assert np.all((ratio == 1) | (ratio == 2) | (ratio == 0.5)), (r, g_hs[r], rhs)
+        scale_moves += int((ratio != 1).sum())
+        hg = O.e4m3_decode(g_hq[r]).reshape(-1, 128) * g_hs[r][:, None]
+        hr = O.e4m3_decode(rhq).reshape(-1, 128) * rhs[:, None]
+        flips += int((hg != hr)[ratio == 1].sum())
+        smax = np.maximum(g_hs[r], rhs)[:, None]
+        assert np.all(np.abs(hg - hr) <= np.abs(hr) / 8 + 4 * 2.0 ** -9 * smax), r
+        ref_y.append(O.expert_ffn_mxfp4(rxq[t], rxs[t], *q13[e], *q2[e]))
+    assert flips <= max(4, 1e-2 * g_hq.size), flips
+    assert scale_moves <= max(1, 1e-2 * g_hs.size), scale_moves
+    err = H.row_rel_err(H.to_f64(y), np.stack(ref_y))
+    assert err.max() <= TOL, err.max()
+
+
+MX_LAYERS = {
+    "mixtral_small": CONFIGS["mixtral_prefill"].with_(T=512, d=512, d_ff=1024),
+    "dsv3_groups_shared": CONFIGS["dsv3_prefill"].with_(T=1024, d=256, E=16, k=4, d_ff=128,
+                                                        n_group=4, topk_group=2, group_topk=2),
+    "v4flash_decode_small": CONFIGS["v4flash_decode"].with_(d=512, d_ff=256),
+    "v4pro_skew_small": CONFIGS["v4pro_skew_prefill"].with_(T=2048, d=256, E=16, k=4, d_ff=256),
+    "decode_T1": CONFIGS["v4flash_decode"].with_(T=1, d=256, d_ff=128),
+}
+
+
+def oracle_layer_mx_rows(lc, inp, rows, route_mode=O.LEARNED):
+    """Oracle MXFP4 layer on the listed rows; the needed experts' weights are
+    quantized from their bf16 masters by the oracle."""
+    hb = to_host_bits(inp["hidden"])
+    wr = to_host_bits(inp["w_router"])
+    bias = to_host_bits(inp.get("bias"))
+    off = to_host_bits(inp.get("logit_offset"))
+    tok = to_host_bits(inp.get("token_ids"))
+    tab = to_host_bits(inp.get("tid2eid"))
+    rows = np.asarray(rows, np.int32)
+    grp = dict(n_group=lc.n_group, topk_group=lc.topk_group, group_topk=lc.group_topk)
+    lg = O.logits(hb, wr, rows=rows, logit_offset=off).astype(np.float32)
+    if route_mode == O.HASH:
+        ids, _ = O.hash_route(lg, tok[rows], tab, lc.scoring)
+    else:
+        ids, _, _ = O.route(lg, lc.k, lc.scoring, bias=bias, **grp)
+    w13q, w13s, w2q, w2s = [None] * lc.E, [None] * lc.E, [None] * lc.E, [None] * lc.E
+    for e in sorted(set(ids.ravel().tolist())):
+        w13q[e], w13s[e] = O.quantize_mxfp4(to_host_bits(inp["w13"][e]))
+        w2q[e], w2s[e] = O.quantize_mxfp4(to_host_bits(inp["w2"][e]))
+    shared = None
+    if inp.get("w13_shared") is not None:
+        shared = O.quantize_mxfp4(to_host_bits(inp["w13_shared"])) + \
+            O.quantize_mxfp4(to_host_bits(inp["w2_shared"]))
+    return O.layer_mxfp4(hb, wr, w13q, w13s, w2q, w2s, lc.k, lc.scoring, rows=rows, bias=bias,
+                         logit_offset=off, shared=shared, route_mode=route_mode, token_ids=tok,
+                         tid2eid=tab, d_ff=lc.d_ff, **grp)
+
+
+def check_layer_mx(lc, inp, out, ids, gates, rows, route_mode=O.LEARNED):
+    ref = oracle_layer_mx_rows(lc, inp, rows, route_mode)
+    rows = np.asarray(rows)
+    g_ids = ids.cpu().numpy()[rows]
+    tie = (ref["margin"] <= H.TIE_LAYER) if route_mode == O.LEARNED else np.zeros(len(rows), bool)
+    ok = ~tie
+    assert tie.sum() <= max(2, 0.02 * len(rows))
+    assert np.array_equal(g_ids[ok], ref["ids"][ok])
+    assert np.abs(gates.cpu().numpy()[rows][ok] - ref["gates"][ok]).max(initial=0) <= 1e-5
+    err = H.row_rel_err(H.to_f64(out)[rows][ok], ref["out"][ok])
+    assert err.max(initial=0) <= LAYER_TOL, err.max()
+    assert np.median(err) <= LAYER_MEDIAN_TOL, np.median(err)
+    return err
+
+
+@pytest.mark.parametrize("name", list(MX_LAYERS))
+def test_forward_mxfp4_small(name):
+    lc = MX_LAYERS[name]
+    inp = make_inputs(lc, "cuda")
+    layer = moe.MoELayer(H.cfg_of(lc), inp)
+    out = layer.forward_mxfp4(moe.quantize_mxfp4_weights(inp))
+    torch.cuda.synchronize()
+    check_layer_mx(lc, inp, out, layer.ids, layer.gates, rows=np.arange(lc.T))
+
+
+def test_forward_mxfp4_hash_pass():
+    lc = CONFIGS["v4flash_decode"].with_(d=256, d_ff=256)
+    inp = make_inputs(lc, "cuda", hash_pass=True)
+    c = H.cfg_of(lc, route_mode=moe.MOE_ROUTE_HASH, vocab=lc.hash_vocab)
+    layer = moe.MoELayer(c, inp)
+    out = layer.forward_mxfp4(moe.quantize_mxfp4_weights(inp))
+    torch.cuda.synchronize()
+    check_layer_mx(lc, inp, out, layer.ids, layer.gates, rows=np.arange(lc.T), route_mode=O.HASH)
+
+
+@pytest.mark.parametrize("name, n_rows", [("mixtral_prefill", 16), ("v4flash_decode", 6),
+                                          ("dsv3_prefill", 6)])
+def test_forward_mxfp4_full_size_sampled(name, n_rows):
+    lc = CONFIGS[name]
+    inp = make_inputs(lc, "cuda")
+    layer = moe.MoELayer(H.cfg_of(lc), inp)
+    mx = moe.quantize_mxfp4_weights(inp)
+    out = layer.forward_mxfp4(mx)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(6).choice(lc.T, n_rows, replace=False)
+    check_layer_mx(lc, inp, out, layer.ids, layer.gates, rows=np.sort(rows))
+
+
+def test_forward_mxfp4_batch_invariant():
+    lc = MX_LAYERS["mixtral_small"]
+    inp = make_inputs(lc, "cuda")
+    mx = moe.quantize_mxfp4_weights(inp)
+    layer = moe.MoELayer(H.cfg_of(lc), inp)
+    full = layer.forward_mxfp4(mx).clone()
+    for a, b in [(0, 1), (7, 60), (400, 512)]:
+        sub = dict(inp)
+        sub["hidden"] = inp["hidden"][a:b].contiguous()
+        part = moe.MoELayer(H.cfg_of(lc, T=b - a), sub).forward_mxfp4(mx)
+        torch.cuda.synchronize()
+        assert torch.equal(part, full[a:b]), (a, b)
