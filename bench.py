@@ -243,10 +243,10 @@ def run_lowp(kind, lc, c, layer, inp, perm, ws, Y, counts, decode, steps, warmup
     ms_step, _ = time_gpu(lambda: fwd(wq), steps, warmup, stream)
     print("[bench] %s %s: %.3f ms/step" % (lc.name, kind, ms_step), file=sys.stderr, flush=True)
     xq = torch.empty((T, d), dtype=torch.uint8, device="cuda")
-    xs = torch.empty((T, d // 128), dtype=torch.float32, device="cuda")
+    xs = torch.empty((d // 128, T), dtype=torch.float32, device="cuda")
     moe.moe_quantize_fp8_rows(inp["hidden"], xq, xs)
     hq = torch.empty((T * k, F), dtype=torch.uint8, device="cuda")
-    hs = torch.empty((T * k, F // 128), dtype=torch.float32, device="cuda")
+    hs = torch.empty((F // 128, T * k), dtype=torch.float32, device="cuda")
     up_fn = moe.moe_expert_up_mxfp4 if mx else moe.moe_expert_up_fp8
     down_fn = moe.moe_expert_down_mxfp4 if mx else moe.moe_expert_down_fp8
 
@@ -281,8 +281,9 @@ def run_lowp(kind, lc, c, layer, inp, perm, ws, Y, counts, decode, steps, warmup
 
 
 def peaks():
-    """Reference points on random N(0,1) bf16 data: the vendor BLAS (torch.mm ->
-    hipBLASLt) on an 8192^3 GEMM, and a device-to-device copy."""
+    """Reference points on random N(0,1) data: the vendor BLAS (torch.mm and
+    torch._scaled_mm -> hipBLASLt) on an 8192^3 GEMM in bf16 and in E4M3, and a
+    device-to-device copy."""
     import torch
     g = torch.Generator(device="cuda").manual_seed(0)
     n = 8192
@@ -290,6 +291,19 @@ def peaks():
     b = torch.randn((n, n), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
     ms, _ = time_gpu(lambda: torch.mm(a, b), 10, 3, torch.cuda.current_stream())
     gemm = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    # the same shape in E4M3 with per-tensor scales (torch._scaled_mm -> hipBLASLt)
+    fp8 = None
+    try:
+        a8 = a.to(torch.float8_e4m3fn)
+        b8 = b.t().contiguous().to(torch.float8_e4m3fn)   # [N, K] row-major = column-major B
+        one = torch.ones((), device="cuda", dtype=torch.float32)
+        ms8, _ = time_gpu(lambda: torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one,
+                                                   out_dtype=torch.bfloat16),
+                          10, 3, torch.cuda.current_stream())
+        fp8 = round(2.0 * n ** 3 / (ms8 * 1e-3) / 1e12, 1)
+        del a8, b8
+    except (RuntimeError, TypeError, AttributeError) as e:  # not offered by this torch build
+        print("[bench] vendor fp8 GEMM unavailable: %s" % str(e)[:120], file=sys.stderr)
     del a, b
     src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -297,6 +311,7 @@ def peaks():
     copy = 2 * (1 << 30) / (ms * 1e-3) / 1e9
     return dict(vendor_bf16_gemm_8192_tflops=round(gemm, 1),
                 vendor_bf16_gemm_frac_of_spec=round(gemm / PEAK_TFLOPS["bf16"], 4),
+                vendor_fp8_gemm_8192_tflops=fp8,
                 copy_1gib_gbs_read_plus_write=round(copy, 1))
 
 

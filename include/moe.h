@@ -181,7 +181,10 @@ int moe_forward(const moe_config *cfg, const void *hidden, const void *w_router,
  *            w2q [E, d, d_ff] with w2s [E, d/128, d_ff/128]: one scale per
  *            128x128 tile (row-major over tiles).  Shared expert: one expert's worth.
  *   Activations (hidden rows before Linear-1, h after the activation): one scale
- *            per row per 128 columns: codes [rows, K], scales [rows, K/128].
+ *            per row per 128 columns: codes [rows, K], scales stored
+ *            K-block-major, [K/128, rows] (column group g of all rows
+ *            together, so the matrix cores' loads read one group's scales of
+ *            consecutive rows as contiguous words).
  *   A group's scale is a power of two, 2^e: the smallest with max |x| <= 448 * 2^e
  *   (e >= -126; an all-zero group has scale 1); its codes are E4M3(x * 2^-e),
  *   nearest-even, saturated to +-448.  Power-of-two tile scales keep FP4 (E2M1)
@@ -196,7 +199,7 @@ int moe_forward(const moe_config *cfg, const void *hidden, const void *w_router,
  * 2 GiB.  Workspace: moe_workspace_size covers them. */
 
 /* Quantize the rows of x [n, K] (in_dtype MOE_F32 or MOE_BF16) in groups of 128
- * columns: q [n, K] uint8 codes, scales [n, K/128].  K a multiple of 128 (else
+ * columns: q [n, K] uint8 codes, scales [K/128, n].  K a multiple of 128 (else
  * MOE_ERR_UNSUPPORTED).  Needs no workspace; n == 0 queues nothing. */
 int moe_quantize_fp8_rows(int n, int K, int in_dtype, const void *x, uint8_t *q, float *scales,
                           void *stream);
@@ -211,14 +214,14 @@ int moe_quantize_fp8_blocks(int R, int C, int in_dtype, const void *w, uint8_t *
  * dispatch row r in [expert_offsets[e], expert_offsets[e+1]),
  *   h = SiLU(W1_e x) (.) W3_e x in float32, x = the codes xq[sorted_token_ids[r]]
  *   with their scales; hq[r], hs[r] = the 128-column-group quantization of h.
- * xq [T, d], xs [T, d/128]; hq [T*k, d_ff] uint8; hs [T*k, d_ff/128]. */
+ * xq [T, d], xs [d/128, T]; hq [T*k, d_ff] uint8; hs [d_ff/128, T*k]. */
 int moe_expert_up_fp8(const moe_config *cfg, const uint8_t *xq, const float *xs,
                       const int32_t *sorted_token_ids, const int32_t *expert_offsets,
                       const uint8_t *w13q, const float *w13s, uint8_t *hq, float *hs,
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /* FP8 Linear-2: expert_out[r] = W2_e h[r] for the same rows, bfloat16 rounded
- * once from float32.  hq [T*k, d_ff], hs [T*k, d_ff/128]; expert_out [T*k, d]. */
+ * once from float32.  hq [T*k, d_ff], hs [d_ff/128, T*k]; expert_out [T*k, d]. */
 int moe_expert_down_fp8(const moe_config *cfg, const uint8_t *hq, const float *hs,
                         const int32_t *expert_offsets, const uint8_t *w2q, const float *w2s,
                         void *expert_out, void *workspace, size_t workspace_bytes,

@@ -255,12 +255,13 @@ _IN_DTYPES = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
 
 
 def moe_quantize_fp8_rows(x, q, scales, stream=None):
-    """x [n, K] float32/bfloat16 -> q [n, K] uint8 E4M3 codes, scales [n, K/128]."""
+    """x [n, K] float32/bfloat16 -> q [n, K] uint8 E4M3 codes, scales [K/128, n]
+    (K-block-major)."""
     if x.dtype not in _IN_DTYPES:
         raise ValueError("x must be float32 or bfloat16, got %s" % x.dtype)
     n, K = x.shape
     args = [n, K, _IN_DTYPES[x.dtype], _t("x", x, (n, K), x.dtype),
-            _t("q", q, (n, K), torch.uint8), _t("scales", scales, (n, K // 128), torch.float32),
+            _t("q", q, (n, K), torch.uint8), _t("scales", scales, (K // 128, n), torch.float32),
             _stream(stream)]
     _check("moe_quantize_fp8_rows", load_library().moe_quantize_fp8_rows(*args))
 
@@ -284,11 +285,11 @@ def moe_expert_up_fp8(cfg, xq, xs, sorted_token_ids, expert_offsets, w13q, w13s,
     T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
     u8, f32 = torch.uint8, torch.float32
     args = [C.byref(cfg),
-            _t("xq", xq, (T, d), u8), _t("xs", xs, (T, d // 128), f32),
+            _t("xq", xq, (T, d), u8), _t("xs", xs, (d // 128, T), f32),
             _t("sorted_token_ids", sorted_token_ids, (T * k,), torch.int32),
             _t("expert_offsets", expert_offsets, (E + 1,), torch.int32),
             _t("w13q", w13q, (E, 2 * F, d), u8), _t("w13s", w13s, (E, 2 * F // 128, d // 128), f32),
-            _t("hq", hq, (T * k, F), u8), _t("hs", hs, (T * k, F // 128), f32),
+            _t("hq", hq, (T * k, F), u8), _t("hs", hs, (F // 128, T * k), f32),
             *_ws(cfg, workspace), _stream(stream)]
     _check("moe_expert_up_fp8", load_library().moe_expert_up_fp8(*args))
 
@@ -298,7 +299,7 @@ def moe_expert_down_fp8(cfg, hq, hs, expert_offsets, w2q, w2s, expert_out, works
     T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
     u8, f32 = torch.uint8, torch.float32
     args = [C.byref(cfg),
-            _t("hq", hq, (T * k, F), u8), _t("hs", hs, (T * k, F // 128), f32),
+            _t("hq", hq, (T * k, F), u8), _t("hs", hs, (F // 128, T * k), f32),
             _t("expert_offsets", expert_offsets, (E + 1,), torch.int32),
             _t("w2q", w2q, (E, d, F), u8), _t("w2s", w2s, (E, d // 128, F // 128), f32),
             _t("expert_out", expert_out, (T * k, d), torch.bfloat16),
@@ -373,12 +374,12 @@ def moe_expert_up_mxfp4(cfg, xq, xs, sorted_token_ids, expert_offsets, w13q, w13
     T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
     u8, f32 = torch.uint8, torch.float32
     args = [C.byref(cfg),
-            _t("xq", xq, (T, d), u8), _t("xs", xs, (T, d // 128), f32),
+            _t("xq", xq, (T, d), u8), _t("xs", xs, (d // 128, T), f32),
             _t("sorted_token_ids", sorted_token_ids, (T * k,), torch.int32),
             _t("expert_offsets", expert_offsets, (E + 1,), torch.int32),
             _t("w13q", w13q, (E, 2 * F, d // 2), u8),
             _t("w13s", w13s, (E, d // 128, 2 * F, 4), u8),
-            _t("hq", hq, (T * k, F), u8), _t("hs", hs, (T * k, F // 128), f32),
+            _t("hq", hq, (T * k, F), u8), _t("hs", hs, (F // 128, T * k), f32),
             *_ws(cfg, workspace), _stream(stream)]
     _check("moe_expert_up_mxfp4", load_library().moe_expert_up_mxfp4(*args))
 
@@ -388,7 +389,7 @@ def moe_expert_down_mxfp4(cfg, hq, hs, expert_offsets, w2q, w2s, expert_out, wor
     T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
     u8, f32 = torch.uint8, torch.float32
     args = [C.byref(cfg),
-            _t("hq", hq, (T * k, F), u8), _t("hs", hs, (T * k, F // 128), f32),
+            _t("hq", hq, (T * k, F), u8), _t("hs", hs, (F // 128, T * k), f32),
             _t("expert_offsets", expert_offsets, (E + 1,), torch.int32),
             _t("w2q", w2q, (E, d, F // 2), u8), _t("w2s", w2s, (E, F // 128, d, 4), u8),
             _t("expert_out", expert_out, (T * k, d), torch.bfloat16),

@@ -36,7 +36,9 @@ __device__ __forceinline__ float wave_max64(float v) {
   return v;
 }
 
-// One wavefront per (row, 128-column group): two elements per lane.
+// One wavefront per (row, 128-column group): two elements per lane.  Scales
+// are stored K-block-major, [K/128, n], so that one group's scales of
+// consecutive rows are contiguous for the GEMMs' loads.
 template <typename TIn>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(int n, int K, const TIn* x,
                                                             uint8_t* q, float* scales) {
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(int n, int K, const 
   const float inv = ldexpf(1.0f, -e);
   const uint32_t c0 = e4m3_code(v0 * inv), c1 = e4m3_code(v1 * inv);
   *reinterpret_cast<uint16_t*>(q + base) = (uint16_t)(c0 | (c1 << 8));
-  if (lane == 0) scales[row * G + g] = ldexpf(1.0f, e);
+  if (lane == 0) scales[(int64_t)g * n + row] = ldexpf(1.0f, e);
 }
 
 // E2M1 code of v, nearest with ties to the even mantissa, saturated to +-6: the
@@ -234,8 +236,9 @@ hipError_t launch_expert_up_fp8(const moe_config& c, const Fp8FfnArgs& a, hipStr
   q.b_scale_group = mx ? 2 * F * (d / 32) : (2 * F / 128) * (d / 128) * 4;
   q.b_scale_kstride = mx ? (uint32_t)(2 * F * 4) : 4u;
   q.c_scale = a.hs;
-  q.ldcs = c.d_ff / 128;
+  q.ldcs = a.rows_bound;
   q.as_bytes = (uint32_t)((int64_t)c.T * (d / 128) * 4);
+  q.as_kstride = (uint32_t)(c.T * 4);
   if (small_rows(a)) {
     g.tile_prefix = a.tile_prefix + tile_height_index(32) * (a.n_groups + 1);
     const int mt = tile_bound8(a.rows_bound, a.n_groups, 32);
@@ -244,8 +247,8 @@ hipError_t launch_expert_up_fp8(const moe_config& c, const Fp8FfnArgs& a, hipStr
   }
   g.tile_prefix = a.tile_prefix + tile_height_index(256) * (a.n_groups + 1);
   const int mt = tile_bound8(a.rows_bound, a.n_groups, 256);
-  return mx ? launch_fp8<256, 256, 4, 4, EPI_SWIGLU8, 3, WF_MXFP4>(q, mt, s)
-            : launch_fp8<256, 256, 4, 4, EPI_SWIGLU8, 2>(q, mt, s);
+  return mx ? launch_fp8<256, 256, 4, 2, EPI_SWIGLU8, 3, WF_MXFP4>(q, mt, s)
+            : launch_fp8<256, 256, 4, 2, EPI_SWIGLU8, 2>(q, mt, s);
 }
 
 hipError_t launch_expert_down_fp8(const moe_config& c, const Fp8FfnArgs& a, hipStream_t s) {
@@ -275,6 +278,7 @@ hipError_t launch_expert_down_fp8(const moe_config& c, const Fp8FfnArgs& a, hipS
   q.b_scale_group = mx ? d * (F / 32) : (d / 128) * (F / 128) * 4;
   q.b_scale_kstride = mx ? (uint32_t)(d * 4) : 4u;
   q.as_bytes = (uint32_t)((int64_t)a.rows_bound * (F / 128) * 4);
+  q.as_kstride = (uint32_t)(a.rows_bound * 4);
   if (small_rows(a)) {
     g.n_tiles = ceil_div(c.d, 128);
     g.tile_prefix = a.tile_prefix + tile_height_index(32) * (a.n_groups + 1);

@@ -41,7 +41,7 @@ enum { WF_E4M3 = 0, WF_MXFP4 = 1 };  // weight formats
 
 struct Fp8Args {
   GemmArgs g;                 // operands as codes (1 byte per element); C: H codes or Y (bf16)
-  const float* a_scale;       // [rows of A, K/128]: A row's scale per K block
+  const float* a_scale;       // [K/128, scale rows]: a K block's scales of all rows together
   const int32_t* a_scale_rows;  // A row -> scale row (nullptr: same as the A row map)
   // weight scales of group 0: E4M3 weights: [N_w/128, K/128] float tile scales
   // (N_w = weight rows); MXFP4: [K/128, N_w, 4] E8M0 bytes (per 128-column
@@ -50,9 +50,10 @@ struct Fp8Args {
   const void* b_scale_last;   // the last group's, when it is not in b_scale (shared expert)
   int64_t b_scale_group;      // bytes between groups' weight scales (= one group's)
   uint32_t b_scale_kstride;   // bytes between the scales of consecutive K blocks of a row
-  float* c_scale;             // EPI_SWIGLU8: [rows, d_ff/128] scales of H
-  int ldcs;                   // floats between rows of c_scale
+  float* c_scale;             // EPI_SWIGLU8: [d_ff/128, rows] scales of H
+  int ldcs;                   // floats between K blocks of c_scale (its rows)
   uint32_t as_bytes;          // bytes of a_scale (buffer range)
+  uint32_t as_kstride;        // bytes between K blocks of a_scale
 };
 
 // E4M3 code of v (finite; saturated to +-448), nearest-even.
@@ -172,14 +173,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
     const int brow = weight_row(row);
     b_off[j] = brow >= 0 ? (uint32_t)brow * (uint32_t)p.ldb + ch * 16 : kOut;
   }
-  // A-row scales: wave w < NSA loads rows 64 w .. 64 w + 63 (4 bytes per lane)
+  // A-row scales: wave w < NSA loads rows 64 w .. 64 w + 63 (4 bytes per lane;
+  // the K-block-major layout keeps a stage's scales of ascending rows together)
   uint32_t s_off = kOut;
   {
     const int row = 64 * wave + lane;
     if (wave < NSA && row < tc.nrows) {
       const int arow = p.a_rows ? p.a_rows[tc.row0 + row] : tc.row0 + row;
       const int srow = q.a_scale_rows ? q.a_scale_rows[tc.row0 + row] : arow;
-      s_off = (uint32_t)srow * (uint32_t)(KB * 4);
+      s_off = (uint32_t)srow * 4u;
     }
   }
   // weight scales, loaded by the last NSBL waves.  E4M3: lane j < NSB loads
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
         load_lds16(b_rs, buf_ + OFF_B + (RPLB * (wave + NW * j)) * BROWB,                   \
                    b_off[j] + kc_ * BROWB);                                                \
     if (has_sa)                                                                            \
-      load_lds4(s_rs, buf_ + OFF_SA + 256 * wave, s_off + kc_ * 4);                        \
+      load_lds4(s_rs, buf_ + OFF_SA + 256 * wave, s_off + (uint32_t)kc_ * q.as_kstride);   \
     if (has_sb)                                                                            \
       load_lds4(sb_rs, buf_ + OFF_SB + 256 * (wave - (NW - NSBL)),                         \
                 sb_off + (uint32_t)kc_ * q.b_scale_kstride);                                \
@@ -376,7 +378,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
           const int col = tc.nt * (BN / 2) + wn * (WTN / 2) + 32 * f + ccol;
           crow_ptr[col] = (uint8_t)e4m3_code(h[i][f][r] * inv);
         }
-        if (wn == 0 && ccol == 0) q.c_scale[row * q.ldcs + tc.nt] = ldexpf(1.0f, e);
+        if (wn == 0 && ccol == 0) q.c_scale[(int64_t)tc.nt * q.ldcs + row] = ldexpf(1.0f, e);
       }
     }
   } else {

@@ -133,7 +133,7 @@ enum { kWeightE4M3 = 0, kWeightMxfp4 = 1 };
 struct Fp8FfnArgs {
   int wfmt;                    // kWeightE4M3 or kWeightMxfp4
   const uint8_t* xq;           // [T, d] codes of the hidden rows
-  const float* xs;             // [T, d/128]
+  const float* xs;             // [d/128, T] (K-block-major)
   const int32_t* sorted_tok;   // [rows]
   const int32_t* g_begin;      // [G]
   const int32_t* g_end;        // [G]
@@ -148,7 +148,7 @@ struct Fp8FfnArgs {
   const uint8_t* w2q_last;
   const void* w2s_last;
   uint8_t* hq;                 // [rows, d_ff]
-  float* hs;                   // [rows, d_ff/128]
+  float* hs;                   // [d_ff/128, rows_bound] (K-block-major)
   void* Y;                     // [rows, d] bfloat16
 };
 hipError_t launch_expert_up_fp8(const moe_config& c, const Fp8FfnArgs& a, hipStream_t s);

@@ -32,12 +32,13 @@ LAYER_TOL, LAYER_MEDIAN_TOL = 5e-2, 1e-2
 
 
 def gpu_rows_q(x):
+    """codes [n, K] and scales as [n, K/128] (the library stores them [K/128, n])"""
     n, K = x.shape
     q = torch.empty((n, K), dtype=torch.uint8, device="cuda")
-    s = torch.empty((n, K // 128), dtype=torch.float32, device="cuda")
+    s = torch.empty((K // 128, n), dtype=torch.float32, device="cuda")
     moe.moe_quantize_fp8_rows(x, q, s)
     torch.cuda.synchronize()
-    return q.cpu().numpy(), s.cpu().numpy()
+    return q.cpu().numpy(), s.cpu().numpy().T
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
@@ -89,11 +90,11 @@ def test_expert_up_down_fp8(T, d, E, k, d_ff):
     ws = torch.empty(moe.moe_workspace_size(c), dtype=torch.uint8, device="cuda")
     # GPU: quantize rows and weights, then the two FP8 stages
     xq = torch.empty((T, d), dtype=torch.uint8, device="cuda")
-    xs = torch.empty((T, d // 128), dtype=torch.float32, device="cuda")
+    xs = torch.empty((d // 128, T), dtype=torch.float32, device="cuda")
     moe.moe_quantize_fp8_rows(inp["hidden"], xq, xs)
     fp8 = moe.quantize_fp8_weights(inp)
     hq = torch.zeros((T * k, d_ff), dtype=torch.uint8, device="cuda")
-    hs = torch.zeros((T * k, d_ff // 128), dtype=torch.float32, device="cuda")
+    hs = torch.zeros((d_ff // 128, T * k), dtype=torch.float32, device="cuda")
     y = torch.zeros((T * k, d), dtype=torch.bfloat16, device="cuda")
     st, off = _dev(perm["sorted_token_ids"]), _dev(perm["offsets"])
     moe.moe_expert_up_fp8(c, xq, xs, st, off, fp8["w13q"], fp8["w13s"], hq, hs, ws)
@@ -102,11 +103,11 @@ def test_expert_up_down_fp8(T, d, E, k, d_ff):
     # oracle from the bf16 masters
     x_f = inp["hidden"].float().cpu().numpy()
     rxq, rxs = O.quantize_rows(x_f)
-    assert np.array_equal(rxq, xq.cpu().numpy()) and np.array_equal(rxs, xs.cpu().numpy())
+    assert np.array_equal(rxq, xq.cpu().numpy()) and np.array_equal(rxs.T, xs.cpu().numpy())
     q13 = [O.quantize_blocks(to_host_bits(inp["w13"][e])) for e in range(E)]
     q2 = [O.quantize_blocks(to_host_bits(inp["w2"][e])) for e in range(E)]
     expert_of_row = np.repeat(np.arange(E), perm["counts"])
-    g_hq, g_hs = hq.cpu().numpy(), hs.cpu().numpy()
+    g_hq, g_hs = hq.cpu().numpy(), hs.cpu().numpy().T   # scales back to [rows, d_ff/128]
     flips, scale_moves, ref_y = 0, 0, []
     for r, (t, e) in enumerate(zip(perm["sorted_token_ids"], expert_of_row)):
         rhq, rhs = O.expert_up_fp8(rxq[t], rxs[t], *q13[e])

@@ -89,11 +89,11 @@ def test_expert_up_down_mxfp4(T, d, E, k, d_ff):
     c = H.cfg_of(lc)
     ws = torch.empty(moe.moe_workspace_size(c), dtype=torch.uint8, device="cuda")
     xq = torch.empty((T, d), dtype=torch.uint8, device="cuda")
-    xs = torch.empty((T, d // 128), dtype=torch.float32, device="cuda")
+    xs = torch.empty((d // 128, T), dtype=torch.float32, device="cuda")
     moe.moe_quantize_fp8_rows(inp["hidden"], xq, xs)
     mx = moe.quantize_mxfp4_weights(inp)
     hq = torch.zeros((T * k, d_ff), dtype=torch.uint8, device="cuda")
-    hs = torch.zeros((T * k, d_ff // 128), dtype=torch.float32, device="cuda")
+    hs = torch.zeros((d_ff // 128, T * k), dtype=torch.float32, device="cuda")
     y = torch.zeros((T * k, d), dtype=torch.bfloat16, device="cuda")
     st, off = _dev(perm["sorted_token_ids"]), _dev(perm["offsets"])
     moe.moe_expert_up_mxfp4(c, xq, xs, st, off, mx["w13q"], mx["w13s"], hq, hs, ws)
@@ -101,6 +101,7 @@ def test_expert_up_down_mxfp4(T, d, E, k, d_ff):
     torch.cuda.synchronize()
     x_f = inp["hidden"].float().cpu().numpy()
     rxq, rxs = O.quantize_rows(x_f)
+    assert np.array_equal(rxq, xq.cpu().numpy()) and np.array_equal(rxs.T, xs.cpu().numpy())
     q13 = [O.quantize_mxfp4(to_host_bits(inp["w13"][e])) for e in range(E)]
     q2 = [O.quantize_mxfp4(to_host_bits(inp["w2"][e])) for e in range(E)]
     for e in range(E):   # the GPU's weight codes and scales are the oracle's
@@ -109,7 +110,7 @@ def test_expert_up_down_mxfp4(T, d, E, k, d_ff):
         assert np.array_equal(mx["w2q"][e].cpu().numpy(), q2[e][0])
         assert np.array_equal(mx["w2s"][e].cpu().numpy(), kmajor(q2[e][1]))
     expert_of_row = np.repeat(np.arange(E), perm["counts"])
-    g_hq, g_hs = hq.cpu().numpy(), hs.cpu().numpy()
+    g_hq, g_hs = hq.cpu().numpy(), hs.cpu().numpy().T   # scales back to [rows, d_ff/128]
     flips, scale_moves, ref_y = 0, 0, []
     for r, (t, e) in enumerate(zip(perm["sorted_token_ids"], expert_of_row)):
         rhq, rhs = O.expert_up_mxfp4(rxq[t], rxs[t], *q13[e])
