@@ -161,3 +161,15 @@ def test_mxfp4_entry_points_check_on_host():
     assert L.moe_forward_mxfp4(C.byref(c), *missing, 1 << 40, z) == -1
     assert L.moe_expert_up_mxfp4(C.byref(c), *([bogus] * 8), z, 1 << 40, z) == -1
     assert L.moe_expert_down_mxfp4(C.byref(c), *([bogus] * 6), bogus, 16, z) == -3
+
+
+@pytest.mark.parametrize("fn", ["moe_forward_fp8", "moe_forward_mxfp4"])
+def test_low_precision_forward_empty_batch(fn):
+    """T == 0 returns before any launch (the pointers are never dereferenced)."""
+    L = moe.load_library()
+    bogus = C.c_void_p(0x1000)
+    c = cfg(T=0, d=256, d_ff=256, dtype="bf16")
+    args = [bogus] * 2 + [None] * 4 + [bogus] * 4 + [None] * 4 + [bogus] + [None] * 2 + [bogus]
+    assert getattr(L, fn)(C.byref(c), *args, 1 << 40, None) == 0
+    assert L.moe_expert_up_fp8(C.byref(c), *([bogus] * 8), bogus, 1 << 40, None) == 0
+    assert L.moe_expert_down_mxfp4(C.byref(c), *([bogus] * 6), bogus, 1 << 40, None) == 0

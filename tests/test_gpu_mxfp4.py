@@ -136,6 +136,7 @@ MX_LAYERS = {
     "v4flash_decode_small": CONFIGS["v4flash_decode"].with_(d=512, d_ff=256),
     "v4pro_skew_small": CONFIGS["v4pro_skew_prefill"].with_(T=2048, d=256, E=16, k=4, d_ff=256),
     "decode_T1": CONFIGS["v4flash_decode"].with_(T=1, d=256, d_ff=128),
+    "single_expert": CONFIGS["mixtral_prefill"].with_(T=100, d=256, E=1, k=1, d_ff=128),
 }
 
 
