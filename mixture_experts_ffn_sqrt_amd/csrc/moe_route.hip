@@ -21,7 +21,7 @@
 namespace moe {
 namespace {
 
-constexpr int kMaxPerLane = 16;  // E <= 1024
+constexpr int kMaxPerLane = 16;  // E <= 1024: experts e = lane + 64 i, i < 16
 constexpr int kWavesPerBlock = 4;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -102,6 +102,9 @@ __device__ __forceinline__ void write_gates(const TopkArgs& p, const float* l, i
   }
 }
 
+// NS = experts per lane (E <= 64 NS), so that the selection rounds touch only
+// the slots that hold experts
+template <int NS>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void topk_kernel(TopkArgs p) {
   __shared__ float skey[kWavesPerBlock][1024];
   __shared__ float slog[kWavesPerBlock][1024];
@@ -160,10 +163,10 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void topk_kernel(TopkArgs p) {
     return;
   }
 
-  float key[kMaxPerLane];
-  bool ok[kMaxPerLane];
+  float key[NS];
+  bool ok[NS];
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < NS; ++i) {
     const int e = lane + 64 * i;
     ok[i] = e < p.E;
     key[i] = 0.0f;
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void topk_kernel(TopkArgs p) {
     const int G = p.E / p.n_group;
     float* kw = skey[wave];
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i)
+    for (int i = 0; i < NS; ++i)
       if (ok[i]) kw[lane + 64 * i] = key[i];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void topk_kernel(TopkArgs p) {
       if (lane == g) gk = 0;
     }
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i)
+    for (int i = 0; i < NS; ++i)
       if (ok[i]) ok[i] = (keep >> ((lane + 64 * i) / G)) & 1ull;
   }
 
@@ -220,7 +223,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void topk_kernel(TopkArgs p) {
   for (int r = 0; r < p.k; ++r) {
     uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i)
+    for (int i = 0; i < NS; ++i)
       if (ok[i]) {
         const uint64_t pk = pack_key(key[i], lane + 64 * i);
         best = pk > best ? pk : best;
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void topk_kernel(TopkArgs p) {
     if (lane == r) my_e = e;
     if ((e & 63) == lane) {
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i)
+      for (int i = 0; i < NS; ++i)
         if (i == (e >> 6)) ok[i] = false;
     }
   }
@@ -246,8 +249,18 @@ hipError_t launch_topk(const moe_config& c, const float* logits, const float* pa
   TopkArgs p{logits, parts, nparts, router_part_ld(c), logit_offset, logits_out, bias, token_ids, tid2eid, ids,
              weights, c.T, c.E, c.k, c.scoring, c.route_mode, c.n_group, c.topk_group,
              c.group_topk, c.vocab};
-  hipLaunchKernelGGL(topk_kernel, dim3(ceil_div(c.T, kWavesPerBlock)), dim3(64 * kWavesPerBlock),
-                     0, s, p);
+  const dim3 grid(ceil_div(c.T, kWavesPerBlock)), block(64 * kWavesPerBlock);
+  static_assert(kMaxPerLane == 16, "slot counts below");
+  if (c.E <= 64)
+    hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, p);
+  else if (c.E <= 128)
+    hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, p);
+  else if (c.E <= 256)
+    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, p);
+  else if (c.E <= 512)
+    hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, p);
   return hipGetLastError();
 }
 
