@@ -3,23 +3,26 @@
 // "DeepSeek-V4 MoE" 四, y_A = 0.7 E1(x_A) + 0.3 E5(x_A)):
 //   out[t] = sum_j w[t,j] * Y[dispatch[t,j]]  (+ shared[t])
 // Each token gathers its k dispatch rows in slot order and sums in float32, so
-// the result does not depend on scheduling (no atomics).  One block per token,
-// 16 bytes per thread per step, coalesced along the row.
+// the result does not depend on scheduling (no atomics).  A block covers one
+// token and a chunk of kThreads * 16 bytes of its row (so that a small batch
+// still spreads over the chip); each thread issues all of its row loads before
+// it sums them.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 128;
 constexpr int kMaxK = 16;
 
+// 16 bytes of TE: raw load, and its float lanes
 template <typename TE>
-struct Vec;  // 16 bytes of TE <-> float lanes
+struct Vec;
 template <>
 struct Vec<uint16_t> {
   static constexpr int N = 8;
-  __device__ static void load(const void* p, float* x) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
+  __device__ static uint4 load(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ static void unpack(const uint4& v, float* x) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -39,9 +42,10 @@ struct Vec<uint16_t> {
 template <>
 struct Vec<float> {
   static constexpr int N = 4;
-  __device__ static void load(const void* p, float* x) {
-    const float4 v = *reinterpret_cast<const float4*>(p);
-    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  __device__ static uint4 load(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ static void unpack(const uint4& v, float* x) {
+    x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
   }
   __device__ static void store(void* p, const float* x) {
     *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
@@ -54,6 +58,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const TE* Y, const in
                                                            TE* out, int k, int d) {
   constexpr int V = Vec<TE>::N;
   const int t = blockIdx.x;
+  const int c = (blockIdx.y * kThreads + threadIdx.x) * V;
+  if (c >= d) return;
   int rows[kMaxK];
   float wt[kMaxK];
 #pragma unroll
@@ -61,26 +67,29 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const TE* Y, const in
     rows[j] = j < k ? dispatch[static_cast<int64_t>(t) * k + j] : -1;
     wt[j] = j < k ? w[static_cast<int64_t>(t) * k + j] : 0.0f;
   }
-  for (int c = threadIdx.x * V; c < d; c += kThreads * V) {
-    float acc[V];
+  uint4 raw[kMaxK + 1];
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = 0.0f;
+  for (int j = 0; j < kMaxK; ++j)
+    if (rows[j] >= 0) raw[j] = Vec<TE>::load(Y + static_cast<int64_t>(rows[j]) * d + c);
+  if (shared) raw[kMaxK] = Vec<TE>::load(shared + static_cast<int64_t>(t) * d + c);
+  float acc[V];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (rows[j] < 0) continue;
-      float x[V];
-      Vec<TE>::load(Y + static_cast<int64_t>(rows[j]) * d + c, x);
+  for (int i = 0; i < V; ++i) acc[i] = 0.0f;
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] += wt[j] * x[i];
-    }
-    if (shared) {
-      float x[V];
-      Vec<TE>::load(shared + static_cast<int64_t>(t) * d + c, x);
+  for (int j = 0; j < kMaxK; ++j) {
+    if (rows[j] < 0) continue;
+    float x[V];
+    Vec<TE>::unpack(raw[j], x);
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] += x[i];
-    }
-    Vec<TE>::store(out + static_cast<int64_t>(t) * d + c, acc);
+    for (int i = 0; i < V; ++i) acc[i] += wt[j] * x[i];
   }
+  if (shared) {
+    float x[V];
+    Vec<TE>::unpack(raw[kMaxK], x);
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] += x[i];
+  }
+  Vec<TE>::store(out + static_cast<int64_t>(t) * d + c, acc);
 }
 
 }  // namespace
@@ -89,11 +98,11 @@ hipError_t launch_combine(const moe_config& c, const void* expert_out, const int
                           const float* weights, const void* shared_out, void* out,
                           hipStream_t s) {
   if (c.dtype == MOE_F32) {
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(c.T), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(c.T, ceil_div(c.d, kThreads * 4)), dim3(kThreads), 0, s,
                        static_cast<const float*>(expert_out), dispatch, weights,
                        static_cast<const float*>(shared_out), static_cast<float*>(out), c.k, c.d);
   } else {
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(c.T), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(c.T, ceil_div(c.d, kThreads * 8)), dim3(kThreads), 0, s,
                        static_cast<const uint16_t*>(expert_out), dispatch, weights,
                        static_cast<const uint16_t*>(shared_out), static_cast<uint16_t*>(out),
                        c.k, c.d);
