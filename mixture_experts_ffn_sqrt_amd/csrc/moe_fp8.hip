@@ -36,25 +36,62 @@ __device__ __forceinline__ float wave_max64(float v) {
   return v;
 }
 
-// One wavefront per (row, 128-column group): two elements per lane.  Scales
-// are stored K-block-major, [K/128, n], so that one group's scales of
-// consecutive rows are contiguous for the GEMMs' loads.
+// 8 consecutive elements of a row as floats (16-byte loads)
+template <typename TIn>
+__device__ __forceinline__ void load8(const TIn* p, float* v);
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* v) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float* v) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+// One wavefront per 512 consecutive elements of a row (four 128-column groups,
+// fewer at a row's end): lane l holds elements 8l .. 8l+7, so group l/16 is
+// reduced over 16 lanes.  Scales are stored K-block-major, [K/128, n], so that
+// one group's scales of consecutive rows are contiguous for the GEMMs' loads.
 template <typename TIn>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(int n, int K, const TIn* x,
                                                             uint8_t* q, float* scales) {
-  const int G = K / 128;
+  const int JR = (K + 511) / 512;  // jobs per row
   const int64_t job = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (job >= (int64_t)n * G) return;
+  if (job >= (int64_t)n * JR) return;
   const int lane = threadIdx.x & 63;
-  const int64_t row = job / G;
-  const int g = (int)(job - row * G);
-  const int64_t base = row * K + g * 128 + 2 * lane;
-  const float v0 = load_in(x, base), v1 = load_in(x, base + 1);
-  const int e = fp8_scale_exp(wave_max64(fmaxf(fabsf(v0), fabsf(v1))));
+  const int64_t row = job / JR;
+  const int col = (int)(job - row * JR) * 512 + 8 * lane;
+  const bool in = col < K;  // K is a multiple of 128: whole groups are in or out
+  float v[8];
+  if (in) {
+    load8(x + row * K + col, v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+  if (!in) return;
+  const int e = fp8_scale_exp(m);
   const float inv = ldexpf(1.0f, -e);
-  const uint32_t c0 = e4m3_code(v0 * inv), c1 = e4m3_code(v1 * inv);
-  *reinterpret_cast<uint16_t*>(q + base) = (uint16_t)(c0 | (c1 << 8));
-  if (lane == 0) scales[(int64_t)g * n + row] = ldexpf(1.0f, e);
+  uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w0 |= e4m3_code(v[i] * inv) << (8 * i);
+    w1 |= e4m3_code(v[4 + i] * inv) << (8 * i);
+  }
+  *reinterpret_cast<uint2*>(q + row * K + col) = make_uint2(w0, w1);
+  if ((lane & 15) == 0) scales[(int64_t)(col / 128) * n + row] = ldexpf(1.0f, e);
 }
 
 // E2M1 code of v, nearest with ties to the even mantissa, saturated to +-6: the
@@ -168,7 +205,7 @@ bool small_rows(const Fp8FfnArgs& a) {
 
 hipError_t launch_quantize_rows(int n, int K, int in_dtype, const void* x, uint8_t* q,
                                 float* scales, hipStream_t s) {
-  const int64_t jobs = (int64_t)n * (K / 128);
+  const int64_t jobs = (int64_t)n * ((K + 511) / 512);
   if (jobs == 0) return hipSuccess;
   const dim3 grid((unsigned)((jobs + 3) / 4));
   if (in_dtype == MOE_F32)

@@ -48,7 +48,8 @@ __host__ __device__ constexpr int group_tiles(int M, int bm) {
 }
 
 // pairs handled by one histogram / scatter block of the permutation
-constexpr int kPermuteChunk = 2048;
+constexpr int kPermuteChunk = 256;   // pairs per histogram / scatter chunk
+constexpr int kPermuteSmall = 2048;  // up to this many pairs: one single-block kernel
 
 // ---------------------------------------------------------------------------
 // workspace carve-up (byte offsets from the workspace base), shared by the

@@ -7,7 +7,7 @@
 //      starting row per expert
 //   3. per chunk, one wavefront walks its pairs in order 64 at a time; lanes with
 //      the same expert are ranked by ballot + popcount, which keeps the order
-// When all pairs fit one chunk (decode-sized batches) the three steps run as one
+// Up to kPermuteSmall pairs (decode-sized batches) the three steps run as one
 // single-block kernel with the same results.  A fourth small kernel turns the
 // offsets into the grouped GEMMs' row ranges and row-tile prefixes (routed
 // experts, then the shared expert as one more group).
@@ -106,14 +106,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* blockcnt, i
   __shared__ int wave_tot[kScanThreads / 64];
   const int e = threadIdx.x;
   int total = 0;
-  if (e < E)
+  if (e < E) {
+#pragma unroll 8
     for (int b = 0; b < nblk; ++b) total += blockcnt[static_cast<int64_t>(b) * E + e];
+  }
   const int off = block_exclusive_scan(e < E ? total : 0, wave_tot);
   if (e < E) {
     counts[e] = total;
     offsets[e] = off;
     if (e == E - 1) offsets[E] = off + total;
     int run = off;
+#pragma unroll 8
     for (int b = 0; b < nblk; ++b) {
       int32_t* c = blockcnt + static_cast<int64_t>(b) * E + e;
       const int n = *c;
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* ids, const f
   }
 }
 
-// All three steps for R <= kPermuteChunk pairs in one block: LDS histogram,
+// All three steps for R <= kPermuteSmall pairs in one block: LDS histogram,
 // scan, then wavefront 0 walks the pairs in order exactly as scatter_kernel
 __global__ __launch_bounds__(kScanThreads) void permute_small_kernel(
     const int32_t* ids, const float* w, int R, int k, int E, int32_t* counts, int32_t* offsets,
@@ -287,7 +290,7 @@ hipError_t launch_permute(const moe_config& c, const int32_t* ids, const float* 
                           hipStream_t s) {
   const int R = c.T * c.k;
   const int nblk = ceil_div(R, kPermuteChunk);
-  if (nblk == 1) {
+  if (R <= kPermuteSmall) {
     hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kScanThreads), 0, s, ids, weights, R,
                        c.k, c.E, counts, offsets, sorted_tok, sorted_w, dispatch);
     return hipGetLastError();
