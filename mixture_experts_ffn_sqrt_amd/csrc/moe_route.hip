@@ -57,6 +57,24 @@ __device__ __forceinline__ uint64_t pack_key(float key, int idx) {
   return (static_cast<uint64_t>(order_bits(key)) << 32) | static_cast<uint32_t>(~idx);
 }
 
+// the float whose order_bits are b (-0 comes back as +0)
+__device__ __forceinline__ float from_order_bits(uint32_t b) {
+  return __uint_as_float((b & 0x80000000u) ? (b & 0x7FFFFFFFu) : ~b);
+}
+
+// maximum over each aligned segment of `width` lanes (a power of two <= 64)
+__device__ __forceinline__ uint64_t segment_max_u64(uint64_t v, int width) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    if (off >= width) continue;  // uniform
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off);
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off);
+    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -106,8 +124,9 @@ __device__ __forceinline__ void write_gates(const TopkArgs& p, const float* l, i
 // the slots that hold experts
 template <int NS>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void topk_kernel(TopkArgs p) {
-  __shared__ float skey[kWavesPerBlock][1024];
-  __shared__ float slog[kWavesPerBlock][1024];
+  // per wavefront: the token's logits and (group stage) its keys, E <= 64 NS
+  __shared__ float skey[kWavesPerBlock][64 * NS];
+  __shared__ float slog[kWavesPerBlock][64 * NS];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * kWavesPerBlock + wave;
   if (t >= p.T) return;  // whole wavefronts only; no block barrier below
@@ -179,33 +198,56 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void topk_kernel(TopkArgs p) {
   if (p.n_group > 1) {
     const int G = p.E / p.n_group;
     float* kw = skey[wave];
-#pragma unroll
-    for (int i = 0; i < NS; ++i)
-      if (ok[i]) kw[lane + 64 * i] = key[i];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // lane g scores group g: sum of its group_topk largest keys, largest first
     uint64_t gk = 0;
-    if (lane < p.n_group) {
-      const float* gkey = kw + lane * G;
-      // round r takes the best member that comes after round r-1's pick in the
-      // (key descending, index ascending) order, i.e. selection without removal
-      float acc = 0.0f, pv = 0.0f;
-      int pi = -1;
-      for (int r = 0; r < p.group_topk; ++r) {
-        int b = -1;
-        float bv = 0.0f;
-        for (int i = 0; i < G; ++i) {
-          const float v = gkey[i];
-          const bool after = r == 0 || v < pv || (v == pv && i > pi);
-          if (after && (b < 0 || v > bv)) { b = i; bv = v; }
+    if ((G & (G - 1)) == 0 && G <= 64) {
+      // a group is G consecutive lanes of one slot: its score is the sum of the
+      // group_topk largest keys, largest first, taken by segment maxima over
+      // the packed (key, index) words; ties go to the lower index, as below
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        if (64 * i >= p.E) continue;  // uniform
+        uint64_t cur = ok[i] ? pack_key(key[i], lane + 64 * i) : 0;
+        float acc = 0.0f;
+        for (int r = 0; r < p.group_topk; ++r) {
+          const uint64_t m = segment_max_u64(cur, G);
+          const float v = from_order_bits(static_cast<uint32_t>(m >> 32));
+          acc = (r == 0) ? v : acc + v;
+          if (cur == m) cur = 0;
         }
-        pv = bv;
-        pi = b;
-        acc = (r == 0) ? bv : acc + bv;
+        if ((lane & (G - 1)) == 0) kw[(64 * i + lane) / G] = acc;
       }
-      gk = pack_key(acc, lane);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (lane < p.n_group) gk = pack_key(kw[lane], lane);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+        if (ok[i]) kw[lane + 64 * i] = key[i];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // lane g scores group g: sum of its group_topk largest keys, largest first
+      if (lane < p.n_group) {
+        const float* gkey = kw + lane * G;
+        // round r takes the best member that comes after round r-1's pick in the
+        // (key descending, index ascending) order, i.e. selection without removal
+        float acc = 0.0f, pv = 0.0f;
+        int pi = -1;
+        for (int r = 0; r < p.group_topk; ++r) {
+          int b = -1;
+          float bv = 0.0f;
+          for (int i = 0; i < G; ++i) {
+            const float v = gkey[i];
+            const bool after = r == 0 || v < pv || (v == pv && i > pi);
+            if (after && (b < 0 || v > bv)) { b = i; bv = v; }
+          }
+          pv = bv;
+          pi = b;
+          acc = (r == 0) ? bv : acc + bv;
+        }
+        gk = pack_key(acc, lane);
+      }
     }
     uint64_t keep = 0;  // bit g set: group g stays eligible
     for (int r = 0; r < p.topk_group; ++r) {

@@ -85,6 +85,15 @@ ROUTE_CASES = [
     dict(T=64, E=3, k=3, scoring=O.SOFTMAX),
     dict(T=64, E=257, k=1, scoring=O.SIGMOID),
     dict(T=100, E=16, k=4, scoring=O.SOFTMAX, quantised=True),  # many exact ties
+    # group sizes: 64 and 1 (lane segments), 24 and 96 (the serial group scan),
+    # and exact ties inside groups
+    dict(T=300, E=256, k=8, scoring=O.SIGMOID, bias=True, n_group=4, topk_group=2, group_topk=3),
+    dict(T=100, E=16, k=4, scoring=O.SIGMOID, bias=True, n_group=16, topk_group=6, group_topk=1),
+    dict(T=300, E=96, k=6, scoring=O.SIGMOID, bias=True, n_group=4, topk_group=2, group_topk=2),
+    dict(T=300, E=384, k=6, scoring=O.SQRTSOFTPLUS, bias=True, n_group=4, topk_group=3,
+         group_topk=4),
+    dict(T=200, E=64, k=6, scoring=O.SIGMOID, n_group=8, topk_group=3, group_topk=2,
+         quantised=True),
 ]
 
 
