@@ -378,6 +378,10 @@ BATCH_INVARIANT = {
                                                         n_group=4, topk_group=2, group_topk=2),
     "v4pro_skew": CONFIGS["v4pro_skew_prefill"].with_(T=2048, d=512, E=16, k=4, d_ff=256),
     "tiny_fp32": CONFIGS["tiny_fp32"].with_(T=64),
+    # the full batch's router GEMM runs 128x128 tiles (T >= 1024, E >= 128), the
+    # slices' 64x64 tiles
+    "dsv3_router_tiles": CONFIGS["dsv3_prefill"].with_(T=1024, d=256, E=128, k=8, d_ff=128,
+                                                       n_group=8, topk_group=4, group_topk=2),
 }
 
 
