@@ -339,7 +339,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
 #pragma unroll
         for (int f = 0; f < HF; ++f) {
           const float g = acc[i][f][r], u = acc[i][f + HF][r];
-          h[i][f][r] = g / (1.0f + expf(-g)) * u;
+          h[i][f][r] = silu_mul(g, u);
           m = fmaxf(m, fabsf(h[i][f][r]));
         }
 #pragma unroll

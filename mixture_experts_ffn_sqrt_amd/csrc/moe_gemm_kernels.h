@@ -7,6 +7,15 @@
 namespace moe {
 namespace gemm {
 
+// SiLU(g) * u = g * u / (1 + exp(-g)) with the hardware exp2 and reciprocal
+// (each within about 1 ulp of float32; the result is rounded to bf16 or E4M3
+// afterwards).  exp(-g) overflows to infinity for g below about -88, and the
+// product is then -0, as the exact value rounds.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);  // exp(-g) = 2^(-g log2 e)
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte chunk
@@ -303,7 +312,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_staged(GemmArgs p) 
 #pragma unroll
         for (int f = 0; f < FN / 2; ++f) {
           const float g = acc[i][f][r], u = acc[i][f + FN / 2][r];
-          const float h = g / (1.0f + expf(-g)) * u;
+          const float h = silu_mul(g, u);
           const int col = nt * (BN / 2) + wn * (WTN / 2) + 16 * f + ccol;
           store_elem<TE>(crow_ptr + (int64_t)col * sizeof(TE), h);
         }
@@ -531,7 +540,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
 #pragma unroll
         for (int f = 0; f < FN / 2; ++f) {
           const float g = acc[i][f][r], u = acc[i][f + FN / 2][r];
-          const float h = g / (1.0f + expf(-g)) * u;
+          const float h = silu_mul(g, u);
           const int col = tc.nt * (BN / 2) + wn * (WTN / 2) + 32 * f + ccol;
           *reinterpret_cast<uint16_t*>(crow_ptr + (int64_t)col * 2) = f32_to_bf16(h);
         }
