@@ -174,9 +174,7 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(int R, int C, cons
 template <int BM, int BN, int WM, int WN, int EPI, int ST, int WF = WF_E4M3>
 hipError_t launch_fp8(const Fp8Args& q, int m_tiles_bound, hipStream_t s) {
   constexpr int NT = 64 * WM * WN;
-  constexpr bool MX = WF == WF_MXFP4;
-  constexpr int LDS = ST * (BM * 128 + BN * (MX ? 64 : 128) + (BM > 64 ? BM : 64) * 4 +
-                            (MX ? BN * 4 : 256));
+  constexpr int LDS = ST * fp8_stage_bytes<BM, BN, WF>();
   const int grid = m_tiles_bound * q.g.n_tiles;
   if (grid <= 0) return hipSuccess;
   auto kern = grouped_gemm_fp8<BM, BN, WM, WN, EPI, ST, WF>;
@@ -193,7 +191,8 @@ int tile_bound8(int64_t rows, int groups, int bm) {
 }
 
 // 32-row streaming tiles when experts have a few rows each (decode), else
-// 256x256 tiles (the same rule as the bf16 experts).  The decode tiles keep
+// 256x256 tiles (288x256 for the down GEMM of large groups; the same rules as
+// the bf16 experts).  The decode tiles keep
 // short LDS rings (2-3 stages, 40-80 KB) so that two to four blocks share a CU
 // and one block's pipeline fill and epilogue overlap another's streaming:
 // measured faster than one block per CU with a 4-12 stage ring.
@@ -324,6 +323,12 @@ hipError_t launch_expert_down_fp8(const moe_config& c, const Fp8FfnArgs& a, hipS
               : launch_fp8<32, 128, 1, 4, EPI_STORE, 3>(q, mt, s);
   }
   g.n_tiles = ceil_div(c.d, 256);
+  if (tall_down_tiles(a.rows_bound, a.n_groups)) {
+    g.tile_prefix = a.tile_prefix + tile_height_index(288) * (a.n_groups + 1);
+    const int mt = tile_bound8(a.rows_bound, a.n_groups, 288);
+    return mx ? launch_fp8<288, 256, 3, 4, EPI_STORE, 2, WF_MXFP4>(q, mt, s)
+              : launch_fp8<288, 256, 3, 4, EPI_STORE, 2>(q, mt, s);
+  }
   g.tile_prefix = a.tile_prefix + tile_height_index(256) * (a.n_groups + 1);
   const int mt = tile_bound8(a.rows_bound, a.n_groups, 256);
   return mx ? launch_fp8<256, 256, 4, 4, EPI_STORE, 3, WF_MXFP4>(q, mt, s)

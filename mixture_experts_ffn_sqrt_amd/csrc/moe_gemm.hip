@@ -119,14 +119,15 @@ namespace {
 
 // Tile shape of the grouped expert GEMMs.  Rows per group on average (known on
 // the host from T, k and the group count) picks 32-row tiles for
-// decode-shaped batches and 256x256 tiles for prefill-shaped ones, both on the
+// decode-shaped batches and 256x256 tiles for prefill-shaped ones (288x256
+// for the down GEMM of large groups, see tall_down_tiles), all on the
 // direct-to-LDS kernel when the shapes allow it (d_ff a multiple of 128 and
 // operands addressable with 31-bit offsets), else 16- or 128-row tiles on the
-// register-staged kernel.  The two direct-to-LDS shapes accumulate K in the
-// same order (64-element slabs, 16-element MFMA steps, one fp32 accumulator
-// per output), so a row's result does not depend on which of them runs: with
-// the router's T-independent split, the layer output of a token does not
-// depend on the batch it is in.
+// register-staged kernel.  The direct-to-LDS shapes accumulate K in the same
+// order (64-element slabs, 16-element MFMA steps, one fp32 accumulator per
+// output), so a row's result does not depend on which of them runs: with the
+// router's T-independent split, the layer output of a token does not depend on
+// the batch it is in.
 enum class FfnTiles { F32_16, BF16_16, BF16_32, BF16_128, BF16_256 };
 
 FfnTiles pick_tiles(const moe_config& c, const ExpertFfnArgs& a) {
@@ -234,6 +235,11 @@ hipError_t launch_expert_down(const moe_config& c, const ExpertFfnArgs& a, hipSt
       g.n_tiles = ceil_div(c.d, 256);
       g.a_bytes = (uint32_t)((int64_t)a.rows_bound * F * es);
       g.b_bytes = (uint32_t)(d * F * es);
+      if (tall_down_tiles(a.rows_bound, a.n_groups)) {
+        g.tile_prefix = a.tile_prefix + tile_height_index(288) * (a.n_groups + 1);
+        return launch_gemm_dma<288, 256, 3, 4, EPI_STORE, 2, 128, 3>(
+            g, tile_bound(a.rows_bound, a.n_groups, 288), s);
+      }
       return launch_gemm_dma<256, 256, 4, 4, EPI_STORE, 2, 128, 3>(g, mb, s);
     default:
       g.n_tiles = ceil_div(c.d, 128);

@@ -95,6 +95,15 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
 // blocks; MXFP4: one dword of four E8M0 bytes per B row).  Everything a stage
 // needs arrives through the same direct-to-LDS loads, issued STAGES-1 stages
 // ahead.
+// LDS bytes of one pipeline stage of grouped_gemm_fp8: A rows (128 bytes), B
+// rows (128 bytes E4M3, 64 MXFP4), A-row scales in whole 64-row loads, weight
+// scales (E4M3: one 256-byte load; MXFP4: a dword per B row).
+template <int BM, int BN, int WF>
+__host__ __device__ constexpr int fp8_stage_bytes() {
+  return BM * 128 + BN * (WF == WF_MXFP4 ? 64 : 128) + (BM + 63) / 64 * 256 +
+         (WF == WF_MXFP4 ? BN * 4 : 256);
+}
+
 template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int WF = WF_E4M3>
 __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
   const GemmArgs& p = q.g;
@@ -108,16 +117,21 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
   constexpr int RPL = 1024 / ROWB;           // A rows filled by one wavefront load
   constexpr int RPLB = 1024 / BROWB;         // B rows filled by one wavefront load
   constexpr int BCH = BROWB / 16;            // 16-byte chunks per B row
-  constexpr int SAB = (BM > 64 ? BM : 64) * 4;  // A-row scale bytes per stage
+  constexpr int NSA = (BM + 63) / 64;        // A-row scale loads per stage (one per wave < NSA)
+  constexpr int SAB = NSA * 256;             // A-row scale bytes per stage
   constexpr int NSBL = MX ? BN / 64 : 1;     // weight-scale wavefront loads per stage
   constexpr int SBB = 256 * NSBL;            // weight-scale bytes per stage
   constexpr int OFF_B = BM * ROWB, OFF_SA = OFF_B + BN * BROWB, OFF_SB = OFF_SA + SAB;
   constexpr int STAGE = OFF_SB + SBB;
+  static_assert(STAGE == fp8_stage_bytes<BM, BN, WF>(), "stage layout");
   constexpr int NSB = BN / 128;              // E4M3: weight blocks per tile (<= 2)
-  constexpr int LA = BM / RPL / NW, LB = BN / RPLB / NW;
-  constexpr int NSA = (BM + 63) / 64;        // scale loads per stage (one per wave < NSA)
+  // 1 KB operand loads per stage: NA of A rows, NB of B rows; wave w issues A
+  // blocks w + NW*j (j < LA) and B blocks w + NW*j (j < LB, block < NB)
+  constexpr int NA = BM / RPL, NB = BN / RPLB;
+  constexpr int LA = NA / NW, LB = (NB + NW - 1) / NW;
+  constexpr bool B_EVEN = NB % NW == 0;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "whole 32x32 fragments");
-  static_assert(LA * NW * RPL == BM && LB * NW * RPLB == BN, "loads must split evenly");
+  static_assert(NA * RPL == BM && NB * RPLB == BN && LA * NW == NA, "A loads must split evenly");
   static_assert(NSBL <= NW, "one weight-scale load per wave at most");
   static_assert(!SW || BN == 256, "SwiGLU8: one 128-column group of H per tile");
   static_assert(!SW || FN % 2 == 0, "SwiGLU waves hold gate and up fragments in pairs");
@@ -173,6 +187,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
     const int brow = weight_row(row);
     b_off[j] = brow >= 0 ? (uint32_t)brow * (uint32_t)p.ldb + ch * 16 : kOut;
   }
+  // the last B slot exists on waves whose block wave + NW*(LB-1) is < NB
+  const bool b_last = B_EVEN || wave + NW * (LB - 1) < NB;
   // A-row scales: wave w < NSA loads rows 64 w .. 64 w + 63 (4 bytes per lane;
   // the K-block-major layout keeps a stage's scales of ascending rows together)
   uint32_t s_off = kOut;
@@ -204,9 +220,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
     char* buf_ = smem + ((kt_) % STAGES) * STAGE;                                          \
     _Pragma("unroll") for (int j = 0; j < LA; ++j)                                          \
         load_lds16(a_rs, buf_ + (RPL * (wave + NW * j)) * ROWB, a_off[j] + kc_ * ROWB);     \
-    _Pragma("unroll") for (int j = 0; j < LB; ++j)                                          \
-        load_lds16(b_rs, buf_ + OFF_B + (RPLB * (wave + NW * j)) * BROWB,                   \
-                   b_off[j] + kc_ * BROWB);                                                \
+    _Pragma("unroll") for (int j = 0; j < LB; ++j) {                                        \
+      if (j == LB - 1 && !b_last) break;                                                   \
+      load_lds16(b_rs, buf_ + OFF_B + (RPLB * (wave + NW * j)) * BROWB,                    \
+                 b_off[j] + kc_ * BROWB);                                                  \
+    }                                                                                      \
     if (has_sa)                                                                            \
       load_lds4(s_rs, buf_ + OFF_SA + 256 * wave, s_off + (uint32_t)kc_ * q.as_kstride);   \
     if (has_sb)                                                                            \
@@ -256,16 +274,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
 
   const int live = min(FM, max(0, (tc.nrows - wm * WTM + 31) / 32));
   for (int kt = 0; kt < KB; ++kt) {
-    static_assert((STAGES - 2) * (LA + LB + 2) <= 63, "vmcnt range");
     // at most (STAGES-2) later stages' loads may still be in flight: a wave's
-    // loads per stage are its operand loads plus one for each kind of scale it
-    // loads (wave-uniform branches, so each wave waits for its own count)
-    if (has_sa && has_sb)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * (LA + LB + 2)));
-    else if (has_sa || has_sb)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * (LA + LB + 1)));
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * (LA + LB)));
+    // loads per stage are its operand loads (one fewer without the last B
+    // slot) plus one for each kind of scale it loads (wave-uniform, so each
+    // wave waits for its own count)
+    wait_loads_le<STAGES - 2, LA + LB - 1>(LA + LB - (b_last ? 0 : 1) + (has_sa ? 1 : 0) +
+                                           (has_sb ? 1 : 0));
     __builtin_amdgcn_s_waitcnt(0xC07F);
     lds_barrier();
     MOE_FP8_ISSUE(kt + STAGES - 1);

@@ -353,6 +353,20 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_staged(GemmArgs p) 
 // lgkmcnt left at their no-wait maxima)
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
+// Wait until at most MUL * n of this wave's vector-memory loads are in flight,
+// for a wave-uniform n in [N0, N0 + 3] (s_waitcnt takes an immediate; an n
+// below the range waits for MUL * N0, which is never too few).
+template <int MUL, int N0>
+__device__ __forceinline__ void wait_loads_le(int n) {
+  static_assert(N0 >= 0 && MUL * (N0 + 3) <= 63, "vmcnt range");
+  switch (n - N0) {
+    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(MUL * (N0 + 1))); break;
+    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(MUL * (N0 + 2))); break;
+    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(MUL * (N0 + 3))); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(MUL * N0)); break;
+  }
+}
+
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 // Workgroup barrier without a memory fence (so outstanding direct-to-LDS loads
@@ -399,11 +413,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
   constexpr int CPR = ROWB / 16;                    // 16-byte chunks per row
   constexpr int RPL = 1024 / ROWB;                  // rows filled by one wavefront load
   constexpr int STAGE = (BM + BN) * ROWB;
-  constexpr int LA = BM / RPL / NW, LB = BN / RPL / NW;  // 1 KB loads per wave per stage
+  // 1 KB loads per stage: NA of A rows, NB of B rows; wave w issues A blocks
+  // w + NW*j (j < LA) and B blocks w + NW*j (j < LB, block < NB)
+  constexpr int NA = BM / RPL, NB = BN / RPL;
+  constexpr int LA = NA / NW, LB = (NB + NW - 1) / NW;
+  constexpr bool B_EVEN = NB % NW == 0;
   static_assert(ROWB == 64 || ROWB == 128, "64- or 128-byte LDS rows");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "whole 32x32 fragments");
   static_assert(!SW || FN % 2 == 0, "SwiGLU waves hold gate and up fragments in pairs");
-  static_assert(LA * NW * RPL == BM && LB * NW * RPL == BN, "loads must split evenly");
+  static_assert(NA * RPL == BM && NB * RPL == BN && LA * NW == NA, "A loads must split evenly");
   static_assert(!SW || (BN / 2) % RPL == 0, "a load is all gate or all up rows");
   static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024, "LDS budget");
   extern __shared__ __align__(16) char smem[];
@@ -452,6 +470,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
     }
     b_off[j] = ok ? (uint32_t)brow * (uint32_t)p.ldb + ch * 16 : kOut;
   }
+  // the last B slot exists on waves whose block wave + NW*(LB-1) is < NB
+  const bool b_last = B_EVEN || wave + NW * (LB - 1) < NB;
   const int KT = p.K / (ROWB / 2);  // ROWB/2 bf16 per stage
   // Stage kt's loads; stages past the end reload the last one (never read;
   // keeps the number of loads in flight constant).
@@ -462,8 +482,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
     const uint32_t ko_ = (uint32_t)kc_ * ROWB;                                           \
     _Pragma("unroll") for (int j = 0; j < LA; ++j)                                        \
         load_lds16(a_rs, buf_ + (RPL * (wave + NW * j)) * ROWB, a_off[j] + ko_);         \
-    _Pragma("unroll") for (int j = 0; j < LB; ++j)                                        \
-        load_lds16(b_rs, buf_ + BM * ROWB + (RPL * (wave + NW * j)) * ROWB, b_off[j] + ko_); \
+    _Pragma("unroll") for (int j = 0; j < LB; ++j) {                                      \
+      if (j == LB - 1 && !b_last) break;                                                 \
+      load_lds16(b_rs, buf_ + BM * ROWB + (RPL * (wave + NW * j)) * ROWB, b_off[j] + ko_); \
+    }                                                                                    \
   } while (0)
 
   f32x16 acc[FM][FN];
@@ -497,8 +519,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
   for (int s = 0; s < STAGES - 1; ++s) MOE_DMA_ISSUE(s);
 #define MOE_DMA_MAIN(CHECK)                                                                   \
   for (int kt = 0; kt < KT; ++kt) {                                                          \
-    static_assert((STAGES - 2) * (LA + LB) <= 63, "vmcnt range");                            \
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * (LA + LB)));                         \
+    /* at most STAGES-2 later stages' loads in flight: LA + LB per stage, one */           \
+    /* fewer on waves without the last B slot */                                             \
+    wait_loads_le<STAGES - 2, LA + LB - 1>(LA + LB - (b_last ? 0 : 1));                      \
     __builtin_amdgcn_s_waitcnt(0xC07F);                                                      \
     lds_barrier();                                                            \
     MOE_DMA_ISSUE(kt + STAGES - 1);                                                           \

@@ -27,10 +27,12 @@ __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / 
 __host__ __device__ constexpr int64_t align_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
 // Row-tile heights for which the permutation builds tile lists.  Index i holds
-// the cumulative m-tile count per group for BM = 16 << i.
-constexpr int kNumTileHeights = 5;  // 16, 32, 64, 128, 256
+// the cumulative m-tile count per group for BM = tile_height(i).  288 = 9
+// fragments: groups of up to 1152 rows in 4 tiles, up to 288 in one.
+constexpr int kNumTileHeights = 6;  // 16, 32, 64, 128, 256, 288
+__host__ __device__ constexpr int tile_height(int i) { return i < 5 ? 16 << i : 288; }
 __host__ __device__ constexpr int tile_height_index(int bm) {
-  return bm == 16 ? 0 : bm == 32 ? 1 : bm == 64 ? 2 : bm == 128 ? 3 : 4;
+  return bm == 16 ? 0 : bm == 32 ? 1 : bm == 64 ? 2 : bm == 128 ? 3 : bm == 256 ? 4 : 5;
 }
 
 // Rows per tile of a group of M rows cut into tiles of at most BM rows: the
@@ -45,6 +47,16 @@ __host__ __device__ constexpr int group_tile_rows(int M, int bm) {
 }
 __host__ __device__ constexpr int group_tiles(int M, int bm) {
   return M <= 0 ? 0 : ceil_div(M, group_tile_rows(M, bm));
+}
+
+// Down GEMM of groups that average 512 rows or more: 288-row tiles (3 x 4
+// waves of 96 x 64).  A group of 4 x 256 rows plus the few percent that a
+// random routing adds to about half of the groups still fits 4 of them, where
+// 256-row tiles would add a fifth row of tiles to those groups and with it a
+// partly filled extra round of blocks over the 256 CUs.  (The up GEMM has many
+// rounds of tiles, so its last partial round weighs little.)
+inline bool tall_down_tiles(int64_t rows_bound, int n_groups) {
+  return n_groups > 0 && rows_bound >= (int64_t)512 * n_groups;
 }
 
 // pairs handled by one histogram / scatter block of the permutation

@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(const int32_t
   int32_t* g_begin = groups;
   int32_t* g_end = groups + G;
   // G <= 1025: thread i handles groups i and (for i == 0) the shared group E;
-  // the prefixes of all tile heights (16 << h) come from one scan per pass
+  // the prefixes of all tile heights come from one scan per pass
   int carry[H];
 #pragma unroll
   for (int h = 0; h < H; ++h) carry[h] = 0;
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(const int32_t
     }
     int tiles[H], ex[H];
 #pragma unroll
-    for (int h = 0; h < H; ++h) tiles[h] = g < G ? group_tiles(rows, 16 << h) : 0;
+    for (int h = 0; h < H; ++h) tiles[h] = g < G ? group_tiles(rows, tile_height(h)) : 0;
     block_exclusive_scan_n<H>(tiles, ex, wave_tot);
 #pragma unroll
     for (int h = 0; h < H; ++h) {

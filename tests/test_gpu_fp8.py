@@ -79,6 +79,8 @@ def _dev(a):
     (40, 256, 16, 4, 256),      # a few rows per expert: 32-row streaming tiles
     (700, 256, 4, 2, 384),      # 256x256 tiles, ragged rows per expert
     (300, 384, 3, 3, 128),      # k = E, d not a multiple of 256 (partial column tile)
+    (2100, 384, 4, 2, 128),     # ~1050 rows per expert: 288x256 down tiles, partial column tile
+    (1300, 256, 2, 1, 128),     # ~650 rows per expert: 288-row down tiles, ragged last row tile
 ])
 def test_expert_up_down_fp8(T, d, E, k, d_ff):
     lc = CONFIGS["mixtral_prefill"].with_(T=T, d=d, E=E, k=k, d_ff=d_ff, seed=31)
@@ -108,7 +110,7 @@ def test_expert_up_down_fp8(T, d, E, k, d_ff):
     q2 = [O.quantize_blocks(to_host_bits(inp["w2"][e])) for e in range(E)]
     expert_of_row = np.repeat(np.arange(E), perm["counts"])
     g_hq, g_hs = hq.cpu().numpy(), hs.cpu().numpy().T   # scales back to [rows, d_ff/128]
-    flips, scale_moves, ref_y = 0, 0, []
+    flips, scale_moves, ref_y, ref_hq, ref_hs, h_differs = 0, 0, [], [], [], []
     for r, (t, e) in enumerate(zip(perm["sorted_token_ids"], expert_of_row)):
         rhq, rhs = O.expert_up_fp8(rxq[t], rxs[t], *q13[e])
         # a scale is the power of two above a group maximum of h (float32 sums on
@@ -117,10 +119,13 @@ def test_expert_up_down_fp8(T, d, E, k, d_ff):
         ratio = g_hs[r] / rhs
         assert np.all((ratio == 1) | (ratio == 2) | (ratio == 0.5)), (r, g_hs[r], rhs)
         scale_moves += int((ratio != 1).sum())
+        ref_hq.append(rhq)
+        ref_hs.append(rhs)
         hg = O.e4m3_decode(g_hq[r]).reshape(-1, 128) * g_hs[r][:, None]
         hr = O.e4m3_decode(rhq).reshape(-1, 128) * rhs[:, None]
         diff = hg != hr
         flips += int(diff[ratio == 1].sum())
+        h_differs.append(bool(diff.any()))
         # a value differs by at most one E4M3 step of either scale (1/8 of its
         # binade), or near zero, where the float32 sums' absolute error shows,
         # by 4 subnormal steps (2^-9 of the scale): |h_gpu - h| <= 2^-7 * scale
@@ -132,7 +137,19 @@ def test_expert_up_down_fp8(T, d, E, k, d_ff):
     # only for a maximum within that distance of 448 * 2^e
     assert flips <= max(4, 1e-2 * g_hq.size), flips
     assert scale_moves <= max(1, 1e-2 * g_hs.size), scale_moves
-    err = H.row_rel_err(H.to_f64(y), np.stack(ref_y))
+    ref_y = np.stack(ref_y)
+    # end to end: rows whose H equals the oracle's (an H value one E4M3 step
+    # off, or a scale one power of two off, moves y by that step's share)
+    err = H.row_rel_err(H.to_f64(y), ref_y)
+    keep = ~np.array(h_differs)
+    assert not keep.any() or err[keep].max() <= TOL, err[keep].max()
+    # the down stage alone: run again on the oracle's H codes and scales
+    hq_o = torch.from_numpy(np.stack(ref_hq)).to("cuda")
+    hs_o = torch.from_numpy(np.ascontiguousarray(np.stack(ref_hs).T)).to("cuda")
+    y.zero_()
+    moe.moe_expert_down_fp8(c, hq_o, hs_o, off, fp8["w2q"], fp8["w2s"], y, ws)
+    torch.cuda.synchronize()
+    err = H.row_rel_err(H.to_f64(y), ref_y)
     assert err.max() <= TOL, err.max()
 
 
@@ -144,6 +161,7 @@ FP8_LAYERS = {
     "v4pro_skew_small": CONFIGS["v4pro_skew_prefill"].with_(T=2048, d=256, E=16, k=4, d_ff=256),
     "decode_T1": CONFIGS["v4flash_decode"].with_(T=1, d=256, d_ff=128),
     "single_expert": CONFIGS["mixtral_prefill"].with_(T=100, d=256, E=1, k=1, d_ff=128),
+    "mixtral_tall_tiles": CONFIGS["mixtral_prefill"].with_(T=2048, d=256, d_ff=256),
 }
 
 
@@ -225,13 +243,15 @@ def test_forward_fp8_full_size_sampled(name, n_rows):
     check_layer_fp8(lc, inp, out, layer.ids, layer.gates, rows=np.sort(rows))
 
 
-def test_forward_fp8_batch_invariant():
-    lc = FP8_LAYERS["mixtral_small"]
+@pytest.mark.parametrize("name", ["mixtral_small", "mixtral_tall_tiles"])
+def test_forward_fp8_batch_invariant(name):
+    # mixtral_tall_tiles: the full batch's down GEMM runs 288-row tiles
+    lc = FP8_LAYERS[name]
     inp = make_inputs(lc, "cuda")
     fp8 = moe.quantize_fp8_weights(inp)
     layer = moe.MoELayer(H.cfg_of(lc), inp)
     full = layer.forward_fp8(fp8).clone()
-    for a, b in [(0, 1), (7, 60), (400, 512)]:
+    for a, b in [(0, 1), (7, 60), (400, 512), (lc.T - 3, lc.T)]:
         sub = dict(inp)
         sub["hidden"] = inp["hidden"][a:b].contiguous()
         part = moe.MoELayer(H.cfg_of(lc, T=b - a), sub).forward_fp8(fp8)

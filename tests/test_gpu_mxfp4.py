@@ -79,6 +79,8 @@ def _dev(a):
     (700, 256, 4, 2, 384),      # 256x256 tiles, ragged rows per expert
     (300, 384, 3, 3, 128),      # k = E, d not a multiple of 256 (partial column tile)
     (1, 512, 8, 2, 256),        # one token
+    (2100, 384, 4, 2, 128),     # ~1050 rows per expert: 288x256 down tiles, partial column tile
+    (1300, 256, 2, 1, 128),     # ~650 rows per expert: 288-row down tiles, ragged last row tile
 ])
 def test_expert_up_down_mxfp4(T, d, E, k, d_ff):
     lc = CONFIGS["mixtral_prefill"].with_(T=T, d=d, E=E, k=k, d_ff=d_ff, seed=37)
@@ -111,21 +113,36 @@ def test_expert_up_down_mxfp4(T, d, E, k, d_ff):
         assert np.array_equal(mx["w2s"][e].cpu().numpy(), kmajor(q2[e][1]))
     expert_of_row = np.repeat(np.arange(E), perm["counts"])
     g_hq, g_hs = hq.cpu().numpy(), hs.cpu().numpy().T   # scales back to [rows, d_ff/128]
-    flips, scale_moves, ref_y = 0, 0, []
+    flips, scale_moves, ref_y, ref_hq, ref_hs, h_differs = 0, 0, [], [], [], []
     for r, (t, e) in enumerate(zip(perm["sorted_token_ids"], expert_of_row)):
         rhq, rhs = O.expert_up_mxfp4(rxq[t], rxs[t], *q13[e])
         ratio = g_hs[r] / rhs
         assert np.all((ratio == 1) | (ratio == 2) | (ratio == 0.5)), (r, g_hs[r], rhs)
         scale_moves += int((ratio != 1).sum())
+        ref_hq.append(rhq)
+        ref_hs.append(rhs)
         hg = O.e4m3_decode(g_hq[r]).reshape(-1, 128) * g_hs[r][:, None]
         hr = O.e4m3_decode(rhq).reshape(-1, 128) * rhs[:, None]
         flips += int((hg != hr)[ratio == 1].sum())
+        h_differs.append(bool((hg != hr).any()))
         smax = np.maximum(g_hs[r], rhs)[:, None]
         assert np.all(np.abs(hg - hr) <= np.abs(hr) / 8 + 4 * 2.0 ** -9 * smax), r
         ref_y.append(O.expert_ffn_mxfp4(rxq[t], rxs[t], *q13[e], *q2[e]))
     assert flips <= max(4, 1e-2 * g_hq.size), flips
     assert scale_moves <= max(1, 1e-2 * g_hs.size), scale_moves
-    err = H.row_rel_err(H.to_f64(y), np.stack(ref_y))
+    ref_y = np.stack(ref_y)
+    # end to end: rows whose H equals the oracle's (an H value one E4M3 step
+    # off, or a scale one power of two off, moves y by that step's share)
+    err = H.row_rel_err(H.to_f64(y), ref_y)
+    keep = ~np.array(h_differs)
+    assert not keep.any() or err[keep].max() <= TOL, err[keep].max()
+    # the down stage alone: run again on the oracle's H codes and scales
+    hq_o = torch.from_numpy(np.stack(ref_hq)).to("cuda")
+    hs_o = torch.from_numpy(np.ascontiguousarray(np.stack(ref_hs).T)).to("cuda")
+    y.zero_()
+    moe.moe_expert_down_mxfp4(c, hq_o, hs_o, off, mx["w2q"], mx["w2s"], y, ws)
+    torch.cuda.synchronize()
+    err = H.row_rel_err(H.to_f64(y), ref_y)
     assert err.max() <= TOL, err.max()
 
 
@@ -137,6 +154,7 @@ MX_LAYERS = {
     "v4pro_skew_small": CONFIGS["v4pro_skew_prefill"].with_(T=2048, d=256, E=16, k=4, d_ff=256),
     "decode_T1": CONFIGS["v4flash_decode"].with_(T=1, d=256, d_ff=128),
     "single_expert": CONFIGS["mixtral_prefill"].with_(T=100, d=256, E=1, k=1, d_ff=128),
+    "mixtral_tall_tiles": CONFIGS["mixtral_prefill"].with_(T=2048, d=256, d_ff=256),
 }
 
 
@@ -217,13 +235,15 @@ def test_forward_mxfp4_full_size_sampled(name, n_rows):
     check_layer_mx(lc, inp, out, layer.ids, layer.gates, rows=np.sort(rows))
 
 
-def test_forward_mxfp4_batch_invariant():
-    lc = MX_LAYERS["mixtral_small"]
+@pytest.mark.parametrize("name", ["mixtral_small", "mixtral_tall_tiles"])
+def test_forward_mxfp4_batch_invariant(name):
+    # mixtral_tall_tiles: the full batch's down GEMM runs 288-row tiles
+    lc = MX_LAYERS[name]
     inp = make_inputs(lc, "cuda")
     mx = moe.quantize_mxfp4_weights(inp)
     layer = moe.MoELayer(H.cfg_of(lc), inp)
     full = layer.forward_mxfp4(mx).clone()
-    for a, b in [(0, 1), (7, 60), (400, 512)]:
+    for a, b in [(0, 1), (7, 60), (400, 512), (lc.T - 3, lc.T)]:
         sub = dict(inp)
         sub["hidden"] = inp["hidden"][a:b].contiguous()
         part = moe.MoELayer(H.cfg_of(lc, T=b - a), sub).forward_mxfp4(mx)

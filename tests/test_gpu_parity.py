@@ -234,6 +234,8 @@ def test_permute_random(T, k, E, mode):
     ("bf16", 700, 128, 3, 3, 64),      # k = E: every expert gets every token
     ("bf16", 700, 320, 4, 2, 256),     # 256x256 tiles: ragged rows, partial last column tile
     ("bf16", 2000, 512, 8, 2, 384),    # 256x256 tiles, several row tiles per expert
+    ("bf16", 2100, 320, 4, 2, 256),    # ~1050 rows per expert: 288x256 down tiles, partial column
+    ("bf16", 1300, 256, 2, 1, 128),    # ~650 rows per expert: 288-row down tiles, ragged last tile
 ])
 def test_expert_ffn_and_combine(dtype, T, d, E, k, d_ff):
     lc = CONFIGS["tiny_fp32"].with_(T=T, d=d, E=E, k=k, d_ff=d_ff, dtype=dtype, seed=23)
@@ -300,6 +302,8 @@ SMALL_LAYERS = {
                                                                    d_ff=256),
     "single_dense_expert": CONFIGS["mixtral_prefill"].with_(T=130, d=256, E=1, k=1, d_ff=128),
     "decode_T1": CONFIGS["v4flash_decode"].with_(T=1, d=256, d_ff=128),
+    # 512 rows per expert: the down GEMM runs 288-row tiles
+    "mixtral_tall_tiles": CONFIGS["mixtral_prefill"].with_(T=2048, d=256, d_ff=256),
 }
 
 
@@ -382,6 +386,8 @@ BATCH_INVARIANT = {
     # slices' 64x64 tiles
     "dsv3_router_tiles": CONFIGS["dsv3_prefill"].with_(T=1024, d=256, E=128, k=8, d_ff=128,
                                                        n_group=8, topk_group=4, group_topk=2),
+    # the full batch's down GEMM runs 288-row tiles (512 rows per expert)
+    "mixtral_tall_tiles": CONFIGS["mixtral_prefill"].with_(T=2048, d=256, d_ff=256),
 }
 
 
