@@ -42,7 +42,6 @@ enum { WF_E4M3 = 0, WF_MXFP4 = 1 };  // weight formats
 struct Fp8Args {
   GemmArgs g;                 // operands as codes (1 byte per element); C: H codes or Y (bf16)
   const float* a_scale;       // [K/128, scale rows]: a K block's scales of all rows together
-  const int32_t* a_scale_rows;  // A row -> scale row (nullptr: same as the A row map)
   // weight scales of group 0: E4M3 weights: [N_w/128, K/128] float tile scales
   // (N_w = weight rows); MXFP4: [K/128, N_w, 4] E8M0 bytes (per 128-column
   // block of K, each row's four 32-element block scales)
@@ -196,8 +195,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
     const int row = 64 * wave + lane;
     if (wave < NSA && row < tc.nrows) {
       const int arow = p.a_rows ? p.a_rows[tc.row0 + row] : tc.row0 + row;
-      const int srow = q.a_scale_rows ? q.a_scale_rows[tc.row0 + row] : arow;
-      s_off = (uint32_t)srow * 4u;
+      s_off = (uint32_t)arow * 4u;  // scales are indexed like the A rows
     }
   }
   // weight scales, loaded by the last NSBL waves.  E4M3: lane j < NSB loads

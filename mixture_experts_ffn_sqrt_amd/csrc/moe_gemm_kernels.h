@@ -39,7 +39,7 @@ struct GemmArgs {
   int G;
   int dense_rows;             // dense mode: number of rows
   int n_tiles;                // column tiles
-  char* C;                    // output rows (indexed by dispatch row)
+  char* C;                    // output rows: dispatch rows (grouped) or A rows (dense)
   int64_t ldc;                // bytes between output rows
   const float* col_add;       // EPI_LOGITS: per-column addend (nullable)
   int k_chunk;                // dense split-K: elements of K per grid row y (0: no split)
