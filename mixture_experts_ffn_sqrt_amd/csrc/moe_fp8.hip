@@ -175,7 +175,7 @@ template <int BM, int BN, int WM, int WN, int EPI, int ST, int WF = WF_E4M3>
 hipError_t launch_fp8(const Fp8Args& q, int m_tiles_bound, hipStream_t s) {
   constexpr int NT = 64 * WM * WN;
   constexpr int LDS = ST * fp8_stage_bytes<BM, BN, WF>();
-  const int grid = m_tiles_bound * q.g.n_tiles;
+  const int grid = xcd_grid((int64_t)m_tiles_bound * q.g.n_tiles);
   if (grid <= 0) return hipSuccess;
   auto kern = grouped_gemm_fp8<BM, BN, WM, WN, EPI, ST, WF>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

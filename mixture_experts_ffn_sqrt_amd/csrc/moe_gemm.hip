@@ -32,7 +32,7 @@ template <typename TE, int BM, int BN, int WM, int WN, int EPI>
 hipError_t launch_gemm(GemmArgs p, int m_tiles_bound, hipStream_t s, int splits = 1) {
   constexpr int NT = 64 * WM * WN;
   constexpr int LDS = 2 * (BM + BN) * 128;
-  const int grid = m_tiles_bound * p.n_tiles;
+  const int grid = xcd_grid((int64_t)m_tiles_bound * p.n_tiles);
   if (grid <= 0) return hipSuccess;
   auto kern = grouped_gemm_staged<TE, BM, BN, WM, WN, EPI>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -47,7 +47,7 @@ template <int BM, int BN, int WM, int WN, int EPI, int ST, int ROWB, int SWZ>
 hipError_t launch_gemm_dma(GemmArgs p, int m_tiles_bound, hipStream_t s) {
   constexpr int NT = 64 * WM * WN;
   constexpr int LDS = ST * (BM + BN) * ROWB;
-  const int grid = m_tiles_bound * p.n_tiles;
+  const int grid = xcd_grid((int64_t)m_tiles_bound * p.n_tiles);
   if (grid <= 0) return hipSuccess;
   auto kern = grouped_gemm_dma<BM, BN, WM, WN, EPI, ST, ROWB, SWZ>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

@@ -49,6 +49,14 @@ __host__ __device__ constexpr int group_tiles(int M, int bm) {
   return M <= 0 ? 0 : ceil_div(M, group_tile_rows(M, bm));
 }
 
+// Consecutive tiles of a grouped GEMM's tile order that run on one XCD (see
+// decode_tile); grids are whole multiples of 8 * kXcdChunk blocks.
+constexpr int kXcdChunk = 16;
+inline int xcd_grid(int64_t tiles) {
+  const int64_t u = 8 * kXcdChunk;
+  return tiles <= 0 ? 0 : (int)((tiles + u - 1) / u * u);
+}
+
 // Down GEMM of groups that average 512 rows or more: 288-row tiles (3 x 4
 // waves of 96 x 64).  A group of 4 x 256 rows plus the few percent that a
 // random routing adds to about half of the groups still fits 4 of them, where
