@@ -171,13 +171,13 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(int R, int C, cons
   if (t == 0) scales[(int64_t)br * GC + bc] = ldexpf(1.0f, e);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int ST, int WF = WF_E4M3>
+template <int BM, int BN, int WM, int WN, int EPI, int ST, int WF = WF_E4M3, int SCHED = 0>
 hipError_t launch_fp8(const Fp8Args& q, int m_tiles_bound, hipStream_t s) {
   constexpr int NT = 64 * WM * WN;
   constexpr int LDS = ST * fp8_stage_bytes<BM, BN, WF>();
   const int grid = xcd_grid((int64_t)m_tiles_bound * q.g.n_tiles);
   if (grid <= 0) return hipSuccess;
-  auto kern = grouped_gemm_fp8<BM, BN, WM, WN, EPI, ST, WF>;
+  auto kern = grouped_gemm_fp8<BM, BN, WM, WN, EPI, ST, WF, SCHED>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   if (e != hipSuccess) return e;
@@ -283,8 +283,9 @@ hipError_t launch_expert_up_fp8(const moe_config& c, const Fp8FfnArgs& a, hipStr
   }
   g.tile_prefix = a.tile_prefix + tile_height_index(256) * (a.n_groups + 1);
   const int mt = tile_bound8(a.rows_bound, a.n_groups, 256);
-  return mx ? launch_fp8<256, 256, 4, 2, EPI_SWIGLU8, 3, WF_MXFP4>(q, mt, s)
-            : launch_fp8<256, 256, 4, 2, EPI_SWIGLU8, 2>(q, mt, s);
+  // scheduled main loop (MXFP4 up GEMMs 1-3% faster, FP8 0-2%)
+  return mx ? launch_fp8<256, 256, 4, 2, EPI_SWIGLU8, 3, WF_MXFP4, 1>(q, mt, s)
+            : launch_fp8<256, 256, 4, 2, EPI_SWIGLU8, 2, WF_E4M3, 1>(q, mt, s);
 }
 
 hipError_t launch_expert_down_fp8(const moe_config& c, const Fp8FfnArgs& a, hipStream_t s) {
@@ -331,8 +332,11 @@ hipError_t launch_expert_down_fp8(const moe_config& c, const Fp8FfnArgs& a, hipS
   }
   g.tile_prefix = a.tile_prefix + tile_height_index(256) * (a.n_groups + 1);
   const int mt = tile_bound8(a.rows_bound, a.n_groups, 256);
-  return mx ? launch_fp8<256, 256, 4, 4, EPI_STORE, 3, WF_MXFP4>(q, mt, s)
-            : launch_fp8<256, 256, 4, 4, EPI_STORE, 2>(q, mt, s);
+  // scheduled main loop (within 1%; the 288-row tiles above keep the
+  // compiler's order: their double-buffered fragments would not fit in the
+  // registers of three waves per SIMD)
+  return mx ? launch_fp8<256, 256, 4, 4, EPI_STORE, 3, WF_MXFP4, 1>(q, mt, s)
+            : launch_fp8<256, 256, 4, 4, EPI_STORE, 2, WF_E4M3, 1>(q, mt, s);
 }
 
 }  // namespace moe

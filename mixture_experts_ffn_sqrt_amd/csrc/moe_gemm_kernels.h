@@ -416,7 +416,38 @@ __device__ __forceinline__ int swz_sel(int r) {
   else return (r >> 2) & M;
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int ROWB, int SWZ>
+// Instruction order of one stage of a scheduled main loop: the R0 LDS reads
+// that come first (the first k-step's fragments, and any per-stage scale
+// reads), then for every k-step but the last its M MFMAs, each followed by its
+// share of the next k-step's R fragment reads, then the last k-step's MFMAs.
+// A wave then multiplies one k-step while the next one's fragments are on
+// their way from LDS, instead of waiting for each k-step's reads in turn.
+// (Scheduling only: the compiler keeps every dependence whatever the groups
+// say.  0x008: MFMA, 0x100: LDS read.)
+template <int J, int M, int R>
+struct SchedInterleave {
+  __device__ __forceinline__ static void run() {
+    constexpr int n = (R * (J + 1) + M - 1) / M - (R * J + M - 1) / M;  // reads after MFMA J
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);
+    SchedInterleave<J + 1, M, R>::run();
+  }
+};
+template <int M, int R>
+struct SchedInterleave<M, M, R> {
+  __device__ __forceinline__ static void run() {}
+};
+template <int KS, int M, int R, int R0 = R>
+__device__ __forceinline__ void sched_stage() {
+  __builtin_amdgcn_sched_group_barrier(0x100, R0, 0);
+#pragma unroll
+  for (int kk = 0; kk < KS - 1; ++kk) SchedInterleave<0, M, R>::run();
+  __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
+}
+
+// SCHED = 1: fragments double-buffered in registers across the k-steps of a
+// stage, in the order sched_stage fixes (full tiles only).
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int ROWB, int SWZ, int SCHED = 0>
 __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) {
   constexpr int NT = 64 * WM * WN, NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -530,27 +561,48 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
 
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) MOE_DMA_ISSUE(s);
+  // fragment reads of k-step kk_ of the stage at cur into fa_ / fb_, and that
+  // k-step's MFMAs (fragments with no valid row skipped when CHECK)
+#define MOE_DMA_FRAGS(fa_, fb_, kk_)                                                          \
+  do {                                                                                       \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i)                                            \
+        fa_[i] = *reinterpret_cast<const u32x4*>(cur + a_rd[kk_] + i * 32 * ROWB);           \
+    _Pragma("unroll") for (int f = 0; f < FN; ++f)                                            \
+        fb_[f] = *reinterpret_cast<const u32x4*>(cur + b_rd[kk_] + b_row[f] * ROWB);         \
+  } while (0)
+#define MOE_DMA_MMA(fa_, fb_, CHECK)                                                          \
+  do {                                                                                       \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                          \
+      if (CHECK && i >= live) continue;                                                      \
+      _Pragma("unroll") for (int f = 0; f < FN; ++f)                                          \
+          acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                               \
+              __builtin_bit_cast(bf16x8, fa_[i]), __builtin_bit_cast(bf16x8, fb_[f]),        \
+              acc[i][f], 0, 0, 0);                                                           \
+    }                                                                                        \
+  } while (0)
 #define MOE_DMA_MAIN(CHECK)                                                                   \
   for (int kt = 0; kt < KT; ++kt) {                                                          \
     /* at most STAGES-2 later stages' loads in flight: LA + LB per stage, one */           \
     /* fewer on waves without the last B slot */                                             \
     wait_loads_le<STAGES - 2, LA + LB - 1>(LA + LB - (b_last ? 0 : 1));                      \
     __builtin_amdgcn_s_waitcnt(0xC07F);                                                      \
-    lds_barrier();                                                            \
+    lds_barrier();                                                                           \
     MOE_DMA_ISSUE(kt + STAGES - 1);                                                           \
     const char* cur = smem + (kt % STAGES) * STAGE;                                          \
-    _Pragma("unroll") for (int kk = 0; kk < KSTEPS; ++kk) {                                  \
-      u32x4 fa[FM], fb[FN];                                                                  \
-      _Pragma("unroll") for (int i = 0; i < FM; ++i)                                          \
-          fa[i] = *reinterpret_cast<const u32x4*>(cur + a_rd[kk] + i * 32 * ROWB);           \
-      _Pragma("unroll") for (int f = 0; f < FN; ++f)                                          \
-          fb[f] = *reinterpret_cast<const u32x4*>(cur + b_rd[kk] + b_row[f] * ROWB);         \
-      _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                        \
-        if (CHECK && i >= live) continue;                                                    \
-        _Pragma("unroll") for (int f = 0; f < FN; ++f)                                        \
-            acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                             \
-                __builtin_bit_cast(bf16x8, fa[i]), __builtin_bit_cast(bf16x8, fb[f]),        \
-                acc[i][f], 0, 0, 0);                                                         \
+    if constexpr (SCHED) {                                                                   \
+      u32x4 fa[2][FM], fb[2][FN];                                                            \
+      MOE_DMA_FRAGS(fa[0], fb[0], 0);                                                        \
+      _Pragma("unroll") for (int kk = 0; kk < KSTEPS; ++kk) {                                \
+        if (kk + 1 < KSTEPS)                                                                 \
+          MOE_DMA_FRAGS(fa[(kk + 1) & 1], fb[(kk + 1) & 1], (kk + 1) % KSTEPS);              \
+        MOE_DMA_MMA(fa[kk & 1], fb[kk & 1], CHECK);                                          \
+      }                                                                                      \
+      if (!CHECK) sched_stage<KSTEPS, FM * FN, FM + FN>();                                   \
+    } else {                                                                                 \
+      _Pragma("unroll") for (int kk = 0; kk < KSTEPS; ++kk) {                                \
+        u32x4 fa[FM], fb[FN];                                                                \
+        MOE_DMA_FRAGS(fa, fb, kk);                                                           \
+        MOE_DMA_MMA(fa, fb, CHECK);                                                          \
       }                                                                                      \
     }                                                                                        \
   }
@@ -560,6 +612,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
     MOE_DMA_MAIN(true)
   }
 #undef MOE_DMA_MAIN
+#undef MOE_DMA_MMA
+#undef MOE_DMA_FRAGS
 #undef MOE_DMA_ISSUE
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no LDS load may still be in flight at exit
 
