@@ -43,13 +43,14 @@ hipError_t launch_gemm(GemmArgs p, int m_tiles_bound, hipStream_t s, int splits 
 }
 
 // Direct-to-LDS bf16 kernel (ST LDS buffers of ROWB/2 K-elements)
-template <int BM, int BN, int WM, int WN, int EPI, int ST, int ROWB, int SWZ, int SCHED = 0>
+template <int BM, int BN, int WM, int WN, int EPI, int ST, int ROWB, int SWZ, int SCHED = 0,
+          int BST = 0>
 hipError_t launch_gemm_dma(GemmArgs p, int m_tiles_bound, hipStream_t s) {
   constexpr int NT = 64 * WM * WN;
-  constexpr int LDS = ST * (BM + BN) * ROWB;
+  constexpr int LDS = (ST * BM + (BST ? BST : ST) * BN) * ROWB;
   const int grid = xcd_grid((int64_t)m_tiles_bound * p.n_tiles);
   if (grid <= 0) return hipSuccess;
-  auto kern = grouped_gemm_dma<BM, BN, WM, WN, EPI, ST, ROWB, SWZ, SCHED>;
+  auto kern = grouped_gemm_dma<BM, BN, WM, WN, EPI, ST, ROWB, SWZ, SCHED, BST>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   if (e != hipSuccess) return e;
@@ -190,9 +191,10 @@ hipError_t launch_expert_up(const moe_config& c, const ExpertFfnArgs& a, hipStre
       g.n_tiles = c.d_ff / 128;
       g.a_bytes = (uint32_t)((int64_t)c.T * c.d * es);
       g.b_bytes = (uint32_t)(2 * F * d * es);
-      // scheduled main loop: Mixtral's up GEMM 1.72 -> 1.69 ms, the
-      // DeepSeek-shaped ones within noise
-      return launch_gemm_dma<256, 256, 4, 4, EPI_SWIGLU, 2, 128, 3, 1>(g, mb, s);
+      // scheduled main loop (Mixtral's up GEMM 1.72 -> 1.69 ms) and a
+      // three-stage weight ring (DeepSeek-V3's 4.59 -> 4.51 ms; all 160 KB
+      // of LDS: two 32 KB A stages, three 32 KB B stages)
+      return launch_gemm_dma<256, 256, 4, 4, EPI_SWIGLU, 2, 128, 3, 1, 3>(g, mb, s);
     default:
       g.n_tiles = c.d_ff / 64;
       return launch_gemm<uint16_t, 128, 128, 2, 2, EPI_SWIGLU>(g, mb, s);
@@ -244,7 +246,8 @@ hipError_t launch_expert_down(const moe_config& c, const ExpertFfnArgs& a, hipSt
         return launch_gemm_dma<288, 256, 3, 4, EPI_STORE, 2, 128, 3, 1>(
             g, tile_bound(a.rows_bound, a.n_groups, 288), s);
       }
-      return launch_gemm_dma<256, 256, 4, 4, EPI_STORE, 2, 128, 3>(g, mb, s);
+      // three-stage weight ring: DeepSeek-V3's down GEMM 2.48 -> 2.43 ms
+      return launch_gemm_dma<256, 256, 4, 4, EPI_STORE, 2, 128, 3, 0, 3>(g, mb, s);
     default:
       g.n_tiles = ceil_div(c.d, 128);
       return launch_gemm<uint16_t, 128, 128, 2, 2, EPI_STORE>(g, mb, s);

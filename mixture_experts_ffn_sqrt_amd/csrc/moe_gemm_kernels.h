@@ -447,7 +447,13 @@ __device__ __forceinline__ void sched_stage() {
 
 // SCHED = 1: fragments double-buffered in registers across the k-steps of a
 // stage, in the order sched_stage fixes (full tiles only).
-template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int ROWB, int SWZ, int SCHED = 0>
+// BST: LDS stages of the weight operand B (0: STAGES, the A ring's depth).  The
+// two rings are separate, so B can be prefetched one stage further ahead than
+// A (BST = STAGES + 1): the weights of a group with a few hundred rows are
+// used by one row tile and so come from HBM, while the gathered A rows are
+// shared by the group's column tiles and mostly hit L2.
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int ROWB, int SWZ, int SCHED = 0,
+          int BST = 0>
 __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) {
   constexpr int NT = 64 * WM * WN, NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -456,7 +462,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
   constexpr int KSTEPS = ROWB / 32;                 // MFMA k-steps of 16 bf16 per stage
   constexpr int CPR = ROWB / 16;                    // 16-byte chunks per row
   constexpr int RPL = 1024 / ROWB;                  // rows filled by one wavefront load
-  constexpr int STAGE = (BM + BN) * ROWB;
+  constexpr int BSTG = BST ? BST : STAGES;
+  constexpr int DA = STAGES - 1, DB = BSTG - 1;     // prefetch distances (stages)
+  constexpr int A_STAGE = BM * ROWB, B_STAGE = BN * ROWB;
+  constexpr int B_RING = STAGES * A_STAGE;          // LDS offset of the B ring
   // 1 KB loads per stage: NA of A rows, NB of B rows; wave w issues A blocks
   // w + NW*j (j < LA) and B blocks w + NW*j (j < LB, block < NB)
   constexpr int NA = BM / RPL, NB = BN / RPL;
@@ -467,7 +476,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
   static_assert(!SW || FN % 2 == 0, "SwiGLU waves hold gate and up fragments in pairs");
   static_assert(NA * RPL == BM && NB * RPL == BN && LA * NW == NA, "A loads must split evenly");
   static_assert(!SW || (BN / 2) % RPL == 0, "a load is all gate or all up rows");
-  static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024, "LDS budget");
+  static_assert(STAGES >= 2 && B_RING + BSTG * B_STAGE <= 160 * 1024, "LDS budget");
+  static_assert(DB == DA || DB == DA + 1, "B runs at most one stage further ahead");
   extern __shared__ __align__(16) char smem[];
 
   TileCoord tc;
@@ -517,18 +527,25 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
   // the last B slot exists on waves whose block wave + NW*(LB-1) is < NB
   const bool b_last = B_EVEN || wave + NW * (LB - 1) < NB;
   const int KT = p.K / (ROWB / 2);  // ROWB/2 bf16 per stage
-  // Stage kt's loads; stages past the end reload the last one (never read;
-  // keeps the number of loads in flight constant).
-#define MOE_DMA_ISSUE(kt_)                                                                \
+  // Stage kt's A and B loads; stages past the end reload the last one (never
+  // read; keeps the number of loads in flight constant).  Loop iteration kt
+  // issues A(kt + DA), then B(kt + DB).
+#define MOE_DMA_ISSUE_A(kt_)                                                              \
   do {                                                                                   \
     const int kc_ = (kt_) < KT ? (kt_) : KT - 1;                                         \
-    char* buf_ = smem + ((kt_) % STAGES) * STAGE;                                        \
+    char* buf_ = smem + ((kt_) % STAGES) * A_STAGE;                                      \
     const uint32_t ko_ = (uint32_t)kc_ * ROWB;                                           \
     _Pragma("unroll") for (int j = 0; j < LA; ++j)                                        \
         load_lds16(a_rs, buf_ + (RPL * (wave + NW * j)) * ROWB, a_off[j] + ko_);         \
+  } while (0)
+#define MOE_DMA_ISSUE_B(kt_)                                                              \
+  do {                                                                                   \
+    const int kc_ = (kt_) < KT ? (kt_) : KT - 1;                                         \
+    char* buf_ = smem + B_RING + ((kt_) % BSTG) * B_STAGE;                               \
+    const uint32_t ko_ = (uint32_t)kc_ * ROWB;                                           \
     _Pragma("unroll") for (int j = 0; j < LB; ++j) {                                      \
       if (j == LB - 1 && !b_last) break;                                                 \
-      load_lds16(b_rs, buf_ + BM * ROWB + (RPL * (wave + NW * j)) * ROWB, b_off[j] + ko_); \
+      load_lds16(b_rs, buf_ + (RPL * (wave + NW * j)) * ROWB, b_off[j] + ko_);           \
     }                                                                                    \
   } while (0)
 
@@ -547,7 +564,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
   for (int kk = 0; kk < KSTEPS; ++kk) {
     const int sl = ((2 * kk + fh) ^ fs) << 4;
     a_rd[kk] = (wm * WTM + fr) * ROWB + sl;
-    b_rd[kk] = BM * ROWB + fr * ROWB + sl;
+    b_rd[kk] = fr * ROWB + sl;
   }
   int b_row[FN];
 #pragma unroll
@@ -559,16 +576,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
   // tile takes the branch-free loop.
   const int live = min(FM, max(0, (tc.nrows - wm * WTM + 31) / 32));
 
+  // prologue: the loads of iterations -DB .. -1 of the loop's issue pattern
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) MOE_DMA_ISSUE(s);
+  for (int j = -DB; j < 0; ++j) {
+    if (j + DA >= 0) MOE_DMA_ISSUE_A(j + DA);
+    MOE_DMA_ISSUE_B(j + DB);
+  }
   // fragment reads of k-step kk_ of the stage at cur into fa_ / fb_, and that
   // k-step's MFMAs (fragments with no valid row skipped when CHECK)
 #define MOE_DMA_FRAGS(fa_, fb_, kk_)                                                          \
   do {                                                                                       \
     _Pragma("unroll") for (int i = 0; i < FM; ++i)                                            \
-        fa_[i] = *reinterpret_cast<const u32x4*>(cur + a_rd[kk_] + i * 32 * ROWB);           \
+        fa_[i] = *reinterpret_cast<const u32x4*>(curA + a_rd[kk_] + i * 32 * ROWB);          \
     _Pragma("unroll") for (int f = 0; f < FN; ++f)                                            \
-        fb_[f] = *reinterpret_cast<const u32x4*>(cur + b_rd[kk_] + b_row[f] * ROWB);         \
+        fb_[f] = *reinterpret_cast<const u32x4*>(curB + b_rd[kk_] + b_row[f] * ROWB);        \
   } while (0)
 #define MOE_DMA_MMA(fa_, fb_, CHECK)                                                          \
   do {                                                                                       \
@@ -582,13 +603,22 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
   } while (0)
 #define MOE_DMA_MAIN(CHECK)                                                                   \
   for (int kt = 0; kt < KT; ++kt) {                                                          \
-    /* at most STAGES-2 later stages' loads in flight: LA + LB per stage, one */           \
-    /* fewer on waves without the last B slot */                                             \
-    wait_loads_le<STAGES - 2, LA + LB - 1>(LA + LB - (b_last ? 0 : 1));                      \
+    /* A(kt) and B(kt) landed: the loads issued after A(kt) may still be in */            \
+    /* flight, i.e. DA-1 later iterations' A and B loads (LA + LB per stage, one */         \
+    /* fewer on waves without the last B slot), and with DB > DA also the B */              \
+    /* loads issued right after A(kt) */                                                    \
+    if constexpr (DB > DA) {                                                                 \
+      static_assert(DA == 1, "one stage of A ahead when B runs further");                   \
+      wait_loads_le<1, LB - 1>(LB - (b_last ? 0 : 1));                                       \
+    } else {                                                                                 \
+      wait_loads_le<STAGES - 2, LA + LB - 1>(LA + LB - (b_last ? 0 : 1));                    \
+    }                                                                                        \
     __builtin_amdgcn_s_waitcnt(0xC07F);                                                      \
     lds_barrier();                                                                           \
-    MOE_DMA_ISSUE(kt + STAGES - 1);                                                           \
-    const char* cur = smem + (kt % STAGES) * STAGE;                                          \
+    MOE_DMA_ISSUE_A(kt + DA);                                                                 \
+    MOE_DMA_ISSUE_B(kt + DB);                                                                 \
+    const char* curA = smem + (kt % STAGES) * A_STAGE;                                       \
+    const char* curB = smem + B_RING + (kt % BSTG) * B_STAGE;                                \
     if constexpr (SCHED) {                                                                   \
       u32x4 fa[2][FM], fb[2][FN];                                                            \
       MOE_DMA_FRAGS(fa[0], fb[0], 0);                                                        \
@@ -614,7 +644,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
 #undef MOE_DMA_MAIN
 #undef MOE_DMA_MMA
 #undef MOE_DMA_FRAGS
-#undef MOE_DMA_ISSUE
+#undef MOE_DMA_ISSUE_A
+#undef MOE_DMA_ISSUE_B
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no LDS load may still be in flight at exit
 
   // epilogue: lane holds C[8*(r/4) + 4*(lane/32) + r%4][lane % 32] of each fragment

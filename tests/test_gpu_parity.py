@@ -236,6 +236,9 @@ def test_permute_random(T, k, E, mode):
     ("bf16", 2000, 512, 8, 2, 384),    # 256x256 tiles, several row tiles per expert
     ("bf16", 2100, 320, 4, 2, 256),    # ~1050 rows per expert: 288x256 down tiles, partial column
     ("bf16", 1300, 256, 2, 1, 128),    # ~650 rows per expert: 288-row down tiles, ragged last tile
+    ("bf16", 600, 64, 4, 2, 128),      # 256x256 tiles with K shorter than the weight ring:
+                                       # one K stage up, two down, partial column tile
+    ("bf16", 900, 128, 3, 2, 128),     # two K stages up; 288-row down tiles
 ])
 def test_expert_ffn_and_combine(dtype, T, d, E, k, d_ff):
     lc = CONFIGS["tiny_fp32"].with_(T=T, d=d, E=E, k=k, d_ff=d_ff, dtype=dtype, seed=23)
