@@ -120,8 +120,8 @@ namespace {
 
 // Tile shape of the grouped expert GEMMs.  Rows per group on average (known on
 // the host from T, k and the group count) picks 32-row tiles for
-// decode-shaped batches and 256x256 tiles for prefill-shaped ones (288x256
-// for the down GEMM of large groups, see tall_down_tiles), all on the
+// decode-shaped batches and 288x256 (up) / 256x256 tiles for prefill-shaped
+// ones (288x256 for the down GEMM of large groups, see tall_down_tiles), all on the
 // direct-to-LDS kernel when the shapes allow it (d_ff a multiple of 128 and
 // operands addressable with 31-bit offsets), else 16- or 128-row tiles on the
 // register-staged kernel.  The direct-to-LDS shapes accumulate K in the same
@@ -191,10 +191,12 @@ hipError_t launch_expert_up(const moe_config& c, const ExpertFfnArgs& a, hipStre
       g.n_tiles = c.d_ff / 128;
       g.a_bytes = (uint32_t)((int64_t)c.T * c.d * es);
       g.b_bytes = (uint32_t)(2 * F * d * es);
-      // scheduled main loop (Mixtral's up GEMM 1.72 -> 1.69 ms) and a
-      // three-stage weight ring (DeepSeek-V3's 4.59 -> 4.51 ms; all 160 KB
-      // of LDS: two 32 KB A stages, three 32 KB B stages)
-      return launch_gemm_dma<256, 256, 4, 4, EPI_SWIGLU, 2, 128, 3, 1, 3>(g, mb, s);
+      // 288-row tiles (3 x 4 waves of 96 x 64) with the scheduled main loop:
+      // Mixtral's up GEMM 1.72 -> 1.67 ms and DeepSeek-V3's 4.52 -> 4.33 ms
+      // against 256-row tiles with a three-stage weight ring
+      g.tile_prefix = a.tile_prefix + tile_height_index(288) * (a.n_groups + 1);
+      return launch_gemm_dma<288, 256, 3, 4, EPI_SWIGLU, 2, 128, 3, 1>(
+          g, tile_bound(a.rows_bound, a.n_groups, 288), s);
     default:
       g.n_tiles = c.d_ff / 64;
       return launch_gemm<uint16_t, 128, 128, 2, 2, EPI_SWIGLU>(g, mb, s);

@@ -61,8 +61,8 @@ inline int xcd_grid(int64_t tiles) {
 // waves of 96 x 64).  A group of 4 x 256 rows plus the few percent that a
 // random routing adds to about half of the groups still fits 4 of them, where
 // 256-row tiles would add a fifth row of tiles to those groups and with it a
-// partly filled extra round of blocks over the 256 CUs.  (The up GEMM has many
-// rounds of tiles, so its last partial round weighs little.)
+// partly filled extra round of blocks over the 256 CUs.  (The up GEMM runs
+// 288-row tiles on every prefill-shaped batch.)
 inline bool tall_down_tiles(int64_t rows_bound, int n_groups) {
   return n_groups > 0 && rows_bound >= (int64_t)512 * n_groups;
 }
