@@ -191,8 +191,10 @@ int tile_bound8(int64_t rows, int groups, int bm) {
 }
 
 // 32-row streaming tiles when experts have a few rows each (decode), else
-// 256x256 tiles (288x256 for the down GEMM of large groups; the same rules as
-// the bf16 experts).  The decode tiles keep
+// 256x256 tiles (288x256 for the down GEMM of large groups, the rule of the
+// bf16 down GEMM; the up GEMM stays at 256 rows, where the bf16 one takes 288:
+// 288-row FP8 up tiles measured 1.5% faster to 5% slower across the prefill
+// shapes).  The decode tiles keep
 // short LDS rings (2-3 stages, 40-80 KB) so that two to four blocks share a CU
 // and one block's pipeline fill and epilogue overlap another's streaming:
 // measured faster than one block per CU with a 4-12 stage ring.

@@ -15,10 +15,12 @@
 // reads the device-side tile prefix to find its (group, row tile), and blocks
 // past the real tile count exit at once.
 //
-// grouped_gemm_dma (bf16): direct global -> LDS buffer loads into a ring of
-// LDS stages, MFMA 32x32x16.  256x256 tiles on 16 wavefronts when experts have
-// many rows (MFMA-bound prefill); 32-row tiles with a four-stage ring when
-// they have a few (each expert's weights streamed once, HBM-bound decode).
+// grouped_gemm_dma (bf16): direct global -> LDS buffer loads into rings of
+// LDS stages, MFMA 32x32x16.  When experts have many rows (MFMA-bound
+// prefill): 288x256 tiles on 12 wavefronts for the up GEMM and for the down
+// GEMM of large experts, else 256x256 tiles on 16 wavefronts; 32-row tiles
+// with a four-stage ring when they have a few (each expert's weights streamed
+// once, HBM-bound decode).
 // grouped_gemm_staged (any element type): global -> registers -> LDS, two
 // stages, MFMA 16x16; the router GEMM (split over K), the fp32 configurations
 // and shapes the buffer-load kernel does not take.
@@ -120,9 +122,9 @@ namespace {
 
 // Tile shape of the grouped expert GEMMs.  Rows per group on average (known on
 // the host from T, k and the group count) picks 32-row tiles for
-// decode-shaped batches and 288x256 (up) / 256x256 tiles for prefill-shaped
-// ones (288x256 for the down GEMM of large groups, see tall_down_tiles), all on the
-// direct-to-LDS kernel when the shapes allow it (d_ff a multiple of 128 and
+// decode-shaped batches and, for prefill-shaped ones, 288x256 tiles for the
+// up GEMM and 256x256 tiles for the down GEMM (288x256 for large groups, see
+// tall_down_tiles), all on the direct-to-LDS kernel when the shapes allow it (d_ff a multiple of 128 and
 // operands addressable with 31-bit offsets), else 16- or 128-row tiles on the
 // register-staged kernel.  The direct-to-LDS shapes accumulate K in the same
 // order (64-element slabs, 16-element MFMA steps, one fp32 accumulator per
