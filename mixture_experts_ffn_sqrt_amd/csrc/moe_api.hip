@@ -27,7 +27,7 @@ Workspace workspace_layout(const moe_config& c) {
   w.counts = take(E * 4);
   w.offsets = take((E + 1) * 4);
   w.groups = take(2 * G * 4);
-  w.tile_prefix = take(kNumTileHeights * (G + 1) * 4);
+  w.tile_prefix = take(kNumTileLists * (G + 1) * 4);
   w.sorted_tok = take(P * 4);
   w.sorted_w = take(R * 4);
   w.dispatch = take(R * 4);

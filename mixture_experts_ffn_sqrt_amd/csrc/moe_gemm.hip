@@ -45,14 +45,13 @@ hipError_t launch_gemm(GemmArgs p, int m_tiles_bound, hipStream_t s, int splits 
 }
 
 // Direct-to-LDS bf16 kernel (ST LDS buffers of ROWB/2 K-elements)
-template <int BM, int BN, int WM, int WN, int EPI, int ST, int ROWB, int SWZ, int SCHED = 0,
-          int BST = 0>
+template <int BM, int BN, int WM, int WN, int EPI, int ST, int ROWB, int SWZ, int SCHED = 0>
 hipError_t launch_gemm_dma(GemmArgs p, int m_tiles_bound, hipStream_t s) {
   constexpr int NT = 64 * WM * WN;
-  constexpr int LDS = (ST * BM + (BST ? BST : ST) * BN) * ROWB;
+  constexpr int LDS = ST * (BM + BN) * ROWB;
   const int grid = xcd_grid((int64_t)m_tiles_bound * p.n_tiles);
   if (grid <= 0) return hipSuccess;
-  auto kern = grouped_gemm_dma<BM, BN, WM, WN, EPI, ST, ROWB, SWZ, SCHED, BST>;
+  auto kern = grouped_gemm_dma<BM, BN, WM, WN, EPI, ST, ROWB, SWZ, SCHED>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   if (e != hipSuccess) return e;
@@ -65,6 +64,11 @@ hipError_t launch_gemm_dma(GemmArgs p, int m_tiles_bound, hipStream_t s) {
 int tile_bound(int64_t rows, int groups, int bm) {
   const int64_t ne = rows < groups ? rows : groups;
   return (int)((rows + ne * (bm - 1)) / bm);
+}
+
+// Row tiles of list kListSmall32: one per group of at most kSmallGroupRows rows.
+int small_group_bound(const ExpertFfnArgs& a) {
+  return (int)(a.rows_bound < a.n_groups ? a.rows_bound : a.n_groups);
 }
 
 }  // namespace
@@ -131,7 +135,7 @@ namespace {
 // output), so a row's result does not depend on which of them runs: with the
 // router's T-independent split, the layer output of a token does not depend on
 // the batch it is in.
-enum class FfnTiles { F32_16, BF16_16, BF16_32, BF16_128, BF16_256 };
+enum class FfnTiles { F32_16, BF16_16, BF16_32, BF16_128, BF16_PREFILL };
 
 FfnTiles pick_tiles(const moe_config& c, const ExpertFfnArgs& a) {
   if (c.dtype == MOE_F32) return FfnTiles::F32_16;
@@ -144,11 +148,11 @@ FfnTiles pick_tiles(const moe_config& c, const ExpertFfnArgs& a) {
   // a few rows per expert: the GEMMs stream each expert's weights once
   // (HBM-bound); 32-row tiles with a deep direct-to-LDS pipeline
   if (avg_rows < 48) return fits ? FfnTiles::BF16_32 : FfnTiles::BF16_16;
-  return fits ? FfnTiles::BF16_256 : FfnTiles::BF16_128;
+  return fits ? FfnTiles::BF16_PREFILL : FfnTiles::BF16_128;
 }
 
 int tile_rows(FfnTiles t) {
-  return t == FfnTiles::BF16_256 ? 256 : t == FfnTiles::BF16_128 ? 128
+  return t == FfnTiles::BF16_PREFILL ? 288 : t == FfnTiles::BF16_128 ? 128
                                          : t == FfnTiles::BF16_32  ? 32 : 16;
 }
 
@@ -189,16 +193,22 @@ hipError_t launch_expert_up(const moe_config& c, const ExpertFfnArgs& a, hipStre
       g.a_bytes = (uint32_t)((int64_t)c.T * c.d * es);
       g.b_bytes = (uint32_t)(2 * F * d * es);
       return launch_gemm_dma<32, 256, 1, 4, EPI_SWIGLU, 4, 128, 3>(g, mb, s);
-    case FfnTiles::BF16_256:
+    case FfnTiles::BF16_PREFILL: {
       g.n_tiles = c.d_ff / 128;
       g.a_bytes = (uint32_t)((int64_t)c.T * c.d * es);
       g.b_bytes = (uint32_t)(2 * F * d * es);
-      // 288-row tiles (3 x 4 waves of 96 x 64) with the scheduled main loop:
-      // Mixtral's up GEMM 1.72 -> 1.67 ms and DeepSeek-V3's 4.52 -> 4.33 ms
-      // against 256-row tiles with a three-stage weight ring
-      g.tile_prefix = a.tile_prefix + tile_height_index(288) * (a.n_groups + 1);
-      return launch_gemm_dma<288, 256, 3, 4, EPI_SWIGLU, 2, 128, 3, 1>(
-          g, tile_bound(a.rows_bound, a.n_groups, 288), s);
+      // groups of a few rows: one 32-row streaming tile each
+      GemmArgs gs = g;
+      gs.tile_prefix = a.tile_prefix + kListSmall32 * (a.n_groups + 1);
+      const hipError_t e =
+          launch_gemm_dma<32, 256, 1, 4, EPI_SWIGLU, 4, 128, 3>(gs, small_group_bound(a), s);
+      if (e != hipSuccess) return e;
+      // the others: 288-row tiles (3 x 4 waves of 96 x 64) with the scheduled
+      // main loop (Mixtral's up GEMM 1.72 -> 1.67 ms and DeepSeek-V3's 4.52 ->
+      // 4.33 ms against 256-row tiles)
+      g.tile_prefix = a.tile_prefix + kListLarge288 * (a.n_groups + 1);
+      return launch_gemm_dma<288, 256, 3, 4, EPI_SWIGLU, 2, 128, 3, 1>(g, mb, s);
+    }
     default:
       g.n_tiles = c.d_ff / 64;
       return launch_gemm<uint16_t, 128, 128, 2, 2, EPI_SWIGLU>(g, mb, s);
@@ -239,19 +249,22 @@ hipError_t launch_expert_down(const moe_config& c, const ExpertFfnArgs& a, hipSt
       g.a_bytes = (uint32_t)((int64_t)a.rows_bound * F * es);
       g.b_bytes = (uint32_t)(d * F * es);
       return launch_gemm_dma<32, 128, 1, 2, EPI_STORE, 4, 128, 3>(g, mb, s);
-    case FfnTiles::BF16_256:
-      g.n_tiles = ceil_div(c.d, 256);
+    case FfnTiles::BF16_PREFILL: {
       g.a_bytes = (uint32_t)((int64_t)a.rows_bound * F * es);
       g.b_bytes = (uint32_t)(d * F * es);
-      if (tall_down_tiles(a.rows_bound, a.n_groups)) {
-        // scheduled main loop: 0.88 -> 0.83 ms on Mixtral's down GEMM (the
-        // 256-row down tiles keep the compiler's order: 0.5% slower scheduled)
-        g.tile_prefix = a.tile_prefix + tile_height_index(288) * (a.n_groups + 1);
-        return launch_gemm_dma<288, 256, 3, 4, EPI_STORE, 2, 128, 3, 1>(
-            g, tile_bound(a.rows_bound, a.n_groups, 288), s);
-      }
-      // three-stage weight ring: DeepSeek-V3's down GEMM 2.48 -> 2.43 ms
-      return launch_gemm_dma<256, 256, 4, 4, EPI_STORE, 2, 128, 3, 0, 3>(g, mb, s);
+      // groups of a few rows: one 32-row streaming tile each
+      GemmArgs gs = g;
+      gs.n_tiles = ceil_div(c.d, 128);
+      gs.tile_prefix = a.tile_prefix + kListSmall32 * (a.n_groups + 1);
+      const hipError_t e =
+          launch_gemm_dma<32, 128, 1, 2, EPI_STORE, 4, 128, 3>(gs, small_group_bound(a), s);
+      if (e != hipSuccess) return e;
+      // the others: 288-row tiles with the scheduled main loop (Mixtral's down
+      // GEMM 0.88 -> 0.83 ms against the compiler's order)
+      g.n_tiles = ceil_div(c.d, 256);
+      g.tile_prefix = a.tile_prefix + kListLarge288 * (a.n_groups + 1);
+      return launch_gemm_dma<288, 256, 3, 4, EPI_STORE, 2, 128, 3, 1>(g, mb, s);
+    }
     default:
       g.n_tiles = ceil_div(c.d, 128);
       return launch_gemm<uint16_t, 128, 128, 2, 2, EPI_STORE>(g, mb, s);

@@ -447,13 +447,7 @@ __device__ __forceinline__ void sched_stage() {
 
 // SCHED = 1: fragments double-buffered in registers across the k-steps of a
 // stage, in the order sched_stage fixes (full tiles only).
-// BST: LDS stages of the weight operand B (0: STAGES, the A ring's depth).  The
-// two rings are separate, so B can be prefetched one stage further ahead than
-// A (BST = STAGES + 1): the weights of a group with a few hundred rows are
-// used by one row tile and so come from HBM, while the gathered A rows are
-// shared by the group's column tiles and mostly hit L2.
-template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int ROWB, int SWZ, int SCHED = 0,
-          int BST = 0>
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int ROWB, int SWZ, int SCHED = 0>
 __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) {
   constexpr int NT = 64 * WM * WN, NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -462,8 +456,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
   constexpr int KSTEPS = ROWB / 32;                 // MFMA k-steps of 16 bf16 per stage
   constexpr int CPR = ROWB / 16;                    // 16-byte chunks per row
   constexpr int RPL = 1024 / ROWB;                  // rows filled by one wavefront load
-  constexpr int BSTG = BST ? BST : STAGES;
-  constexpr int DA = STAGES - 1, DB = BSTG - 1;     // prefetch distances (stages)
   constexpr int A_STAGE = BM * ROWB, B_STAGE = BN * ROWB;
   constexpr int B_RING = STAGES * A_STAGE;          // LDS offset of the B ring
   // 1 KB loads per stage: NA of A rows, NB of B rows; wave w issues A blocks
@@ -476,8 +468,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
   static_assert(!SW || FN % 2 == 0, "SwiGLU waves hold gate and up fragments in pairs");
   static_assert(NA * RPL == BM && NB * RPL == BN && LA * NW == NA, "A loads must split evenly");
   static_assert(!SW || (BN / 2) % RPL == 0, "a load is all gate or all up rows");
-  static_assert(STAGES >= 2 && B_RING + BSTG * B_STAGE <= 160 * 1024, "LDS budget");
-  static_assert(DB == DA || DB == DA + 1, "B runs at most one stage further ahead");
+  static_assert(STAGES >= 2 && B_RING + STAGES * B_STAGE <= 160 * 1024, "LDS budget");
   extern __shared__ __align__(16) char smem[];
 
   TileCoord tc;
@@ -527,9 +518,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
   // the last B slot exists on waves whose block wave + NW*(LB-1) is < NB
   const bool b_last = B_EVEN || wave + NW * (LB - 1) < NB;
   const int KT = p.K / (ROWB / 2);  // ROWB/2 bf16 per stage
-  // Stage kt's A and B loads; stages past the end reload the last one (never
-  // read; keeps the number of loads in flight constant).  Loop iteration kt
-  // issues A(kt + DA), then B(kt + DB).
+  // Stage kt's A and B loads (A and B in rings of their own); stages past the
+  // end reload the last one (never read; keeps the number of loads in flight
+  // constant).
 #define MOE_DMA_ISSUE_A(kt_)                                                              \
   do {                                                                                   \
     const int kc_ = (kt_) < KT ? (kt_) : KT - 1;                                         \
@@ -541,7 +532,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
 #define MOE_DMA_ISSUE_B(kt_)                                                              \
   do {                                                                                   \
     const int kc_ = (kt_) < KT ? (kt_) : KT - 1;                                         \
-    char* buf_ = smem + B_RING + ((kt_) % BSTG) * B_STAGE;                               \
+    char* buf_ = smem + B_RING + ((kt_) % STAGES) * B_STAGE;                             \
     const uint32_t ko_ = (uint32_t)kc_ * ROWB;                                           \
     _Pragma("unroll") for (int j = 0; j < LB; ++j) {                                      \
       if (j == LB - 1 && !b_last) break;                                                 \
@@ -576,11 +567,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
   // tile takes the branch-free loop.
   const int live = min(FM, max(0, (tc.nrows - wm * WTM + 31) / 32));
 
-  // prologue: the loads of iterations -DB .. -1 of the loop's issue pattern
 #pragma unroll
-  for (int j = -DB; j < 0; ++j) {
-    if (j + DA >= 0) MOE_DMA_ISSUE_A(j + DA);
-    MOE_DMA_ISSUE_B(j + DB);
+  for (int st = 0; st < STAGES - 1; ++st) {
+    MOE_DMA_ISSUE_A(st);
+    MOE_DMA_ISSUE_B(st);
   }
   // fragment reads of k-step kk_ of the stage at cur into fa_ / fb_, and that
   // k-step's MFMAs (fragments with no valid row skipped when CHECK)
@@ -603,22 +593,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
   } while (0)
 #define MOE_DMA_MAIN(CHECK)                                                                   \
   for (int kt = 0; kt < KT; ++kt) {                                                          \
-    /* A(kt) and B(kt) landed: the loads issued after A(kt) may still be in */            \
-    /* flight, i.e. DA-1 later iterations' A and B loads (LA + LB per stage, one */         \
-    /* fewer on waves without the last B slot), and with DB > DA also the B */              \
-    /* loads issued right after A(kt) */                                                    \
-    if constexpr (DB > DA) {                                                                 \
-      static_assert(DA == 1, "one stage of A ahead when B runs further");                   \
-      wait_loads_le<1, LB - 1>(LB - (b_last ? 0 : 1));                                       \
-    } else {                                                                                 \
-      wait_loads_le<STAGES - 2, LA + LB - 1>(LA + LB - (b_last ? 0 : 1));                    \
-    }                                                                                        \
+    /* at most STAGES-2 later stages' loads in flight: LA + LB per stage, one */           \
+    /* fewer on waves without the last B slot */                                             \
+    wait_loads_le<STAGES - 2, LA + LB - 1>(LA + LB - (b_last ? 0 : 1));                      \
     __builtin_amdgcn_s_waitcnt(0xC07F);                                                      \
     lds_barrier();                                                                           \
-    MOE_DMA_ISSUE_A(kt + DA);                                                                 \
-    MOE_DMA_ISSUE_B(kt + DB);                                                                 \
+    MOE_DMA_ISSUE_A(kt + STAGES - 1);                                                         \
+    MOE_DMA_ISSUE_B(kt + STAGES - 1);                                                         \
     const char* curA = smem + (kt % STAGES) * A_STAGE;                                       \
-    const char* curB = smem + B_RING + (kt % BSTG) * B_STAGE;                                \
+    const char* curB = smem + B_RING + (kt % STAGES) * B_STAGE;                              \
     if constexpr (SCHED) {                                                                   \
       u32x4 fa[2][FM], fb[2][FN];                                                            \
       MOE_DMA_FRAGS(fa[0], fb[0], 0);                                                        \

@@ -26,9 +26,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ constexpr int64_t align_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
-// Row-tile heights for which the permutation builds tile lists.  Index i holds
-// the cumulative m-tile count per group for BM = tile_height(i).  288 = 9
-// fragments: groups of up to 1152 rows in 4 tiles, up to 288 in one.
+// Row-tile heights for which the permutation builds tile lists.  List i < 6
+// holds the cumulative m-tile count per group for BM = tile_height(i) over
+// every group.  288 = 9 fragments: groups of up to 1152 rows in 4 tiles, up to
+// 288 in one.
 constexpr int kNumTileHeights = 6;  // 16, 32, 64, 128, 256, 288
 __host__ __device__ constexpr int tile_height(int i) { return i < 5 ? 16 << i : 288; }
 __host__ __device__ constexpr int tile_height_index(int bm) {
@@ -49,6 +50,20 @@ __host__ __device__ constexpr int group_tiles(int M, int bm) {
   return M <= 0 ? 0 : ceil_div(M, group_tile_rows(M, bm));
 }
 
+// Two more lists split the groups by size, for prefill-shaped batches whose
+// routing leaves some experts a few rows (a skewed load): the groups with at
+// most kSmallGroupRows rows get one 32-row tile each (list kListSmall32), run
+// on the streaming tiles that keep a deep ring of weight loads in flight; the
+// others get 288-row tiles (list kListLarge288).
+constexpr int kSmallGroupRows = 32;
+constexpr int kListLarge288 = kNumTileHeights, kListSmall32 = kNumTileHeights + 1;
+constexpr int kNumTileLists = kNumTileHeights + 2;
+__host__ __device__ constexpr int list_tiles(int list, int M) {
+  return list < kNumTileHeights ? group_tiles(M, tile_height(list))
+         : list == kListLarge288 ? (M > kSmallGroupRows ? group_tiles(M, 288) : 0)
+                                 : (M > kSmallGroupRows ? 0 : group_tiles(M, 32));
+}
+
 // Consecutive tiles of a grouped GEMM's tile order that run on one XCD (see
 // decode_tile); grids are whole multiples of 8 * kXcdChunk blocks.
 constexpr int kXcdChunk = 16;
@@ -57,11 +72,11 @@ inline int xcd_grid(int64_t tiles) {
   return tiles <= 0 ? 0 : (int)((tiles + u - 1) / u * u);
 }
 
-// Down GEMM of groups that average 512 rows or more: 288-row tiles (3 x 4
-// waves of 96 x 64).  A group of 4 x 256 rows plus the few percent that a
+// FP8 / MXFP4 down GEMM of groups that average 512 rows or more: 288-row
+// tiles (3 x 4 waves of 96 x 64).  A group of 4 x 256 rows plus the few percent that a
 // random routing adds to about half of the groups still fits 4 of them, where
 // 256-row tiles would add a fifth row of tiles to those groups and with it a
-// partly filled extra round of blocks over the 256 CUs.  (The up GEMM runs
+// partly filled extra round of blocks over the 256 CUs.  (The bf16 GEMMs run
 // 288-row tiles on every prefill-shaped batch.)
 inline bool tall_down_tiles(int64_t rows_bound, int n_groups) {
   return n_groups > 0 && rows_bound >= (int64_t)512 * n_groups;
@@ -80,7 +95,7 @@ struct Workspace {
   int64_t blockcnt;                    // [nblk*E] i32
   int64_t counts, offsets;             // [E] i32, [E+1] i32
   int64_t groups;                      // [2*G] i32: first rows, then ends
-  int64_t tile_prefix;                 // [kNumTileHeights][G+1] i32
+  int64_t tile_prefix;                 // [kNumTileLists][G+1] i32
   int64_t sorted_tok, sorted_w;        // [P] i32, [R] f32
   int64_t dispatch;                    // [R] i32
   int64_t H, Y;                        // [P*d_ff], [P*d] elements of the layer dtype
@@ -131,7 +146,7 @@ struct ExpertFfnArgs {
   const int32_t* sorted_tok;   // [rows] token of each dispatch row
   const int32_t* g_begin;      // [G] device: first dispatch row of each group
   const int32_t* g_end;        // [G] device: one past its last row
-  const int32_t* tile_prefix;  // [kNumTileHeights][G+1] device
+  const int32_t* tile_prefix;  // [kNumTileLists][G+1] device
   int n_groups;                // G (routed experts + shared)
   int rows_bound;              // host bound on the total number of rows (T*(k+S))
   int routed_groups;           // groups whose weights live in w13/w2 (E)
@@ -158,7 +173,7 @@ struct Fp8FfnArgs {
   const int32_t* sorted_tok;   // [rows]
   const int32_t* g_begin;      // [G]
   const int32_t* g_end;        // [G]
-  const int32_t* tile_prefix;  // [kNumTileHeights][G+1]
+  const int32_t* tile_prefix;  // [kNumTileLists][G+1]
   int n_groups, rows_bound, routed_groups;
   const uint8_t* w13q;         // E4M3: [E, 2*d_ff, d]; MXFP4: [E, 2*d_ff, d/2]
   const void* w13s;            // E4M3: [E, 2*d_ff/128, d/128] float; MXFP4: [E, d/128, 2*d_ff, 4] bytes

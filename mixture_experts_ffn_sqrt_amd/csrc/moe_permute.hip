@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(const int32_t
                                                                    int shared_rows, int32_t* groups,
                                                                    int32_t* tile_prefix,
                                                                    int32_t* sorted_tok) {
-  constexpr int H = kNumTileHeights;
+  constexpr int H = kNumTileLists;
   __shared__ int wave_tot[kScanThreads / 64 * H];
   __shared__ int pass_total[H];
   const int G = E + (shared_rows > 0 ? 1 : 0);
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(const int32_t
     }
     int tiles[H], ex[H];
 #pragma unroll
-    for (int h = 0; h < H; ++h) tiles[h] = g < G ? group_tiles(rows, tile_height(h)) : 0;
+    for (int h = 0; h < H; ++h) tiles[h] = g < G ? list_tiles(h, rows) : 0;
     block_exclusive_scan_n<H>(tiles, ex, wave_tot);
 #pragma unroll
     for (int h = 0; h < H; ++h) {

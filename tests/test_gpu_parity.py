@@ -268,6 +268,36 @@ def test_expert_ffn_and_combine(dtype, T, d, E, k, d_ff):
     assert err.max() <= H.out_tol(dtype), err.max()
 
 
+@pytest.mark.parametrize("d, d_ff", [(256, 256), (320, 128)])
+def test_expert_ffn_mixed_group_sizes(d, d_ff):
+    """A prefill-shaped batch (195 rows per expert on average) whose routing
+    leaves some experts a few rows: groups of 0, 1, 31 and 32 rows take one
+    32-row streaming tile each, groups of 33 rows and more take 288-row tiles
+    (the boundary on both sides, and ragged tails)."""
+    sizes = [0, 1, 31, 32, 33, 64, 300, 1100]
+    E, k, T = len(sizes), 1, sum(sizes)
+    lc = CONFIGS["tiny_fp32"].with_(T=T, d=d, E=E, k=k, d_ff=d_ff, dtype="bf16", seed=31)
+    inp = make_inputs(lc, "cuda")
+    rng = np.random.default_rng(31)
+    ids = rng.permutation(np.repeat(np.arange(E), sizes)).astype(np.int32)[:, None]
+    gates = np.ones((T, k), np.float32)
+    perm = O.permute(ids, gates, E)
+    assert list(perm["counts"]) == sizes
+    c = H.cfg_of(lc)
+    ws = torch.empty(moe.moe_workspace_size(c), dtype=torch.uint8, device="cuda")
+    eo = torch.empty((T * k, d), dtype=lc.torch_dtype, device="cuda")
+    moe.moe_expert_ffn(c, inp["hidden"], dev(perm["sorted_token_ids"]), dev(perm["offsets"]),
+                       inp["w13"], inp["w2"], eo, ws)
+    torch.cuda.synchronize()
+    w13, w2 = to_host_bits(inp["w13"]), to_host_bits(inp["w2"])
+    x = inp["hidden"].double().cpu().numpy()
+    expert_of_row = np.repeat(np.arange(E), perm["counts"])
+    ref_eo = np.stack([O.expert_ffn(x[t], w13[e], w2[e])
+                       for t, e in zip(perm["sorted_token_ids"], expert_of_row)])
+    err = H.row_rel_err(H.to_f64(eo), ref_eo)
+    assert err.max() <= H.out_tol("bf16"), err.max()
+
+
 def test_combine_worked_example(golden):
     g = golden("dispatch_combine_toy.json")
     ids = np.array(g["ids"], np.int32)
