@@ -71,6 +71,15 @@ int small_group_bound(const ExpertFfnArgs& a) {
   return (int)(a.rows_bound < a.n_groups ? a.rows_bound : a.n_groups);
 }
 
+// Whether a prefill-shaped launch splits off the groups of a few rows.  Not
+// when the groups average 512 rows or more (Mixtral's 8 experts): few groups
+// can be that small then, and the launch of the streaming tiles would mostly
+// be empty blocks (about 4.5 us each for GEMM 1 and GEMM 2); the 288-row
+// tiles then take every group.
+bool split_small_groups(const ExpertFfnArgs& a) {
+  return a.rows_bound < (int64_t)512 * a.n_groups;
+}
+
 }  // namespace
 
 int router_splits(const moe_config& c) {
@@ -198,15 +207,17 @@ hipError_t launch_expert_up(const moe_config& c, const ExpertFfnArgs& a, hipStre
       g.a_bytes = (uint32_t)((int64_t)c.T * c.d * es);
       g.b_bytes = (uint32_t)(2 * F * d * es);
       // groups of a few rows: one 32-row streaming tile each
-      GemmArgs gs = g;
-      gs.tile_prefix = a.tile_prefix + kListSmall32 * (a.n_groups + 1);
-      const hipError_t e =
-          launch_gemm_dma<32, 256, 1, 4, EPI_SWIGLU, 4, 128, 3>(gs, small_group_bound(a), s);
-      if (e != hipSuccess) return e;
+      if (split_small_groups(a)) {
+        GemmArgs gs = g;
+        gs.tile_prefix = a.tile_prefix + kListSmall32 * (a.n_groups + 1);
+        const hipError_t e =
+            launch_gemm_dma<32, 256, 1, 4, EPI_SWIGLU, 4, 128, 3>(gs, small_group_bound(a), s);
+        if (e != hipSuccess) return e;
+        g.tile_prefix = a.tile_prefix + kListLarge288 * (a.n_groups + 1);
+      }
       // the others: 288-row tiles (3 x 4 waves of 96 x 64) with the scheduled
       // main loop (Mixtral's up GEMM 1.72 -> 1.67 ms and DeepSeek-V3's 4.52 ->
       // 4.33 ms against 256-row tiles)
-      g.tile_prefix = a.tile_prefix + kListLarge288 * (a.n_groups + 1);
       return launch_gemm_dma<288, 256, 3, 4, EPI_SWIGLU, 2, 128, 3, 1>(g, mb, s);
     }
     default:
@@ -253,16 +264,18 @@ hipError_t launch_expert_down(const moe_config& c, const ExpertFfnArgs& a, hipSt
       g.a_bytes = (uint32_t)((int64_t)a.rows_bound * F * es);
       g.b_bytes = (uint32_t)(d * F * es);
       // groups of a few rows: one 32-row streaming tile each
-      GemmArgs gs = g;
-      gs.n_tiles = ceil_div(c.d, 128);
-      gs.tile_prefix = a.tile_prefix + kListSmall32 * (a.n_groups + 1);
-      const hipError_t e =
-          launch_gemm_dma<32, 128, 1, 2, EPI_STORE, 4, 128, 3>(gs, small_group_bound(a), s);
-      if (e != hipSuccess) return e;
+      if (split_small_groups(a)) {
+        GemmArgs gs = g;
+        gs.n_tiles = ceil_div(c.d, 128);
+        gs.tile_prefix = a.tile_prefix + kListSmall32 * (a.n_groups + 1);
+        const hipError_t e =
+            launch_gemm_dma<32, 128, 1, 2, EPI_STORE, 4, 128, 3>(gs, small_group_bound(a), s);
+        if (e != hipSuccess) return e;
+        g.tile_prefix = a.tile_prefix + kListLarge288 * (a.n_groups + 1);
+      }
       // the others: 288-row tiles with the scheduled main loop (Mixtral's down
       // GEMM 0.88 -> 0.83 ms against the compiler's order)
       g.n_tiles = ceil_div(c.d, 256);
-      g.tile_prefix = a.tile_prefix + kListLarge288 * (a.n_groups + 1);
       return launch_gemm_dma<288, 256, 3, 4, EPI_STORE, 2, 128, 3, 1>(g, mb, s);
     }
     default:
