@@ -34,7 +34,7 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--all", action="store_true", help="also time the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the workload, copy 1 GiB three times (counter calibration)")
     ap.add_argument("--no-peaks", action="store_true",
@@ -123,6 +123,37 @@ def time_gpu(fn, steps, warmup, stream):
     return ev0.elapsed_time(ev1) / steps, wall
 
 
+def step_percentiles(fn, steps, stream):
+    """Each of `steps` further steps timed on its own (HIP events on the launch
+    stream): p10 / p50 / p90 in ms.  Outside the timed region of `value`."""
+    import numpy as np
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    return [round(float(np.percentile(t, q)), 4) for q in (10, 50, 90)]
+
+
+def input_sha256(inp):
+    """SHA-256 of every input buffer's bytes, so that a result can be tied to
+    the exact synthetic inputs whatever generator produced them."""
+    import hashlib
+    import torch
+    out = {}
+    for name in sorted(inp):
+        t = inp[name]
+        if t is None:
+            continue
+        b = t.detach().contiguous().view(torch.uint8).cpu().numpy()
+        out[name] = hashlib.sha256(b.tobytes()).hexdigest()
+    return out
+
+
 def lowp_accounting(lc, counts, kind):
     """Algorithmic work of the low-precision expert GEMM 1 (routed rows): the same
     FLOPs as bf16; bytes = every active expert's w13 codes and scales (FP8: 1
@@ -161,6 +192,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True, with
 
     ms_step, wall = time_gpu(layer.forward, steps, warmup, stream)
     print("[bench] %s: %.3f ms/step" % (name, ms_step), file=sys.stderr, flush=True)
+    pct = step_percentiles(layer.forward, steps, stream)
 
     # staged pieces on the same stream: routing decision of the last step
     ids = layer.ids
@@ -203,6 +235,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True, with
     gemm_tflops = 6 * lc.d * lc.d_ff * T * k / ((ms_up + ms_down) * 1e-3) / 1e12
     res = dict(
         workload=name, ms_per_step=ms_step, tokens_per_s=T / (ms_step * 1e-3), wall_s=wall,
+        step_ms_p10_p50_p90=pct,
         roofline=roof,
         grouped_gemm=dict(ms_up=round(ms_up, 4), ms_down=round(ms_down, 4),
                           tflops=round(gemm_tflops, 1),
@@ -222,6 +255,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True, with
                                  warmup, stream)
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(lc, inp, cpu_seconds)
+        res["input_sha256"] = input_sha256(inp)
     del layer, inp, H, Y, perm
     torch.cuda.empty_cache()
     return res
@@ -401,6 +435,8 @@ def main():
         "grouped_gemm": head["grouped_gemm"],
         "layer": head["layer"],
         "routing": head["routing"],
+        "step_ms_p10_p50_p90": head["step_ms_p10_p50_p90"],
+        "input_sha256": head.get("input_sha256"),
         "fp8": head.get("fp8"),
         "mxfp4": head.get("mxfp4"),
     }
@@ -412,8 +448,8 @@ def main():
             r = run_workload(name, args.steps, args.warmup, False, 0, not args.no_fp8,
                              not args.no_mxfp4)
             others[name] = {kk: r.get(kk) for kk in ("ms_per_step", "tokens_per_s", "roofline",
-                                                      "grouped_gemm", "layer", "routing", "fp8",
-                                                      "mxfp4")}
+                                                      "grouped_gemm", "layer", "routing",
+                                                      "step_ms_p10_p50_p90", "fp8", "mxfp4")}
         line["workloads"] = others
     if not args.no_peaks:
         line["context"] = peaks()
