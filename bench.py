@@ -7,7 +7,11 @@ inputs already resident in HBM.  Prints ONE JSON line with tokens/s, the
 roofline of the dominant kernel (grouped GEMM 1 + SwiGLU), and the CPU oracle
 timed on a bounded sample of the same workload.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--all] [--no-decode]
+
+Beside the headline workload the line carries the decode-shaped workload
+("decode": its grouped GEMM 1 against HBM bandwidth), or every workload
+with --all.
 """
 import argparse
 import json
@@ -20,6 +24,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s + grouped-GEMM % bf16 MFMA peak (prefill), % HBM BW (decode)"
 DEFAULT_WORKLOAD = "mixtral_prefill"  # T=4096, d=4096, E=8, top-2, d_ff=14336, bf16
+DECODE_WORKLOAD = "v4flash_decode"    # T=64, d=4096, E=256+1, top-6, d_ff=2048, bf16
 
 # MI355X published peaks
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8": 5000.0}  # dense MFMA
@@ -33,6 +38,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--all", action="store_true", help="also time the other workloads")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-shaped workload reported beside the headline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -440,6 +447,13 @@ def main():
         "fp8": head.get("fp8"),
         "mxfp4": head.get("mxfp4"),
     }
+    keep = ("ms_per_step", "tokens_per_s", "roofline", "grouped_gemm", "layer", "routing",
+            "step_ms_p10_p50_p90", "fp8", "mxfp4")
+    if not args.all and not args.no_decode and args.workload != DECODE_WORKLOAD:
+        # the metric's second half: decode-shaped batches against HBM bandwidth
+        r = run_workload(DECODE_WORKLOAD, args.steps, args.warmup, False, 0, not args.no_fp8,
+                         not args.no_mxfp4)
+        line["decode"] = dict({kk: r.get(kk) for kk in keep}, workload=DECODE_WORKLOAD)
     if args.all:
         others = {}
         for name in CONFIGS:
@@ -447,9 +461,7 @@ def main():
                 continue
             r = run_workload(name, args.steps, args.warmup, False, 0, not args.no_fp8,
                              not args.no_mxfp4)
-            others[name] = {kk: r.get(kk) for kk in ("ms_per_step", "tokens_per_s", "roofline",
-                                                      "grouped_gemm", "layer", "routing",
-                                                      "step_ms_p10_p50_p90", "fp8", "mxfp4")}
+            others[name] = {kk: r.get(kk) for kk in keep}
         line["workloads"] = others
     if not args.no_peaks:
         line["context"] = peaks()
