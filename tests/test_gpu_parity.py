@@ -226,19 +226,19 @@ def test_permute_random(T, k, E, mode):
 @pytest.mark.parametrize("dtype, T, d, E, k, d_ff", [
     ("f32", 16, 64, 8, 2, 128),
     ("f32", 50, 128, 5, 3, 192),
-    ("bf16", 300, 256, 5, 2, 192),     # ~120 rows/expert: square tiles, ragged tails
+    ("bf16", 300, 256, 5, 2, 192),     # ~120 rows/expert, d_ff not a multiple of 128: 128-row tiles
     ("bf16", 40, 256, 64, 6, 128),     # ~4 rows/expert: 32-row streaming tiles
     ("bf16", 200, 256, 16, 2, 256),    # ~25 rows/expert: 32-row tiles, some experts span two
     ("bf16", 40, 256, 64, 6, 192),     # ~4 rows/expert, d_ff not a multiple of 128: 16-row tiles
     ("bf16", 1, 512, 16, 4, 256),      # single token
     ("bf16", 700, 128, 3, 3, 64),      # k = E: every expert gets every token
-    ("bf16", 700, 320, 4, 2, 256),     # 256x256 tiles: ragged rows, partial last column tile
-    ("bf16", 2000, 512, 8, 2, 384),    # 256x256 tiles, several row tiles per expert
-    ("bf16", 2100, 320, 4, 2, 256),    # ~1050 rows per expert: 288x256 down tiles, partial column
-    ("bf16", 1300, 256, 2, 1, 128),    # ~650 rows per expert: 288-row down tiles, ragged last tile
-    ("bf16", 600, 64, 4, 2, 128),      # 256x256 tiles with K shorter than the weight ring:
+    ("bf16", 700, 320, 4, 2, 256),     # prefill (288x256) tiles: ragged rows, partial last column tile
+    ("bf16", 2000, 512, 8, 2, 384),    # prefill tiles, several row tiles per expert
+    ("bf16", 2100, 320, 4, 2, 256),    # ~1050 rows per expert: 4 row tiles each, partial column
+    ("bf16", 1300, 256, 2, 1, 128),    # ~650 rows per expert: 3 row tiles each, ragged last tile
+    ("bf16", 600, 64, 4, 2, 128),      # prefill tiles with K shorter than the LDS ring:
                                        # one K stage up, two down, partial column tile
-    ("bf16", 900, 128, 3, 2, 128),     # two K stages up; 288-row down tiles
+    ("bf16", 900, 128, 3, 2, 128),     # two K stages up
 ])
 def test_expert_ffn_and_combine(dtype, T, d, E, k, d_ff):
     lc = CONFIGS["tiny_fp32"].with_(T=T, d=d, E=E, k=k, d_ff=d_ff, dtype=dtype, seed=23)
@@ -337,6 +337,9 @@ SMALL_LAYERS = {
     "decode_T1": CONFIGS["v4flash_decode"].with_(T=1, d=256, d_ff=128),
     # 512 rows per expert: the down GEMM runs 288-row tiles
     "mixtral_tall_tiles": CONFIGS["mixtral_prefill"].with_(T=2048, d=256, d_ff=256),
+    # 128 rows per expert on average with a skewed load: the experts with at
+    # most 32 rows run on streaming tiles, the others on 288-row tiles
+    "v4pro_skew_split": CONFIGS["v4pro_skew_prefill"].with_(T=1024, d=256, E=32, k=4, d_ff=128),
 }
 
 
@@ -409,7 +412,7 @@ def test_forward_full_size_sampled(name):
 # MoE reduction order is fixed, no split-K whose split depends on the batch)
 # ----------------------------------------------------------------------------
 BATCH_INVARIANT = {
-    # the full batch runs 256x256 tiles, the slices 32-row tiles
+    # the full batch runs 288-row prefill tiles, the slices 32-row tiles
     "mixtral_small": CONFIGS["mixtral_prefill"].with_(T=512, d=512, d_ff=1024),
     "dsv3_groups_shared": CONFIGS["dsv3_prefill"].with_(T=1024, d=256, E=16, k=4, d_ff=128,
                                                         n_group=4, topk_group=2, group_topk=2),
@@ -421,6 +424,9 @@ BATCH_INVARIANT = {
                                                        n_group=8, topk_group=4, group_topk=2),
     # the full batch's down GEMM runs 288-row tiles (512 rows per expert)
     "mixtral_tall_tiles": CONFIGS["mixtral_prefill"].with_(T=2048, d=256, d_ff=256),
+    # the full batch runs its small experts on streaming tiles, the rest on
+    # 288-row tiles
+    "v4pro_skew_split": CONFIGS["v4pro_skew_prefill"].with_(T=1024, d=256, E=32, k=4, d_ff=128),
 }
 
 
