@@ -191,10 +191,10 @@ int tile_bound8(int64_t rows, int groups, int bm) {
 }
 
 // 32-row streaming tiles when experts have a few rows each (decode), else
-// 256x256 tiles (288x256 for the down GEMM of large groups, the rule of the
-// bf16 down GEMM; the up GEMM stays at 256 rows, where the bf16 one takes 288:
-// 288-row FP8 up tiles measured 1.5% faster to 5% slower across the prefill
-// shapes).  The decode tiles keep
+// 256x256 tiles (288x256 for the down GEMM of large groups; 128x256 for the
+// other MXFP4 GEMMs, two blocks per CU; the E4M3 up GEMM stays at 256 rows, where
+// the bf16 one takes 288: 288-row E4M3 up tiles measured 1.5% faster to 5%
+// slower across the prefill shapes).  The decode tiles keep
 // short LDS rings (2-3 stages, 40-80 KB) so that two to four blocks share a CU
 // and one block's pipeline fill and epilogue overlap another's streaming:
 // measured faster than one block per CU with a 4-12 stage ring.
@@ -283,11 +283,21 @@ hipError_t launch_expert_up_fp8(const moe_config& c, const Fp8FfnArgs& a, hipStr
     return mx ? launch_fp8<32, 256, 1, 4, EPI_SWIGLU8, 3, WF_MXFP4>(q, mt, s)
               : launch_fp8<32, 256, 1, 4, EPI_SWIGLU8, 2>(q, mt, s);
   }
+  if (mx) {
+    // 128x256 tiles (8 waves of 64 x 64) in two 34 KB stages, so that two
+    // blocks share a CU and one block's SwiGLU + FP8-cast epilogue (VALU work
+    // with the matrix cores idle) overlaps the other's main loop: up GEMM
+    // V4-Pro 4.42 -> 3.97 ms, Mixtral 0.97 -> 0.92 ms, DeepSeek-V3 2.23 ->
+    // 2.07 ms against one block of 256x256 per CU.  (An E4M3 tile of the same
+    // shape needs 100 KB: one block per CU.)
+    g.tile_prefix = a.tile_prefix + tile_height_index(128) * (a.n_groups + 1);
+    return launch_fp8<128, 256, 2, 4, EPI_SWIGLU8, 2, WF_MXFP4>(
+        q, tile_bound8(a.rows_bound, a.n_groups, 128), s);
+  }
   g.tile_prefix = a.tile_prefix + tile_height_index(256) * (a.n_groups + 1);
   const int mt = tile_bound8(a.rows_bound, a.n_groups, 256);
-  // scheduled main loop (MXFP4 up GEMMs 1-3% faster, FP8 0-2%)
-  return mx ? launch_fp8<256, 256, 4, 2, EPI_SWIGLU8, 3, WF_MXFP4, 1>(q, mt, s)
-            : launch_fp8<256, 256, 4, 2, EPI_SWIGLU8, 2, WF_E4M3, 1>(q, mt, s);
+  // scheduled main loop (0-2% faster)
+  return launch_fp8<256, 256, 4, 2, EPI_SWIGLU8, 2, WF_E4M3, 1>(q, mt, s);
 }
 
 hipError_t launch_expert_down_fp8(const moe_config& c, const Fp8FfnArgs& a, hipStream_t s) {
@@ -332,13 +342,20 @@ hipError_t launch_expert_down_fp8(const moe_config& c, const Fp8FfnArgs& a, hipS
     return mx ? launch_fp8<288, 256, 3, 4, EPI_STORE, 2, WF_MXFP4>(q, mt, s)
               : launch_fp8<288, 256, 3, 4, EPI_STORE, 2>(q, mt, s);
   }
+  if (mx) {
+    // 128x256 tiles, two blocks per CU as for the up GEMM: DeepSeek-V3's down
+    // GEMM 1.24 -> 1.14 ms, V4-Pro's 2.31 -> 2.08 ms (not for the large
+    // groups above: Mixtral's 288-row tiles 0.42 ms, 128-row 0.46 ms)
+    g.tile_prefix = a.tile_prefix + tile_height_index(128) * (a.n_groups + 1);
+    return launch_fp8<128, 256, 2, 4, EPI_STORE, 2, WF_MXFP4>(
+        q, tile_bound8(a.rows_bound, a.n_groups, 128), s);
+  }
   g.tile_prefix = a.tile_prefix + tile_height_index(256) * (a.n_groups + 1);
   const int mt = tile_bound8(a.rows_bound, a.n_groups, 256);
   // scheduled main loop (within 1%; the 288-row tiles above keep the
   // compiler's order: their double-buffered fragments would not fit in the
   // registers of three waves per SIMD)
-  return mx ? launch_fp8<256, 256, 4, 4, EPI_STORE, 3, WF_MXFP4, 1>(q, mt, s)
-            : launch_fp8<256, 256, 4, 4, EPI_STORE, 2, WF_E4M3, 1>(q, mt, s);
+  return launch_fp8<256, 256, 4, 4, EPI_STORE, 2, WF_E4M3, 1>(q, mt, s);
 }
 
 }  // namespace moe

@@ -76,8 +76,9 @@ def _dev(a):
 
 @pytest.mark.parametrize("T, d, E, k, d_ff", [
     (40, 256, 16, 4, 256),      # a few rows per expert: 32-row streaming tiles
-    (700, 256, 4, 2, 384),      # 256x256 tiles, ragged rows per expert
+    (700, 256, 4, 2, 384),      # 128x256 tiles (two blocks per CU), ragged rows per expert
     (300, 384, 3, 3, 128),      # k = E, d not a multiple of 256 (partial column tile)
+    (1100, 256, 8, 2, 256),     # ~275 rows per expert: three 128-row tiles, a ragged third
     (1, 512, 8, 2, 256),        # one token
     (2100, 384, 4, 2, 128),     # ~1050 rows per expert: 288x256 down tiles, partial column tile
     (1300, 256, 2, 1, 128),     # ~650 rows per expert: 288-row down tiles, ragged last row tile
