@@ -236,9 +236,11 @@ def test_forward_mxfp4_full_size_sampled(name, n_rows):
     check_layer_mx(lc, inp, out, layer.ids, layer.gates, rows=np.sort(rows))
 
 
-@pytest.mark.parametrize("name", ["mixtral_small", "mixtral_tall_tiles"])
+@pytest.mark.parametrize("name", ["mixtral_small", "mixtral_tall_tiles", "dsv3_groups_shared"])
 def test_forward_mxfp4_batch_invariant(name):
-    # mixtral_tall_tiles: the full batch's down GEMM runs 288-row tiles
+    # mixtral_tall_tiles: the full batch's down GEMM runs 288-row tiles;
+    # dsv3_groups_shared: both of its GEMMs run 128-row tiles (two blocks per
+    # CU), the slices 32-row tiles
     lc = MX_LAYERS[name]
     inp = make_inputs(lc, "cuda")
     mx = moe.quantize_mxfp4_weights(inp)
