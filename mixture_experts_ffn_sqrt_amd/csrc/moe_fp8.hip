@@ -19,6 +19,12 @@
 
 namespace moe {
 namespace {
+
+// workgroups of a grid-strided quantizer launch (256 per CU)
+constexpr int64_t kQuantizeMaxGrid = 65536;
+// most workgroups of 256 threads in one dispatch (2^32 work-items)
+constexpr int64_t kMaxWorkgroups256 = (int64_t)1 << 24;
+
 using namespace gemm;
 
 template <typename TIn>
@@ -119,29 +125,36 @@ __device__ __forceinline__ int mx_scale_exp(float amax) {
 // 16 lanes per 32-element block (two elements each, one output byte), four
 // blocks per wavefront, blocks numbered over the row-major [n_mat * R, C]
 // input (a row's C/32 blocks are consecutive).  Scale of block b of row r of
-// matrix m goes to scales[m][b / 4][r][b % 4].
+// matrix m goes to scales[m][b / 4][r][b % 4].  A workgroup takes 16 blocks
+// per pass and strides over the grid: a dispatch's work-item count is 32-bit,
+// and all the experts' weights of a large layer (384 x 6144 x 7168 elements)
+// would need more work-items than that at one thread per two elements.
 template <typename TIn>
 __global__ __launch_bounds__(256) void quantize_mxfp4_kernel(int64_t nblocks, int R, int C,
                                                              const TIn* w, uint8_t* q,
                                                              uint8_t* scales) {
   const int lane = threadIdx.x & 63, sub = lane & 15;
-  const int64_t blk = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
-  const bool ok = blk < nblocks;
-  const int64_t base = blk * 32 + 2 * sub;
-  const float v0 = ok ? load_in(w, base) : 0.0f, v1 = ok ? load_in(w, base + 1) : 0.0f;
-  float m = fmaxf(fabsf(v0), fabsf(v1));
+  const int GB = C / 32;
+  // the pass condition is the same for the whole workgroup, so every lane of
+  // a 16-lane group takes part in its shuffles
+  for (int64_t pass = blockIdx.x; pass * 16 < nblocks; pass += gridDim.x) {
+    const int64_t blk = (pass * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+    const bool ok = blk < nblocks;
+    const int64_t base = blk * 32 + 2 * sub;
+    const float v0 = ok ? load_in(w, base) : 0.0f, v1 = ok ? load_in(w, base + 1) : 0.0f;
+    float m = fmaxf(fabsf(v0), fabsf(v1));
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
-  if (!ok) return;
-  const int e = mx_scale_exp(m);
-  const float inv = ldexpf(1.0f, -e);
-  q[base / 2] = (uint8_t)(e2m1_code(v0 * inv) | (e2m1_code(v1 * inv) << 4));
-  if (sub == 0) {
-    const int GB = C / 32;
-    const int64_t row = blk / GB;  // over all matrices
-    const int b = (int)(blk - row * GB);
-    const int64_t m = row / R, r = row - m * R;
-    scales[((m * (C / 128) + b / 4) * R + r) * 4 + (b & 3)] = (uint8_t)(e + 127);
+    for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+    if (!ok) continue;
+    const int e = mx_scale_exp(m);
+    const float inv = ldexpf(1.0f, -e);
+    q[base / 2] = (uint8_t)(e2m1_code(v0 * inv) | (e2m1_code(v1 * inv) << 4));
+    if (sub == 0) {
+      const int64_t row = blk / GB;  // over all matrices
+      const int b = (int)(blk - row * GB);
+      const int64_t mat = row / R, r = row - mat * R;
+      scales[((mat * (C / 128) + b / 4) * R + r) * 4 + (b & 3)] = (uint8_t)(e + 127);
+    }
   }
 }
 
@@ -208,6 +221,7 @@ hipError_t launch_quantize_rows(int n, int K, int in_dtype, const void* x, uint8
                                 float* scales, hipStream_t s) {
   const int64_t jobs = (int64_t)n * ((K + 511) / 512);
   if (jobs == 0) return hipSuccess;
+  if ((jobs + 3) / 4 > kMaxWorkgroups256) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((jobs + 3) / 4));
   if (in_dtype == MOE_F32)
     hipLaunchKernelGGL(quantize_rows_kernel<float>, grid, dim3(256), 0, s, n, K,
@@ -222,7 +236,8 @@ hipError_t launch_quantize_mxfp4(int n_mat, int R, int C, int in_dtype, const vo
                                  uint8_t* scales, hipStream_t s) {
   const int64_t nblocks = (int64_t)n_mat * R * (C / 32);
   if (nblocks == 0) return hipSuccess;
-  const dim3 grid((unsigned)((nblocks + 15) / 16));
+  const int64_t passes = (nblocks + 15) / 16;
+  const dim3 grid((unsigned)(passes < kQuantizeMaxGrid ? passes : kQuantizeMaxGrid));
   if (in_dtype == MOE_F32)
     hipLaunchKernelGGL(quantize_mxfp4_kernel<float>, grid, dim3(256), 0, s, nblocks, R, C,
                        static_cast<const float*>(w), q, scales);
@@ -236,6 +251,7 @@ hipError_t launch_quantize_blocks(int R, int C, int in_dtype, const void* w, uin
                                   float* scales, hipStream_t s) {
   const int64_t tiles = (int64_t)(R / 128) * (C / 128);
   if (tiles == 0) return hipSuccess;
+  if (tiles > kMaxWorkgroups256) return hipErrorInvalidConfiguration;
   if (in_dtype == MOE_F32)
     hipLaunchKernelGGL(quantize_blocks_kernel<float>, dim3((unsigned)tiles), dim3(256), 0, s, R,
                        C, static_cast<const float*>(w), q, scales);

@@ -120,3 +120,12 @@ def check_routing(ids, gates, ref_ids, ref_gates, margin, keys=None, tie=TIE_GIV
             b = np.sort(keys[t, ref_ids[t]])
             assert np.all(np.abs(a - b) <= tie * 4)
     return int((~ok).sum())
+
+
+def hot_cold_rows(ids, counts, n=2):
+    """Token rows routed to the expert with the most rows and to the expert with
+    the fewest (but some) rows: on a skewed workload the first runs on the
+    288-row tiles, the second on the small-group streaming tiles."""
+    hot = int(np.argmax(counts))
+    cold = int(np.argmin(np.where(counts > 0, counts, counts.max() + 1)))
+    return np.r_[np.nonzero((ids == hot).any(1))[0][:n], np.nonzero((ids == cold).any(1))[0][:n]]

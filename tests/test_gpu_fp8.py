@@ -231,7 +231,8 @@ def test_forward_fp8_hash_pass():
 
 
 @pytest.mark.parametrize("name, n_rows", [("mixtral_prefill", 24), ("v4flash_decode", 6),
-                                          ("dsv3_prefill", 6)])
+                                          ("dsv3_prefill", 6),
+                                          ("v4pro_skew_prefill", 6)])
 def test_forward_fp8_full_size_sampled(name, n_rows):
     lc = CONFIGS[name]
     inp = make_inputs(lc, "cuda")
@@ -240,6 +241,10 @@ def test_forward_fp8_full_size_sampled(name, n_rows):
     out = layer.forward_fp8(fp8)
     torch.cuda.synchronize()
     rows = np.random.default_rng(5).choice(lc.T, n_rows, replace=False)
+    if lc.zipf_s > 0:  # the hottest expert's rows and a cold (streaming-tile) expert's
+        ids_np = layer.ids.cpu().numpy()
+        counts = np.bincount(ids_np.ravel(), minlength=lc.E)
+        rows = np.unique(np.r_[rows, H.hot_cold_rows(ids_np, counts)])
     check_layer_fp8(lc, inp, out, layer.ids, layer.gates, rows=np.sort(rows))
 
 

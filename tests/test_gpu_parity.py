@@ -400,8 +400,7 @@ def test_forward_full_size_sampled(name):
     n = min(T, 16 if lc.d * lc.d_ff < 2e7 else 8)
     rows = np.sort(rng.choice(T, n, replace=False))
     if lc.zipf_s > 0:  # include the token rows of the hottest expert and of a cold one
-        hot = int(np.argmax(counts))
-        rows = np.unique(np.r_[rows, np.nonzero((ids_np == hot).any(1))[0][:2]])
+        rows = np.unique(np.r_[rows, H.hot_cold_rows(ids_np, counts)])
     res = H.check_layer(lc, inp, out, ids, gates, rows=rows, max_tie_frac=0.2)
     assert res["rows"] - res["ties"] >= n // 2
 
