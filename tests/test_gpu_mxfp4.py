@@ -70,6 +70,21 @@ def test_quantize_mxfp4_expert_stack_bit_exact():
         assert np.array_equal(q[e], rq), e
 
 
+def test_quantize_mxfp4_grid_stride_bit_exact():
+    # 5 x 1663 x 132 = 1 097 580 blocks: more than one pass of the capped grid
+    # (65 536 workgroups x 16 blocks), and a last pass that ends inside a
+    # workgroup; each matrix's scale table still lands in its own place
+    g = torch.Generator().manual_seed(43)
+    w = (torch.randn((5, 1663, 4224), generator=g) * 0.02).to(torch.bfloat16)
+    w[4, -1, -32:] = 0.0                                 # the very last block all zero
+    w[3, :, :128] *= 300
+    q, s = gpu_mx(w.cuda())
+    for e in range(5):
+        rq, rs = O.quantize_mxfp4(to_host_bits(w[e]))
+        assert np.array_equal(s[e], kmajor(rs)), e
+        assert np.array_equal(q[e], rq), e
+
+
 def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
