@@ -118,12 +118,16 @@ constexpr int kSuperRows = 8;
 // contiguous run per XCD: XCD x takes tiles x*q + min(x, r) + b/8 (q, r: the
 // tile count divided by 8), measured 4% faster there than chunks.  (The grid
 // is a whole number of 8 * kXcdChunk blocks; blocks past the tiles exit.)
+//
+// `vbid` (default: the block index) lets a persistent block walk the tiles of
+// blocks vbid, vbid + gridDim.x, ...; with a grid of a multiple of 8 blocks
+// each of those runs on the XCD the mapping assumes.
 template <int BM>
-__device__ __forceinline__ bool decode_tile(const GemmArgs& p, TileCoord& tc) {
+__device__ __forceinline__ bool decode_tile(const GemmArgs& p, TileCoord& tc, int vbid = -1) {
   const int nt_all = p.n_tiles;
   const int total_m = p.g_begin ? p.tile_prefix[p.G] : group_tiles(p.dense_rows, BM);
   const int nact = total_m * nt_all;
-  const int bid = blockIdx.x, i = bid >> 3, xcd = bid & 7;
+  const int bid = vbid < 0 ? (int)blockIdx.x : vbid, i = bid >> 3, xcd = bid & 7;
   int logical;
   if constexpr (BM > 32) {
     logical = ((i / kXcdChunk) * 8 + xcd) * kXcdChunk + i % kXcdChunk;
@@ -445,10 +449,11 @@ __device__ __forceinline__ void sched_stage() {
   __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
 }
 
+// One tile of grouped_gemm_dma (below).
 // SCHED = 1: fragments double-buffered in registers across the k-steps of a
 // stage, in the order sched_stage fixes (full tiles only).
-template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int ROWB, int SWZ, int SCHED = 0>
-__global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) {
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int ROWB, int SWZ, int SCHED>
+__device__ __forceinline__ void gemm_dma_tile(const GemmArgs& p, const TileCoord& tc) {
   constexpr int NT = 64 * WM * WN, NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -471,8 +476,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
   static_assert(STAGES >= 2 && B_RING + STAGES * B_STAGE <= 160 * 1024, "LDS budget");
   extern __shared__ __align__(16) char smem[];
 
-  TileCoord tc;
-  if (!decode_tile<BM>(p, tc)) return;
   // the wavefront index is uniform: say so, so that everything derived from it
   // (LDS bases, fragment liveness) lives in scalar registers
   const int tid = threadIdx.x, lane = tid & 63;
@@ -665,6 +668,26 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
   }
 }
 
+// Direct-to-LDS grouped GEMM: one tile per block, or (PERSIST = 1, a grid of a
+// multiple of 8 blocks smaller than the tile count) each block takes the
+// tiles of blocks b, b + gridDim.x, ... in turn, so that the launch occupies
+// at most gridDim.x CUs.  Every wave sees the same tile sequence; the barrier
+// between tiles keeps the next tile's first LDS loads from landing in a stage
+// another wave still reads.
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int ROWB, int SWZ, int SCHED = 0,
+          int PERSIST = 0>
+__global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) {
+  TileCoord tc;
+  if constexpr (PERSIST) {
+    for (int vb = blockIdx.x; decode_tile<BM>(p, tc, vb); vb += gridDim.x) {
+      if (vb != (int)blockIdx.x) __syncthreads();
+      gemm_dma_tile<BM, BN, WM, WN, EPI, STAGES, ROWB, SWZ, SCHED>(p, tc);
+    }
+  } else {
+    if (!decode_tile<BM>(p, tc)) return;
+    gemm_dma_tile<BM, BN, WM, WN, EPI, STAGES, ROWB, SWZ, SCHED>(p, tc);
+  }
+}
 
 }  // namespace gemm
 }  // namespace moe

@@ -340,6 +340,11 @@ SMALL_LAYERS = {
     # 128 rows per expert on average with a skewed load: the experts with at
     # most 32 rows run on streaming tiles, the others on 288-row tiles
     "v4pro_skew_split": CONFIGS["v4pro_skew_prefill"].with_(T=1024, d=256, E=32, k=4, d_ff=128),
+    # about 70 experts of at most 32 rows x 8 column tiles: the up GEMM's
+    # streaming launch (64 persistent blocks beside the 288-row tiles) walks
+    # several tiles per block
+    "v4pro_skew_many_small": CONFIGS["v4pro_skew_prefill"].with_(T=4096, d=256, E=128, k=6,
+                                                                 d_ff=1024),
 }
 
 
@@ -426,6 +431,9 @@ BATCH_INVARIANT = {
     # the full batch runs its small experts on streaming tiles, the rest on
     # 288-row tiles
     "v4pro_skew_split": CONFIGS["v4pro_skew_prefill"].with_(T=1024, d=256, E=32, k=4, d_ff=128),
+    # the full batch runs the small groups on the persistent streaming launch
+    "v4pro_skew_many_small": CONFIGS["v4pro_skew_prefill"].with_(T=4096, d=256, E=128, k=6,
+                                                                 d_ff=1024),
 }
 
 
