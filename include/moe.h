@@ -25,10 +25,16 @@
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers on the current HIP device, row-major
  *    and contiguous, 16-byte aligned.  Outputs must not alias inputs.  The caller
- *    owns all memory, including the workspace; the library never allocates,
- *    frees or synchronises.  Work is queued on `stream` (a hipStream_t; NULL is
- *    the default stream) and completes asynchronously.  No global mutable state:
- *    calls with distinct workspaces may run concurrently.
+ *    owns all memory, including the workspace; the library never allocates
+ *    device memory, frees or synchronises.  Work is queued on `stream` (a
+ *    hipStream_t; NULL is the default stream) and completes asynchronously.
+ *    Calls with distinct workspaces may run concurrently.
+ *  - Part of the bf16 up GEMM of a prefill-shaped batch (the experts with at
+ *    most 32 rows) may run on a second stream that the library creates per
+ *    device on first use (default priority; kept, with two events, until the
+ *    process ends).  Events order it after the work queued on `stream` before
+ *    the call and before the work queued on `stream` after it, so the call
+ *    behaves as if queued on `stream` alone.
  *  - Floating-point tensors (hidden, weights, expert outputs, out) are float32
  *    when cfg->dtype == MOE_F32 and bfloat16 when MOE_BF16.  Logits, gates, bias
  *    and logit offsets are always float32; accumulation is always float32.
