@@ -437,6 +437,29 @@ BATCH_INVARIANT = {
 }
 
 
+def test_forward_on_a_caller_stream():
+    # the up GEMM runs its small groups on a stream of the library's own,
+    # forked from and joined to the caller's: on a non-default caller stream,
+    # three calls in a row (sharing one workspace) whose outputs are copied on
+    # that stream right after each call, with no host synchronisation between
+    # them, equal the default stream's result bitwise
+    lc = SMALL_LAYERS["v4pro_skew_many_small"]
+    inp = make_inputs(lc, "cuda")
+    ref = [t.clone() for t in H.gpu_forward(H.cfg_of(lc), inp)]
+    layer = moe.MoELayer(H.cfg_of(lc), inp)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    got = []
+    with torch.cuda.stream(st):
+        for _ in range(3):
+            layer.forward()
+            got.append([layer.out.clone(), layer.ids.clone(), layer.gates.clone()])
+    st.synchronize()
+    for outs in got:
+        for a, b in zip(outs, ref):
+            assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("name", list(BATCH_INVARIANT))
 def test_forward_batch_invariant(name):
     lc = BATCH_INVARIANT[name]
