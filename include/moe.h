@@ -29,12 +29,8 @@
  *    device memory, frees or synchronises.  Work is queued on `stream` (a
  *    hipStream_t; NULL is the default stream) and completes asynchronously.
  *    Calls with distinct workspaces may run concurrently.
- *  - Part of the bf16 up GEMM of a prefill-shaped batch (the experts with at
- *    most 32 rows) may run on a second stream that the library creates per
- *    device on first use (default priority; kept, with two events, until the
- *    process ends).  Events order it after the work queued on `stream` before
- *    the call and before the work queued on `stream` after it, so the call
- *    behaves as if queued on `stream` alone.
+ *  - The library keeps no state between calls: no streams, events, handles
+ *    or memory of its own.  Every launch of a call goes to `stream`, in order.
  *  - Floating-point tensors (hidden, weights, expert outputs, out) are float32
  *    when cfg->dtype == MOE_F32 and bfloat16 when MOE_BF16.  Logits, gates, bias
  *    and logit offsets are always float32; accumulation is always float32.

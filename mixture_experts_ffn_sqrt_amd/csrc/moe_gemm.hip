@@ -24,8 +24,6 @@
 // grouped_gemm_staged (any element type): global -> registers -> LDS, two
 // stages, MFMA 16x16; the router GEMM (split over K), the fp32 configurations
 // and shapes the buffer-load kernel does not take.
-#include <mutex>
-
 #include "moe_gemm_kernels.h"
 
 namespace moe {
@@ -46,20 +44,14 @@ hipError_t launch_gemm(GemmArgs p, int m_tiles_bound, hipStream_t s, int splits 
   return hipGetLastError();
 }
 
-// Direct-to-LDS bf16 kernel (ST LDS buffers of ROWB/2 K-elements).  With
-// PERSIST, at most max_blocks (a multiple of 8) blocks walk the tiles.
-template <int BM, int BN, int WM, int WN, int EPI, int ST, int ROWB, int SWZ, int SCHED = 0,
-          int PERSIST = 0>
-hipError_t launch_gemm_dma(GemmArgs p, int m_tiles_bound, hipStream_t s, int max_blocks = 0) {
+// Direct-to-LDS bf16 kernel (ST LDS buffers of ROWB/2 K-elements).
+template <int BM, int BN, int WM, int WN, int EPI, int ST, int ROWB, int SWZ, int SCHED = 0>
+hipError_t launch_gemm_dma(GemmArgs p, int m_tiles_bound, hipStream_t s) {
   constexpr int NT = 64 * WM * WN;
   constexpr int LDS = ST * (BM + BN) * ROWB;
-  int grid = xcd_grid((int64_t)m_tiles_bound * p.n_tiles);
+  const int grid = xcd_grid((int64_t)m_tiles_bound * p.n_tiles);
   if (grid <= 0) return hipSuccess;
-  if (PERSIST) {
-    if (max_blocks <= 0 || max_blocks % 8) return hipErrorInvalidValue;
-    grid = grid < max_blocks ? grid : max_blocks;
-  }
-  auto kern = grouped_gemm_dma<BM, BN, WM, WN, EPI, ST, ROWB, SWZ, SCHED, PERSIST>;
+  auto kern = grouped_gemm_dma<BM, BN, WM, WN, EPI, ST, ROWB, SWZ, SCHED>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   if (e != hipSuccess) return e;
@@ -88,71 +80,27 @@ bool split_small_groups(const ExpertFfnArgs& a) {
   return a.rows_bound < (int64_t)512 * a.n_groups;
 }
 
-// Blocks of the small groups' streaming launch when it runs beside the
-// 288-row tiles of the up GEMM (a multiple of 8; one block per CU).  V4-Pro's
-// up GEMM (127 groups of at most 32 rows): 9.11 ms with the two launches in
-// sequence, 8.61 ms beside them on 64 blocks (8.77 on 32, 8.69 on 128).
-#ifndef MOE_SMALL_GROUP_BLOCKS
-#define MOE_SMALL_GROUP_BLOCKS 64
-#endif
+// Blocks that walk the small groups' streaming tiles when they share the up
+// GEMM's launch with the 288-row tiles (a multiple of 8; one block per CU).
+// V4-Pro's up GEMM (127 groups of at most 32 rows): 9.11 ms with the two
+// kinds of tile in two launches in sequence, 8.61 ms with the streaming tiles
+// on 64 CUs beside the 288-row tiles (8.77 on 32, 8.69 on 128).
+constexpr int kSmallGroupBlocks = 64;
 
-// A second stream per device (default priority, created on first use and kept
-// until the process ends) and the two events that fork it from and join it to
-// the caller's stream.  The mutex keeps one fork/join sequence of host calls
-// together when several host threads use the same device.
-struct SideStream {
-  std::mutex mu;
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-constexpr int kMaxDevices = 64;
-
-SideStream* side_stream() {
-  static SideStream side[kMaxDevices];
-  static std::mutex init_mu;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  std::lock_guard<std::mutex> lk(init_mu);
-  SideStream& ss = side[dev];
-  if (!ss.stream) {
-    hipStream_t st = nullptr;
-    hipEvent_t f = nullptr, j = nullptr;
-    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
-      (void)hipStreamDestroy(st);
-      if (f) (void)hipEventDestroy(f);
-      return nullptr;
-    }
-    ss.fork = f;
-    ss.join = j;
-    ss.stream = st;
-  }
-  return &ss;
-}
-
-// Launches `side_work` (the small groups' streaming tiles: HBM-bound, on a
-// few CUs) on the device's side stream first, then `main_work` (the 288-row
-// tiles: MFMA-bound) on s, which gets the other CUs at once; s then waits for
-// both.  The launches write disjoint output rows, so the results are those of
-// running them in sequence.  Without a side stream both run in sequence on s.
-template <class SideWork, class MainWork>
-hipError_t fork_join(hipStream_t s, SideWork side_work, MainWork main_work) {
-  SideStream* ss = side_stream();
-  if (!ss) {
-    const hipError_t e = side_work(s);
-    return e != hipSuccess ? e : main_work(s);
-  }
-  std::lock_guard<std::mutex> lk(ss->mu);
-  hipError_t e = hipEventRecord(ss->fork, s);
-  if (e == hipSuccess) e = hipStreamWaitEvent(ss->stream, ss->fork, 0);
+// The up GEMM's two tile lists in one launch (grouped_gemm_dma_split): the
+// streaming tiles of `small` on the first kSmallGroupBlocks blocks, one
+// 288-row tile of `big` on each later block.
+hipError_t launch_up_split(const GemmArgs& big, int big_m_tiles, const GemmArgs& small,
+                           hipStream_t s) {
+  const int big_grid = xcd_grid((int64_t)big_m_tiles * big.n_tiles);
+  const int grid = kSmallGroupBlocks + big_grid;
+  auto kern = grouped_gemm_dma_split<EPI_SWIGLU>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kSplitLds);
   if (e != hipSuccess) return e;
-  const hipError_t e_side = side_work(ss->stream);
-  // join even when a launch failed, so that s never runs ahead of the side work
-  e = hipEventRecord(ss->join, ss->stream);
-  const hipError_t e_main = e_side == hipSuccess ? main_work(s) : hipSuccess;
-  if (e == hipSuccess) e = hipStreamWaitEvent(s, ss->join, 0);
-  return e_side != hipSuccess ? e_side : e_main != hipSuccess ? e_main : e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kSplitBigWaves), kSplitLds, s, big, small,
+                     kSmallGroupBlocks);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -284,23 +232,14 @@ hipError_t launch_expert_up(const moe_config& c, const ExpertFfnArgs& a, hipStre
       // the groups of more rows: 288-row tiles (3 x 4 waves of 96 x 64) with
       // the scheduled main loop (Mixtral's up GEMM 1.72 -> 1.67 ms and
       // DeepSeek-V3's 4.52 -> 4.33 ms against 256-row tiles)
-      auto large = [&](hipStream_t st) {
-        return launch_gemm_dma<288, 256, 3, 4, EPI_SWIGLU, 2, 128, 3, 1>(g, mb, st);
-      };
-      if (!split_small_groups(a)) return large(s);
-      // groups of a few rows: one 32-row streaming tile each, on a few
-      // persistent blocks beside them
+      if (!split_small_groups(a))
+        return launch_gemm_dma<288, 256, 3, 4, EPI_SWIGLU, 2, 128, 3, 1>(g, mb, s);
+      // groups of a few rows: one 32-row streaming tile each, walked by a few
+      // blocks of the same launch beside the 288-row tiles
       GemmArgs gs = g;
       gs.tile_prefix = a.tile_prefix + kListSmall32 * (a.n_groups + 1);
       g.tile_prefix = a.tile_prefix + kListLarge288 * (a.n_groups + 1);
-      const int sb = small_group_bound(a);
-      return fork_join(
-          s,
-          [&](hipStream_t st) {
-            return launch_gemm_dma<32, 256, 1, 4, EPI_SWIGLU, 4, 128, 3, 0, 1>(
-                gs, sb, st, MOE_SMALL_GROUP_BLOCKS);
-          },
-          large);
+      return launch_up_split(g, mb, gs, s);
     }
     default:
       g.n_tiles = c.d_ff / 64;

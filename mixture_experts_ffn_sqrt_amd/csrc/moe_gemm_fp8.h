@@ -108,7 +108,7 @@ __host__ __device__ constexpr int fp8_stage_bytes() {
 template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int WF = WF_E4M3, int SCHED = 0>
 __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
   const GemmArgs& p = q.g;
-  constexpr int NT = 64 * WM * WN, NW = WM * WN;
+  constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr bool SW = EPI == EPI_SWIGLU8;

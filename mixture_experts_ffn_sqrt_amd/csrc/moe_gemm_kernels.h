@@ -119,9 +119,11 @@ constexpr int kSuperRows = 8;
 // tile count divided by 8), measured 4% faster there than chunks.  (The grid
 // is a whole number of 8 * kXcdChunk blocks; blocks past the tiles exit.)
 //
-// `vbid` (default: the block index) lets a persistent block walk the tiles of
-// blocks vbid, vbid + gridDim.x, ...; with a grid of a multiple of 8 blocks
-// each of those runs on the XCD the mapping assumes.
+// `vbid` (default: the block index) is the block's number in this order: a
+// persistent block walks virtual blocks vbid, vbid + n, ..., and a block of a
+// launch that serves two tile lists counts from the first block of its list.
+// Whenever vbid and the block index agree modulo 8, every tile runs on the XCD
+// the mapping assumes.
 template <int BM>
 __device__ __forceinline__ bool decode_tile(const GemmArgs& p, TileCoord& tc, int vbid = -1) {
   const int nt_all = p.n_tiles;
@@ -454,7 +456,7 @@ __device__ __forceinline__ void sched_stage() {
 // stage, in the order sched_stage fixes (full tiles only).
 template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int ROWB, int SWZ, int SCHED>
 __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& p, const TileCoord& tc) {
-  constexpr int NT = 64 * WM * WN, NW = WM * WN;
+  constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr bool SW = EPI == EPI_SWIGLU;
@@ -668,25 +670,47 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& p, const TileCoord
   }
 }
 
-// Direct-to-LDS grouped GEMM: one tile per block, or (PERSIST = 1, a grid of a
-// multiple of 8 blocks smaller than the tile count) each block takes the
-// tiles of blocks b, b + gridDim.x, ... in turn, so that the launch occupies
-// at most gridDim.x CUs.  Every wave sees the same tile sequence; the barrier
-// between tiles keeps the next tile's first LDS loads from landing in a stage
-// another wave still reads.
-template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int ROWB, int SWZ, int SCHED = 0,
-          int PERSIST = 0>
+// Direct-to-LDS grouped GEMM: one tile per block.
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int ROWB, int SWZ, int SCHED = 0>
 __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) {
   TileCoord tc;
-  if constexpr (PERSIST) {
-    for (int vb = blockIdx.x; decode_tile<BM>(p, tc, vb); vb += gridDim.x) {
-      if (vb != (int)blockIdx.x) __syncthreads();
-      gemm_dma_tile<BM, BN, WM, WN, EPI, STAGES, ROWB, SWZ, SCHED>(p, tc);
+  if (!decode_tile<BM>(p, tc)) return;
+  gemm_dma_tile<BM, BN, WM, WN, EPI, STAGES, ROWB, SWZ, SCHED>(p, tc);
+}
+
+// Tile shapes of the two roles of grouped_gemm_dma_split (the up GEMM of a
+// prefill-shaped batch with a skewed load): 288 x 256 tiles on 12 waves with
+// the scheduled main loop for the groups of more than 32 rows, and 32-row
+// streaming tiles (4 waves, a four-stage ring of weight loads) for the others.
+constexpr int kSplitBigWaves = 12, kSplitSmallWaves = 4;
+constexpr int kSplitLds = 4 * (32 + 256) * 128;  // the larger of the two rings
+static_assert(kSplitLds >= 2 * (288 + 256) * 128, "LDS of the 288-row role");
+
+// Both kinds of tile in one launch: blocks [0, n_small) walk the streaming
+// tiles of `small` in turn (block b takes the tiles of virtual blocks b,
+// b + n_small, ..., which keeps each on the XCD the tile order assumes, since
+// n_small is a multiple of 8), and every later block takes one 288-row tile of
+// `big`.  The hardware dispatches blocks in index order, so the streaming
+// blocks start first on n_small CUs and the 288-row tiles fill the others and,
+// as the streaming blocks finish, theirs too.  The streaming tiles use 4 of
+// the 12 waves; the other 8 end at once, and a barrier then waits only for the
+// waves still running (S_BARRIER in the CDNA ISA).  The two roles write
+// disjoint output rows.
+template <int EPI>
+__global__ __launch_bounds__(64 * kSplitBigWaves, 1) void grouped_gemm_dma_split(
+    GemmArgs big, GemmArgs small, int n_small) {
+  TileCoord tc;
+  const int bid = blockIdx.x;
+  if (bid < n_small) {
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= kSplitSmallWaves) return;
+    for (int vb = bid; decode_tile<32>(small, tc, vb); vb += n_small) {
+      if (vb != bid) __syncthreads();
+      gemm_dma_tile<32, 256, 1, kSplitSmallWaves, EPI, 4, 128, 3, 0>(small, tc);
     }
-  } else {
-    if (!decode_tile<BM>(p, tc)) return;
-    gemm_dma_tile<BM, BN, WM, WN, EPI, STAGES, ROWB, SWZ, SCHED>(p, tc);
+    return;
   }
+  if (!decode_tile<288>(big, tc, bid - n_small)) return;
+  gemm_dma_tile<288, 256, 3, 4, EPI, 2, 128, 3, 1>(big, tc);
 }
 
 }  // namespace gemm
