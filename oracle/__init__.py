@@ -43,6 +43,12 @@ def lib():
         L.oracle_logits.restype = None
         L.oracle_layer.argtypes = [I, P, I, I, I, I, I, I, I, I, I, I, I,
                                    P, P, P, P, P, P, I, P, P, P, P, P, P, P, P]
+        L.oracle_expert_rows.argtypes = [I, P, I, I, P, I, P, P, P]
+        L.oracle_expert_rows.restype = None
+        L.oracle_expert_rows_lowp.argtypes = [I, I, P, I, I, P, I, P, P, P, P, P]
+        L.oracle_expert_rows_lowp.restype = None
+        L.oracle_set_num_threads.argtypes = [I]
+        L.oracle_set_num_threads.restype = None
         L.oracle_num_threads.argtypes = []
         L.oracle_e4m3_decode.argtypes = [C.c_uint8]
         L.oracle_e4m3_decode.restype = C.c_double
@@ -173,6 +179,21 @@ def expert_ffn(x, w13_e, w2_e):
     return y
 
 
+def expert_rows(hidden, tokens, w13_e, w2_e):
+    """One SwiGLU expert on the listed token rows of hidden [T, d]: [n, d] double,
+    row q = expert_ffn(hidden[tokens[q]], w13_e, w2_e)."""
+    h, dt = _tensor(hidden)
+    w13_e, dt2 = _tensor(w13_e)
+    w2_e, dt3 = _tensor(w2_e)
+    assert dt == dt2 == dt3
+    d = h.shape[1]
+    d_ff = w13_e.shape[0] // 2
+    tok = _c(tokens, np.int32)
+    y = np.zeros((len(tok), d), np.float64)
+    lib().oracle_expert_rows(len(tok), _p(tok), d, d_ff, _p(h), dt, _p(w13_e), _p(w2_e), _p(y))
+    return y
+
+
 def logits(hidden, w_router, rows=None, logit_offset=None):
     h, dt = _tensor(hidden)
     w, dt2 = _tensor(w_router)
@@ -245,6 +266,11 @@ def layer(hidden, w_router, w13, w2, k, scoring, rows=None, bias=None,
 
 def num_threads():
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n):
+    """Threads of the oracle's later parallel loops (for a single-core timing)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 # ----------------------------------------------------------------------------
@@ -429,6 +455,23 @@ def expert_ffn_mxfp4(xq, xs, w13q, w13s, w2q, w2s):
     y = np.zeros(d, np.float64)
     lib().oracle_expert_ffn_mxfp4(d, d_ff, _p(xq), _p(xs), _p(w13q), _p(w13s), _p(w2q),
                                   _p(w2s), _p(y))
+    return y
+
+
+def expert_rows_lowp(fmt, hidden, tokens, w13q, w13s, w2q, w2s):
+    """One low-precision expert on the listed token rows of hidden [T, d] (bf16
+    bits or float32): each row is quantized 1x128 as in the FP8 layer, then
+    expert_ffn_fp8 (fmt "fp8": float tile scales) or expert_ffn_mxfp4 (fmt
+    "mxfp4": E8M0 block scales [R, C/32]).  Returns [n, d] double."""
+    h, dt = _tensor(hidden)
+    sd = np.float32 if fmt == "fp8" else np.uint8
+    w13q, w13s, w2q, w2s = (_c(w13q, np.uint8), _c(w13s, sd), _c(w2q, np.uint8), _c(w2s, sd))
+    d = h.shape[1]
+    d_ff = w13q.shape[0] // 2
+    tok = _c(tokens, np.int32)
+    y = np.zeros((len(tok), d), np.float64)
+    lib().oracle_expert_rows_lowp(0 if fmt == "fp8" else 1, len(tok), _p(tok), d, d_ff, _p(h),
+                                  dt, _p(w13q), _p(w13s), _p(w2q), _p(w2s), _p(y))
     return y
 
 

@@ -882,6 +882,62 @@ int oracle_layer_mxfp4(int n, const int32_t *rows, int d, int E, int k, int d_ff
                       ids_out, gates_out, margin_out);
 }
 
+/* ---------------------------------------------------------------------------
+ * One expert over a list of token rows (test convenience): y[q] = FFN_e(x_t)
+ * for t = tokens[q], each row exactly as oracle_expert_ffn evaluates it (the
+ * rows are independent; OpenMP over rows).  hidden [T, d] in dtype.
+ * ------------------------------------------------------------------------- */
+void oracle_expert_rows(int n, const int32_t *tokens, int d, int d_ff, const void *hidden,
+                        int dtype, const void *w13, const void *w2, double *y)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int q = 0; q < n; ++q) {
+        double *x = malloc(sizeof(double) * d);
+        size_t t = (size_t)tokens[q];
+        for (int i = 0; i < d; ++i)
+            x[i] = elem(hidden, t * d + i, dtype);
+        oracle_expert_ffn(d, d_ff, x, w13, w2, dtype, y + (size_t)q * d);
+        free(x);
+    }
+}
+
+/* The same with FP8 (fmt 0: E4M3 weights, float tile scales) or MXFP4 (fmt 1:
+   E2M1 weights, E8M0 block scales) expert weights: each token's hidden row is
+   rounded to float and quantized 1x128 as in the FP8 layer, then goes through
+   the low-precision expert. */
+void oracle_expert_rows_lowp(int fmt, int n, const int32_t *tokens, int d, int d_ff,
+                             const void *hidden, int dtype, const uint8_t *w13q,
+                             const void *w13s, const uint8_t *w2q, const void *w2s, double *y)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int q = 0; q < n; ++q) {
+        float *xf = malloc(sizeof(float) * d);
+        uint8_t *xq = malloc(d);
+        float *xs = malloc(sizeof(float) * (d / 128));
+        size_t t = (size_t)tokens[q];
+        for (int i = 0; i < d; ++i)
+            xf[i] = (float)elem(hidden, t * d + i, dtype);
+        oracle_quantize_rows(1, d, xf, xq, xs);
+        if (fmt == 0)
+            ffn_fp8_any(d, d_ff, xq, xs, w13q, w13s, w2q, w2s, y + (size_t)q * d);
+        else
+            ffn_mxfp4_any(d, d_ff, xq, xs, w13q, w13s, w2q, w2s, y + (size_t)q * d);
+        free(xf);
+        free(xq);
+        free(xs);
+    }
+}
+
+/* set the number of OpenMP threads later parallel loops use (timing on one core) */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}
+
 /* number of OpenMP threads the layer loop runs on (reported with timings) */
 int oracle_num_threads(void)
 {

@@ -173,3 +173,26 @@ def test_low_precision_forward_empty_batch(fn):
     assert getattr(L, fn)(C.byref(c), *args, 1 << 40, None) == 0
     assert L.moe_expert_up_fp8(C.byref(c), *([bogus] * 8), bogus, 1 << 40, None) == 0
     assert L.moe_expert_down_mxfp4(C.byref(c), *([bogus] * 6), bogus, 1 << 40, None) == 0
+
+
+def test_peaks_library_exports_every_declared_symbol():
+    from mixture_experts_ffn_sqrt_amd import peaks
+    text = open(os.path.join(ROOT, "include", "moe_peaks.h")).read()
+    declared = sorted(set(re.findall(r"^(?:int|size_t|double)\s*(moe_peaks_\w+)\s*\(", text, re.M)))
+    assert declared == sorted(peaks.EXPORTS)
+    L = peaks.load_library()
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.moe_peaks_operand_bytes() == 16 << 20
+    assert L.moe_peaks_mfma_flops(0, 1, 4) == 2.0 * 32 * 32 * 16 * 8 * 4 * 4
+
+
+def test_peaks_reject_bad_arguments_on_the_host():
+    from mixture_experts_ffn_sqrt_amd import peaks
+    L = peaks.load_library()
+    p = C.c_void_p(16)  # never dereferenced: every call below fails its host checks
+    assert L.moe_peaks_mfma(2, p, 1, 4, p, None) == -1      # unknown kind
+    assert L.moe_peaks_mfma(0, p, 1, 6, p, None) == -1      # iters not a multiple of 4
+    assert L.moe_peaks_mfma(0, None, 1, 4, p, None) == -1
+    assert L.moe_peaks_read(p, 4095, 1, p, None) == -1      # not a multiple of 4096
+    assert L.moe_peaks_read(p, 4096, 0, p, None) == -1

@@ -165,48 +165,11 @@ FP8_LAYERS = {
 }
 
 
-def oracle_layer_fp8_rows(lc, inp, rows, route_mode=O.LEARNED):
-    """Oracle FP8 layer on the listed rows; weights of the needed experts are
-    quantized from their bf16 masters by the oracle."""
-    hb = to_host_bits(inp["hidden"])
-    wr = to_host_bits(inp["w_router"])
-    bias = to_host_bits(inp.get("bias"))
-    off = to_host_bits(inp.get("logit_offset"))
-    tok = to_host_bits(inp.get("token_ids"))
-    tab = to_host_bits(inp.get("tid2eid"))
-    rows = np.asarray(rows, np.int32)
-    grp = dict(n_group=lc.n_group, topk_group=lc.topk_group, group_topk=lc.group_topk)
-    lg = O.logits(hb, wr, rows=rows, logit_offset=off).astype(np.float32)
-    if route_mode == O.HASH:
-        ids, _ = O.hash_route(lg, tok[rows], tab, lc.scoring)
-    else:
-        ids, _, _ = O.route(lg, lc.k, lc.scoring, bias=bias, **grp)
-    w13q, w13s, w2q, w2s = [None] * lc.E, [None] * lc.E, [None] * lc.E, [None] * lc.E
-    for e in sorted(set(ids.ravel().tolist())):
-        w13q[e], w13s[e] = O.quantize_blocks(to_host_bits(inp["w13"][e]))
-        w2q[e], w2s[e] = O.quantize_blocks(to_host_bits(inp["w2"][e]))
-    shared = None
-    if inp.get("w13_shared") is not None:
-        shared = O.quantize_blocks(to_host_bits(inp["w13_shared"])) + \
-            O.quantize_blocks(to_host_bits(inp["w2_shared"]))
-    return O.layer_fp8(hb, wr, w13q, w13s, w2q, w2s, lc.k, lc.scoring, rows=rows, bias=bias,
-                       logit_offset=off, shared=shared, route_mode=route_mode, token_ids=tok,
-                       tid2eid=tab, **grp)
-
-
 def check_layer_fp8(lc, inp, out, ids, gates, rows, route_mode=O.LEARNED):
-    ref = oracle_layer_fp8_rows(lc, inp, rows, route_mode)
-    rows = np.asarray(rows)
-    g_ids = ids.cpu().numpy()[rows]
-    tie = (ref["margin"] <= H.TIE_LAYER) if route_mode == O.LEARNED else np.zeros(len(rows), bool)
-    ok = ~tie
-    assert tie.sum() <= max(2, 0.02 * len(rows))
-    assert np.array_equal(g_ids[ok], ref["ids"][ok])
-    assert np.abs(gates.cpu().numpy()[rows][ok] - ref["gates"][ok]).max(initial=0) <= 1e-5
-    err = H.row_rel_err(H.to_f64(out)[rows][ok], ref["out"][ok])
-    assert err.max(initial=0) <= LAYER_TOL, err.max()
-    assert np.median(err) <= LAYER_MEDIAN_TOL, np.median(err)
-    return err
+    """The FP8 layer on the listed rows against the oracle's FP8 layer (which
+    quantizes the bf16 masters itself), near-tie tokens included."""
+    return H.check_layer(lc, inp, out, ids, gates, rows, route_mode=route_mode, fmt="fp8",
+                         tol=LAYER_TOL, median_tol=LAYER_MEDIAN_TOL)
 
 
 @pytest.mark.parametrize("name", list(FP8_LAYERS))
@@ -230,22 +193,27 @@ def test_forward_fp8_hash_pass():
                     route_mode=O.HASH)
 
 
-@pytest.mark.parametrize("name, n_rows", [("mixtral_prefill", 24), ("v4flash_decode", 6),
-                                          ("dsv3_prefill", 6),
-                                          ("v4pro_skew_prefill", 6)])
-def test_forward_fp8_full_size_sampled(name, n_rows):
+@pytest.mark.parametrize("name, n_rows", [("mixtral_prefill", 24), ("v4flash_decode", 64),
+                                          ("dsv3_prefill", 6), ("v4pro_skew_prefill", 6)])
+def test_forward_fp8_full_size(name, n_rows):
+    """Full size, in the launch configuration the bench times: the layer on
+    sampled rows (hottest and coldest experts' included), the two expert stages
+    on every row tile of a spread of experts, and every expert's quantized
+    weights spot-checked against the oracle's quantizer."""
     lc = CONFIGS[name]
     inp = make_inputs(lc, "cuda")
     layer = moe.MoELayer(H.cfg_of(lc), inp)
     fp8 = moe.quantize_fp8_weights(inp)
     out = layer.forward_fp8(fp8)
     torch.cuda.synchronize()
-    rows = np.random.default_rng(5).choice(lc.T, n_rows, replace=False)
-    if lc.zipf_s > 0:  # the hottest expert's rows and a cold (streaming-tile) expert's
-        ids_np = layer.ids.cpu().numpy()
-        counts = np.bincount(ids_np.ravel(), minlength=lc.E)
-        rows = np.unique(np.r_[rows, H.hot_cold_rows(ids_np, counts)])
-    check_layer_fp8(lc, inp, out, layer.ids, layer.gates, rows=np.sort(rows))
+    ids_np = layer.ids.cpu().numpy()
+    counts = np.bincount(ids_np.ravel(), minlength=lc.E)
+    rows = np.random.default_rng(5).choice(lc.T, min(n_rows, lc.T), replace=False)
+    rows = np.unique(np.r_[rows, H.hot_cold_rows(ids_np, counts)])
+    check_layer_fp8(lc, inp, out, layer.ids, layer.gates, rows=rows)
+    H.check_lowp_stages(lc, inp, "fp8", fp8, layer.ids, layer.gates, LAYER_TOL,
+                        LAYER_MEDIAN_TOL, seed=lc.seed)
+    H.check_quantized_tiles(inp, fp8, "fp8", seed=lc.seed)
 
 
 @pytest.mark.parametrize("name", ["mixtral_small", "mixtral_tall_tiles"])

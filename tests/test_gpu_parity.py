@@ -36,17 +36,6 @@ def dev(x, dtype=None):
     return t.contiguous().cuda()
 
 
-def np_keys(logits, scoring, bias):
-    l = logits.astype(np.float64)
-    if scoring == O.SIGMOID:
-        s = 1 / (1 + np.exp(-l))
-    elif scoring == O.SQRTSOFTPLUS:
-        s = np.sqrt(np.logaddexp(0, l))
-    else:
-        s = l
-    return s + (0 if bias is None else bias.astype(np.float64))
-
-
 # ----------------------------------------------------------------------------
 # routing from identical logits
 # ----------------------------------------------------------------------------
@@ -113,7 +102,8 @@ def test_route_from_given_logits(case):
         assert np.array_equal(ids, rid)
         assert np.abs(gates - rg).max() <= H.GATE_TOL
         return
-    H.check_routing(ids, gates, rid, rg, margin, keys=None if grp else np_keys(lg, case["scoring"], bias))
+    H.check_routing(ids, gates, rid, rg, margin, keys=H.np_keys(lg, case["scoring"], bias),
+                    grp=grp)
     if grp:
         G = E // grp["n_group"]
         assert max(len(np.unique(r // G)) for r in ids) <= grp["topk_group"]
@@ -384,9 +374,12 @@ FULL = ["tiny_fp32", "mixtral_prefill", "dsv3_prefill", "v4flash_decode", "v4pro
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_forward_full_size_sampled(name):
-    """The workload at its full size, in the same launch configuration the bench
-    times; the oracle recomputes sampled token rows one by one."""
+def test_forward_full_size_stratified(name):
+    """The workload at its full size, in the launch configuration the bench
+    times.  The oracle recomputes, from its own routing, one token row in every
+    32-row fragment of every expert's dispatch rows (and of the shared expert's):
+    every (expert, row tile) of both grouped GEMMs and every combine path is
+    compared, near-tie tokens included."""
     lc = CONFIGS[name]
     inp = make_inputs(lc, "cuda")
     out, ids, gates = H.gpu_forward(H.cfg_of(lc), inp)
@@ -394,20 +387,29 @@ def test_forward_full_size_sampled(name):
     ids_np = ids.cpu().numpy()
     # properties at any size
     assert ((ids_np >= 0) & (ids_np < lc.E)).all()
-    assert all(len(set(r)) == lc.k for r in ids_np[:: max(1, T // 512)])
+    assert all(len(set(r)) == lc.k for r in ids_np)
     g = gates.cpu().numpy()
     assert np.allclose(g.sum(1), 1.0, atol=1e-5)
     counts = np.bincount(ids_np.ravel(), minlength=lc.E)
     assert counts.sum() == T * lc.k
     if lc.zipf_s > 0:  # the skewed workload must actually be skewed
         assert counts.max() > 10 * counts.mean() and (counts == 0).any()
-    rng = np.random.default_rng(lc.seed)
-    n = min(T, 16 if lc.d * lc.d_ff < 2e7 else 8)
-    rows = np.sort(rng.choice(T, n, replace=False))
-    if lc.zipf_s > 0:  # include the token rows of the hottest expert and of a cold one
-        rows = np.unique(np.r_[rows, H.hot_cold_rows(ids_np, counts)])
-    res = H.check_layer(lc, inp, out, ids, gates, rows=rows, max_tie_frac=0.2)
-    assert res["rows"] - res["ties"] >= n // 2
+    rows = H.stratified_rows(ids_np, lc.E, T, lc.n_shared, seed=lc.seed)
+    res = H.check_layer(lc, inp, out, ids, gates, rows=rows)
+    print("%s: %d rows checked, %d near-ties, max row rel err %.3g, frobenius %.3g" % (
+        name, res["rows"], res["ties"], res["max_row_rel_err"], res["fro_rel_err"]))
+
+
+def test_forward_hash_pass_full_size():
+    """The decode workload's hash-routed pass at its real shape: tid2eid
+    [129280, 6] indexed by uniform random token ids, d = 4096, d_ff = 2048."""
+    lc = CONFIGS["v4flash_decode"]
+    inp = make_inputs(lc, "cuda", hash_pass=True)
+    assert tuple(inp["tid2eid"].shape) == (129280, 6)
+    out, ids, gates = H.gpu_forward(H.cfg_of(lc, route_mode=1), inp)
+    assert np.array_equal(ids.cpu().numpy(),
+                          inp["tid2eid"].cpu().numpy()[inp["token_ids"].cpu().numpy()])
+    H.check_layer(lc, inp, out, ids, gates, rows=np.arange(lc.T), route_mode=O.HASH)
 
 
 # ----------------------------------------------------------------------------

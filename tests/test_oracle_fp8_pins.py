@@ -171,6 +171,21 @@ def test_expert_ffn_fp8_against_dequantized_arrays():
     assert np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
 
 
+def test_expert_rows_lowp_fp8_equal_single_rows():
+    """The batched helper quantizes each listed row 1x128 and runs the FP8 expert
+    on it, exactly as quantize_rows followed by expert_ffn_fp8."""
+    rng = np.random.default_rng(8)
+    d, d_ff = 256, 128
+    x = rng.standard_normal((5, d)).astype(np.float32)
+    w13q, w13s = O.quantize_blocks((rng.standard_normal((2 * d_ff, d)) / 16).astype(np.float32))
+    w2q, w2s = O.quantize_blocks((rng.standard_normal((d, d_ff)) / 11).astype(np.float32))
+    tokens = np.array([4, 1, 4, 0], np.int32)
+    y = O.expert_rows_lowp("fp8", x, tokens, w13q, w13s, w2q, w2s)
+    xq, xs = O.quantize_rows(x)
+    for q, t in enumerate(tokens):
+        assert np.array_equal(y[q], O.expert_ffn_fp8(xq[t], xs[t], w13q, w13s, w2q, w2s))
+
+
 def test_expert_ffn_fp8_exact_on_small_integers():
     """Codes of small integers with unit scales: every sum is an exact integer."""
     rng = np.random.default_rng(8)

@@ -180,6 +180,21 @@ def test_expert_ffn_mxfp4_against_dequantized_arrays():
     assert np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
 
 
+def test_expert_rows_lowp_mxfp4_equal_single_rows():
+    """The batched helper quantizes each listed row 1x128 and runs the MXFP4
+    expert on it, exactly as quantize_rows followed by expert_ffn_mxfp4."""
+    rng = np.random.default_rng(9)
+    d, d_ff = 256, 128
+    x = rng.standard_normal((5, d)).astype(np.float32)
+    w13q, w13s = O.quantize_mxfp4((rng.standard_normal((2 * d_ff, d)) / 16).astype(np.float32))
+    w2q, w2s = O.quantize_mxfp4((rng.standard_normal((d, d_ff)) / 11).astype(np.float32))
+    tokens = np.array([2, 2, 4, 0], np.int32)
+    y = O.expert_rows_lowp("mxfp4", x, tokens, w13q, w13s, w2q, w2s)
+    xq, xs = O.quantize_rows(x)
+    for q, t in enumerate(tokens):
+        assert np.array_equal(y[q], O.expert_ffn_mxfp4(xq[t], xs[t], w13q, w13s, w2q, w2s))
+
+
 def test_expert_ffn_mxfp4_exact_on_grid_weights():
     """Weights drawn from the E2M1 grid with a 6 in every block (scale 1) are
     stored exactly: the expert equals the dense float64 expert on those weights

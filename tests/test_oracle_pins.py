@@ -306,6 +306,28 @@ def test_expert_ffn_matches_dense():
     assert np.allclose(y, dense_swiglu(x[0], w13[0], w2[0]).numpy(), rtol=1e-12, atol=1e-13)
 
 
+def test_expert_rows_equal_single_rows():
+    """The batched helper evaluates each listed token row exactly as expert_ffn
+    does (repeated and unordered tokens; float32 and bf16 inputs)."""
+    rng = np.random.default_rng(3)
+    x, _, w13, w2 = random_layer(rng, 9, 32, 1, 40)
+    tokens = np.array([3, 0, 3, 8, 5, 1], np.int32)
+    y = O.expert_rows(x, tokens, w13[0], w2[0])
+    for q, t in enumerate(tokens):
+        assert np.array_equal(y[q], O.expert_ffn(x[t], w13[0], w2[0]))
+        assert np.allclose(y[q], dense_swiglu(x[t], w13[0], w2[0]).numpy(), rtol=1e-12,
+                           atol=1e-13)
+
+    def bits(a):
+        return torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+    xb, w13b, w2b = bits(x), bits(w13[0]), bits(w2[0])
+    yb = O.expert_rows(xb, tokens, w13b, w2b)
+    xd = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    for q, t in enumerate(tokens):
+        assert np.array_equal(yb[q], O.expert_ffn(xd[t], w13b, w2b))
+
+
 @pytest.mark.parametrize("case", [
     dict(scoring=O.SOFTMAX, k=2),
     dict(scoring=O.SIGMOID, k=3, bias=True, n_group=3, topk_group=2, group_topk=2, shared=True),
