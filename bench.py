@@ -3,15 +3,19 @@
 
 A step is one moe_forward call (router GEMM, scores + top-k, permutation,
 grouped SwiGLU GEMM 1, grouped GEMM 2, combine) over one batch of synthetic
-inputs already resident in HBM.  Prints ONE JSON line with tokens/s, the
-roofline of the dominant kernel (grouped GEMM 1 + SwiGLU), and the CPU oracle
-timed on a bounded sample of the same workload.
+inputs already resident in HBM.  Prints ONE JSON line with tokens/s of the
+headline workload (DeepSeek-V4-Pro-shaped prefill with a Zipf-skewed load,
+T=16384, d=7168, E=384+1, top-6, d_ff=3072: the largest configuration), the
+roofline of its dominant kernel (grouped GEMM 1 + SwiGLU), the chip's measured
+ceilings, and the CPU oracle timed on a bounded sample of the same workload.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--all] [--no-decode]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--side NAMES|none]
 
-Beside the headline workload the line carries the decode-shaped workload
-("decode": its grouped GEMM 1 against HBM bandwidth), or every workload
-with --all.
+Beside the headline the line carries the other prefill workloads (DeepSeek-V3
+and Mixtral shapes: grouped GEMMs against the bf16 matrix-core peak) and the
+decode workload (V4-Flash shapes, learned and hash-routed passes: GEMM 1
+against HBM bandwidth), each with its own roofline, and the FP8 / MXFP4 expert
+variants of every workload.
 """
 import argparse
 import json
@@ -23,8 +27,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s + grouped-GEMM % bf16 MFMA peak (prefill), % HBM BW (decode)"
-DEFAULT_WORKLOAD = "mixtral_prefill"  # T=4096, d=4096, E=8, top-2, d_ff=14336, bf16
-DECODE_WORKLOAD = "v4flash_decode"    # T=64, d=4096, E=256+1, top-6, d_ff=2048, bf16
+DEFAULT_WORKLOAD = "v4pro_skew_prefill"  # T=16384, d=7168, E=384+1, top-6, d_ff=3072, bf16
+SIDE_WORKLOADS = ("dsv3_prefill", "mixtral_prefill", "v4flash_decode")
 
 # MI355X published peaks
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8": 5000.0}  # dense MFMA
@@ -37,15 +41,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--all", action="store_true", help="also time the other workloads")
-    ap.add_argument("--no-decode", action="store_true",
-                    help="skip the decode-shaped workload reported beside the headline")
+    ap.add_argument("--side", default=",".join(SIDE_WORKLOADS),
+                    help="comma-separated workloads reported beside the headline, or 'none'")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=25.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the workload, copy 1 GiB three times (counter calibration)")
     ap.add_argument("--no-peaks", action="store_true",
-                    help="skip the vendor-library bf16 GEMM and copy reference points")
+                    help="skip the measured ceilings and the vendor-library reference points")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the FP8-expert measurements reported beside the bf16 ones")
     ap.add_argument("--no-mxfp4", action="store_true",
@@ -146,19 +149,29 @@ def step_percentiles(fn, steps, stream):
     return [round(float(np.percentile(t, q)), 4) for q in (10, 50, 90)]
 
 
-def input_sha256(inp):
-    """SHA-256 of every input buffer's bytes, so that a result can be tied to
-    the exact synthetic inputs whatever generator produced them."""
+def input_digests(inp):
+    """Digests of every input buffer's bytes, so that a result can be tied to the
+    exact synthetic inputs whatever generator produced them: SHA-256 of the
+    small tensors, XXH3-128 of the expert weight stacks (tens of GB, streamed
+    to the host one expert at a time)."""
     import hashlib
+
     import torch
-    out = {}
+    import xxhash
+    sha, xxh = {}, {}
     for name in sorted(inp):
         t = inp[name]
         if t is None:
             continue
-        b = t.detach().contiguous().view(torch.uint8).cpu().numpy()
-        out[name] = hashlib.sha256(b.tobytes()).hexdigest()
-    return out
+        if name in ("w13", "w2"):
+            h = xxhash.xxh3_128()
+            for e in range(t.shape[0]):
+                h.update(t[e].detach().contiguous().view(torch.uint8).cpu().numpy().tobytes())
+            xxh[name] = h.hexdigest()
+        else:
+            b_ = t.detach().contiguous().view(torch.uint8).cpu().numpy()
+            sha[name] = hashlib.sha256(b_.tobytes()).hexdigest()
+    return dict(sha256=sha, xxh3_128=xxh)
 
 
 def lowp_accounting(lc, counts, kind):
@@ -180,7 +193,32 @@ def lowp_accounting(lc, counts, kind):
     return flops, nbytes
 
 
-def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True, with_mx=True):
+def up_roofline(acct, ms_up, decode, dtype, measured, name):
+    """Roofline of the dominant kernel (grouped GEMM 1 + SwiGLU, routed rows):
+    algorithmic bytes (decode-shaped batches) or FLOPs (prefill-shaped) of one
+    launch over its measured duration, against the published peak and the
+    chip's measured ceiling."""
+    if decode:
+        ach = acct["up_routed_bytes"] / (ms_up * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(ach / PEAK_HBM_GBS, 4))
+        ceil = measured.get("hbm_read_stream_gbs") if measured else None
+    else:
+        ach = acct["up_routed_flops"] / (ms_up * 1e-3) / 1e12
+        peak = PEAK_TFLOPS[dtype]
+        roof = dict(bound="mfma", achieved=round(ach, 1), peak=peak, unit="TFLOP/s",
+                    frac=round(ach / peak, 4))
+        ceil = measured.get("mfma_bf16_random_tflops") if measured and dtype == "bf16" else None
+    roof["traffic"] = measured_traffic(name)
+    roof["measured_peak"] = ceil
+    roof["frac_of_measured_peak"] = round(ach / ceil, 4) if ceil else None
+    roof["kernel"] = "grouped GEMM 1 + SwiGLU (moe_expert_up, routed rows)"
+    roof["kernel_ms"] = round(ms_up, 4)
+    return roof
+
+
+def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True, with_mx=True,
+                 measured=None):
     import numpy as np
     import torch
 
@@ -189,11 +227,13 @@ def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True, with
 
     lc = CONFIGS[name]
     stream = torch.cuda.current_stream()
-    inp = make_inputs(lc, "cuda")
+    with_hash = lc.hash_vocab > 0
+    inp = make_inputs(lc, "cuda", hash_pass=with_hash)
     c = moe.make_config(T=lc.T, d=lc.d, E=lc.E, k=lc.k, d_ff=lc.d_ff, n_shared=lc.n_shared,
                         dtype=lc.dtype, scoring=lc.scoring, n_group=lc.n_group,
                         topk_group=lc.topk_group, group_topk=lc.group_topk)
-    layer = moe.MoELayer(c, inp)
+    # the learned-route layer does not take the hash pass's table
+    layer = moe.MoELayer(c, dict(inp, token_ids=None, tid2eid=None))
     print("[bench] %s: inputs ready, workspace %.1f MB" % (name, layer.workspace.numel() / 1e6),
           file=sys.stderr, flush=True)
 
@@ -216,6 +256,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True, with
                     perm["disp"], ws)
     H = torch.empty((T * k, lc.d_ff), dtype=lc.torch_dtype, device="cuda")
     Y = torch.empty((T * k, lc.d), dtype=lc.torch_dtype, device="cuda")
+    out = torch.empty((T, lc.d), dtype=lc.torch_dtype, device="cuda")
 
     def up():
         moe.moe_expert_up(c, inp["hidden"], perm["tok"], perm["offsets"], inp["w13"], H, ws)
@@ -223,22 +264,15 @@ def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True, with
     def down():
         moe.moe_expert_down(c, H, perm["offsets"], inp["w2"], Y, ws)
 
+    def combine():
+        moe.moe_combine(c, Y, perm["disp"], layer.gates, None, out)
+
     ms_up, _ = time_gpu(up, steps, warmup, stream)
     ms_down, _ = time_gpu(down, steps, warmup, stream)
+    ms_combine, _ = time_gpu(combine, steps, warmup, stream)
 
     decode = acct["rows"] / max(acct["active_experts"], 1) < 48
-    if decode:
-        ach = acct["up_routed_bytes"] / (ms_up * 1e-3) / 1e9
-        roof = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(ach / PEAK_HBM_GBS, 4), traffic=None)
-    else:
-        ach = acct["up_routed_flops"] / (ms_up * 1e-3) / 1e12
-        peak = PEAK_TFLOPS[lc.dtype]
-        roof = dict(bound="mfma", achieved=round(ach, 1), peak=peak, unit="TFLOP/s",
-                    frac=round(ach / peak, 4), traffic=None)
-    roof["traffic"] = measured_traffic(name)
-    roof["kernel"] = "grouped GEMM 1 + SwiGLU (moe_expert_up, routed rows)"
-    roof["kernel_ms"] = round(ms_up, 4)
+    roof = up_roofline(acct, ms_up, decode, lc.dtype, measured, name)
     gemm_tflops = 6 * lc.d * lc.d_ff * T * k / ((ms_up + ms_down) * 1e-3) / 1e12
     res = dict(
         workload=name, ms_per_step=ms_step, tokens_per_s=T / (ms_step * 1e-3), wall_s=wall,
@@ -247,6 +281,10 @@ def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True, with
         grouped_gemm=dict(ms_up=round(ms_up, 4), ms_down=round(ms_down, 4),
                           tflops=round(gemm_tflops, 1),
                           frac_bf16_peak=round(gemm_tflops / PEAK_TFLOPS[lc.dtype], 4)),
+        # the combine of the routed rows on its own (the GEMM 2 output read back
+        # and the gated sum written): the cost of keeping the weighted sum out
+        # of the GEMM 2 epilogue
+        combine=dict(ms=round(ms_combine, 4), share_of_step=round(ms_combine / ms_step, 4)),
         layer=dict(tflops=round(acct["layer_flops"] / (ms_step * 1e-3) / 1e12, 1),
                    gbs=round(acct["layer_bytes"] / (ms_step * 1e-3) / 1e9, 1),
                    hbm_frac=round(acct["layer_bytes"] / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -255,20 +293,37 @@ def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True, with
         routing=dict(active_experts=acct["active_experts"], max_rows=int(counts.max()),
                      mean_rows=float(counts.mean()), empty_experts=int((counts == 0).sum())),
     )
+    if with_hash:
+        # the hash-routed pass: ids from tid2eid[token_ids], same experts and shapes
+        hc = moe.make_config(T=lc.T, d=lc.d, E=lc.E, k=lc.k, d_ff=lc.d_ff,
+                             n_shared=lc.n_shared, dtype=lc.dtype, scoring=lc.scoring,
+                             route_mode=moe.MOE_ROUTE_HASH, vocab=lc.hash_vocab)
+        hl = moe.MoELayer(hc, inp)
+        ms_hash, _ = time_gpu(hl.forward, steps, warmup, stream)
+        hcounts = np.bincount(hl.ids.cpu().numpy().ravel(), minlength=lc.E)
+        hacct = accounting(lc, hcounts)
+        res["hash_pass"] = dict(
+            ms_per_step=round(ms_hash, 4), tokens_per_s=round(T / (ms_hash * 1e-3), 1),
+            vocab=lc.hash_vocab, active_experts=hacct["active_experts"],
+            layer_gbs=round(hacct["layer_bytes"] / (ms_hash * 1e-3) / 1e9, 1),
+            layer_hbm_frac=round(hacct["layer_bytes"] / (ms_hash * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+        print("[bench] %s hash pass: %.3f ms/step" % (name, ms_hash), file=sys.stderr, flush=True)
+        del hl
     lowp_ok = lc.dtype == "bf16" and lc.d % 128 == 0 and lc.d_ff % 128 == 0
     for kind, on in (("fp8", with_fp8), ("mxfp4", with_mx)):
         if on and lowp_ok:
             res[kind] = run_lowp(kind, lc, c, layer, inp, perm, ws, Y, counts, decode, steps,
-                                 warmup, stream)
+                                 warmup, stream, measured)
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(lc, inp, cpu_seconds)
-        res["input_sha256"] = input_sha256(inp)
-    del layer, inp, H, Y, perm
+        res["input_digests"] = input_digests(inp)
+    del layer, inp, H, Y, out, perm
     torch.cuda.empty_cache()
     return res
 
 
-def run_lowp(kind, lc, c, layer, inp, perm, ws, Y, counts, decode, steps, warmup, stream):
+def run_lowp(kind, lc, c, layer, inp, perm, ws, Y, counts, decode, steps, warmup, stream,
+             measured=None):
     """The same step with FP8 activations and FP8 (E4M3, kind "fp8") or MXFP4
     (kind "mxfp4") expert weights (moe_forward_fp8 / moe_forward_mxfp4), and its
     two grouped GEMMs on their own; weights quantized once on the GPU beforehand.
@@ -309,6 +364,12 @@ def run_lowp(kind, lc, c, layer, inp, perm, ws, Y, counts, decode, steps, warmup
         roof = dict(bound="mfma", achieved=round(ach, 1), peak=PEAK_TFLOPS["fp8"],
                     unit="TFLOP/s", frac=round(ach / PEAK_TFLOPS["fp8"], 4),
                     traffic=measured_traffic(lc.name, kind))
+    ceil = None
+    if measured:
+        ceil = measured.get("hbm_read_stream_gbs") if decode else measured.get(
+            "mfma_fp8_random_tflops")
+    roof["measured_peak"] = ceil
+    roof["frac_of_measured_peak"] = round(ach / ceil, 4) if ceil else None
     roof["kernel"] = "%s grouped GEMM 1 + SwiGLU + FP8 cast (%s, routed rows)" % (
         "MXFP4-weight" if mx else "FP8", up_fn.__name__)
     roof["kernel_ms"] = round(ms_up, 4)
@@ -319,6 +380,15 @@ def run_lowp(kind, lc, c, layer, inp, perm, ws, Y, counts, decode, steps, warmup
                 grouped_gemm=dict(ms_up=round(ms_up, 4), ms_down=round(ms_down, 4),
                                   tflops=round(gemm_tflops, 1),
                                   frac_fp8_peak=round(gemm_tflops / PEAK_TFLOPS["fp8"], 4)))
+
+
+def measured_ceilings():
+    """The chip's ceilings measured by the committed microbenchmarks
+    (include/moe_peaks.h): matrix-core rates on random operands, HBM read stream."""
+    from mixture_experts_ffn_sqrt_amd import peaks as P
+    m = P.measure()
+    print("[bench] measured ceilings: %s" % m, file=sys.stderr, flush=True)
+    return m
 
 
 def peaks():
@@ -368,9 +438,23 @@ def calibrate_copy():
     print("[bench] calibration copy: 3 x %d bytes" % (1 << 30), file=sys.stderr, flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(lc, inp, seconds):
-    """The oracle as it stands, on a bounded sample of this workload's tokens
-    (the first n rows), all host threads.  Reported in tokens/s."""
+    """The oracle as it stands, on a bounded sample of this workload's tokens (the
+    first n rows, n sized from a probe to about `seconds` of work), on all the
+    host threads OpenMP gives it, and on one thread for a smaller sample.
+    Reported in tokens/s.  Only the experts the sampled tokens select are copied
+    to the host (the oracle's own routing of those rows decides which)."""
     import numpy as np
 
     import oracle as O
@@ -381,13 +465,22 @@ def cpu_baseline(lc, inp, seconds):
     wr = to_host_bits(inp["w_router"])
     bias = to_host_bits(inp.get("bias"))
     off = to_host_bits(inp.get("logit_offset"))
-    w13 = to_host_bits(inp["w13"])
-    w2 = to_host_bits(inp["w2"])
     s13 = to_host_bits(inp.get("w13_shared"))
     s2 = to_host_bits(inp.get("w2_shared"))
     grp = dict(n_group=lc.n_group, topk_group=lc.topk_group, group_topk=lc.group_topk)
+    w13 = [None] * lc.E
+    w2 = [None] * lc.E
+
+    def fetch(rows):
+        lg = O.logits(h, wr, rows=rows, logit_offset=off).astype(np.float32)
+        ids, _, _ = O.route(lg, lc.k, lc.scoring, bias=bias, **grp)
+        for e in sorted(set(ids.ravel().tolist())):
+            if w13[e] is None:
+                w13[e] = to_host_bits(inp["w13"][e])
+                w2[e] = to_host_bits(inp["w2"][e])
 
     def run(rows):
+        fetch(rows)
         t0 = time.perf_counter()
         O.layer(h, wr, w13, w2, k=lc.k, scoring=lc.scoring, rows=rows, bias=bias,
                 logit_offset=off, w13_shared=s13, w2_shared=s2, **grp)
@@ -395,12 +488,25 @@ def cpu_baseline(lc, inp, seconds):
 
     probe = np.arange(min(threads, lc.T), dtype=np.int32)
     tp = run(probe)
-    reps = max(1, min(int(seconds / max(tp, 1e-3)), lc.T // max(len(probe), 1)))
-    rows = np.arange(min(lc.T, len(probe) * reps), dtype=np.int32)
+    n = int(min(lc.T, max(len(probe), seconds / max(tp, 1e-4) * len(probe))))
+    n = max(len(probe), n // len(probe) * len(probe))
+    rows = np.arange(n, dtype=np.int32)
     t = run(rows)
+    # one thread: a sample of about a quarter of the time budget
+    O.set_num_threads(1)
+    try:
+        per_token_1 = tp * threads / len(probe)
+        n1 = int(min(lc.T, max(1, 0.25 * seconds / max(per_token_1, 1e-4))))
+        rows1 = np.arange(n1, dtype=np.int32)
+        t1 = run(rows1)
+    finally:
+        O.set_num_threads(threads)
     return dict(value=round(len(rows) / t, 3), unit="tokens/s", cores=threads, kind="oracle",
-                sample="first %d of %d tokens of %s, full layer per token (float64 FFN), %.1f s"
-                       % (len(rows), lc.T, lc.name, t))
+                sample="first %d of %d tokens of %s, full layer per token (float64 FFN), "
+                       "%.1f s on %d threads" % (len(rows), lc.T, lc.name, t, threads),
+                cpu_model=cpu_model(),
+                single_core=dict(value=round(n1 / t1, 3), unit="tokens/s", cores=1,
+                                 sample="first %d tokens, %.1f s" % (n1, t1)))
 
 
 def main():
@@ -416,8 +522,9 @@ def main():
     import mixture_experts_ffn_sqrt_amd as moe
     moe.load_library()
 
+    measured = None if args.no_peaks else measured_ceilings()
     head = run_workload(args.workload, args.steps, args.warmup, not args.no_cpu, args.cpu_seconds,
-                        not args.no_fp8, not args.no_mxfp4)
+                        not args.no_fp8, not args.no_mxfp4, measured)
     from mixture_experts_ffn_sqrt_amd.synth import CONFIGS
     lc = CONFIGS[args.workload]
     line = {
@@ -436,32 +543,30 @@ def main():
         "config": {"workload": lc.name, "T": lc.T, "d": lc.d, "E": lc.E, "k": lc.k,
                    "d_ff": lc.d_ff, "n_shared": lc.n_shared, "scoring": lc.scoring,
                    "n_group": lc.n_group, "topk_group": lc.topk_group,
-                   "group_topk": lc.group_topk, "parallelism": "single GPU"},
+                   "group_topk": lc.group_topk, "zipf_s": lc.zipf_s,
+                   "parallelism": "single GPU"},
         "roofline": head["roofline"],
         "cpu_baseline": head.get("cpu_baseline"),
         "grouped_gemm": head["grouped_gemm"],
+        "combine": head["combine"],
         "layer": head["layer"],
         "routing": head["routing"],
         "step_ms_p10_p50_p90": head["step_ms_p10_p50_p90"],
-        "input_sha256": head.get("input_sha256"),
+        "input_digests": head.get("input_digests"),
         "fp8": head.get("fp8"),
         "mxfp4": head.get("mxfp4"),
+        "measured_peaks": measured,
     }
-    keep = ("ms_per_step", "tokens_per_s", "roofline", "grouped_gemm", "layer", "routing",
-            "step_ms_p10_p50_p90", "fp8", "mxfp4")
-    if not args.all and not args.no_decode and args.workload != DECODE_WORKLOAD:
-        # the metric's second half: decode-shaped batches against HBM bandwidth
-        r = run_workload(DECODE_WORKLOAD, args.steps, args.warmup, False, 0, not args.no_fp8,
-                         not args.no_mxfp4)
-        line["decode"] = dict({kk: r.get(kk) for kk in keep}, workload=DECODE_WORKLOAD)
-    if args.all:
-        others = {}
-        for name in CONFIGS:
-            if name == args.workload:
-                continue
-            r = run_workload(name, args.steps, args.warmup, False, 0, not args.no_fp8,
-                             not args.no_mxfp4)
-            others[name] = {kk: r.get(kk) for kk in keep}
+    keep = ("ms_per_step", "tokens_per_s", "roofline", "grouped_gemm", "combine", "layer",
+            "routing", "step_ms_p10_p50_p90", "hash_pass", "fp8", "mxfp4")
+    side = [] if args.side in ("", "none") else [w for w in args.side.split(",")
+                                                 if w != args.workload]
+    others = {}
+    for name in side:
+        r = run_workload(name, args.steps, args.warmup, False, 0, not args.no_fp8,
+                         not args.no_mxfp4, measured)
+        others[name] = {kk: r.get(kk) for kk in keep if r.get(kk) is not None}
+    if others:
         line["workloads"] = others
     if not args.no_peaks:
         line["context"] = peaks()
