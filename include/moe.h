@@ -29,8 +29,9 @@
  *    device memory, frees or synchronises.  Work is queued on `stream` (a
  *    hipStream_t; NULL is the default stream) and completes asynchronously.
  *    Calls with distinct workspaces may run concurrently.
- *  - The library keeps no state between calls: no streams, events, handles
- *    or memory of its own.  Every launch of a call goes to `stream`, in order.
+ *  - The library keeps no state between calls (no streams, events or handles
+ *    of its own), except moe_forward_noalloc's static scratch (below).  Every
+ *    launch of a call goes to `stream`, in order.
  *  - Floating-point tensors (hidden, weights, expert outputs, out) are float32
  *    when cfg->dtype == MOE_F32 and bfloat16 when MOE_BF16.  Logits, gates, bias
  *    and logit offsets are always float32; accumulation is always float32.
@@ -61,7 +62,8 @@ typedef enum {
     MOE_ERR_INVALID_ARG = -1, /* null required pointer, inconsistent sizes */
     MOE_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels handle */
     MOE_ERR_WORKSPACE = -3,   /* workspace too small (see moe_workspace_size) */
-    MOE_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+    MOE_ERR_HIP = -4,         /* a HIP launch or runtime call failed */
+    MOE_ERR_TOO_LARGE = -5    /* moe_forward_noalloc: workspace beyond its static scratch */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -171,6 +173,26 @@ int moe_forward(const moe_config *cfg, const void *hidden, const void *w_router,
                 const void *w13_shared, const void *w2_shared, void *out,
                 int32_t *topk_ids_out, float *topk_weights_out, void *workspace,
                 size_t workspace_bytes, void *stream);
+
+/* moe_forward without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the workspace is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES in the library (one copy per GPU, held until the
+ * process ends; its address is looked up once per device on the first call
+ * there).  Arguments and results as moe_forward.  A configuration whose
+ * workspace (moe_workspace_size) exceeds the scratch returns MOE_ERR_TOO_LARGE
+ * before any launch: 64 MiB holds decode-shaped batches, e.g. T up to ~770 at
+ * d = 4096, d_ff = 2048, k = 6 with a shared expert.  Nothing in the scratch
+ * needs clearing between calls (every region is written before it is read).
+ * All calls on one GPU share its scratch: calls that overlap in time on one
+ * GPU (two streams, two threads) race and must be serialised by the caller.
+ * The call allocates and frees nothing. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_forward_noalloc(const moe_config *cfg, const void *hidden, const void *w_router,
+                        const float *logit_offset, const float *bias, const int32_t *token_ids,
+                        const int32_t *tid2eid, const void *w13, const void *w2,
+                        const void *w13_shared, const void *w2_shared, void *out,
+                        int32_t *topk_ids_out, float *topk_weights_out, void *stream);
 
 /* ---------------------------------------------------------------------------
  * FP8 experts.  Codes are E4M3 (the OCP "FN" encoding: sign, 4 exponent bits with

@@ -16,12 +16,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_ERR_TOO_LARGE = -5
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SQRTSOFTPLUS = 0, 1, 2
 MOE_ROUTE_LEARNED, MOE_ROUTE_HASH = 0, 1
 
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_up",
-           "moe_expert_down", "moe_combine", "moe_forward", "moe_quantize_fp8_rows",
+           "moe_expert_down", "moe_combine", "moe_forward", "moe_forward_noalloc",
+           "moe_quantize_fp8_rows",
            "moe_quantize_fp8_blocks", "moe_expert_up_fp8", "moe_expert_down_fp8",
            "moe_forward_fp8", "moe_quantize_mxfp4", "moe_expert_up_mxfp4",
            "moe_expert_down_mxfp4", "moe_forward_mxfp4", "moe_strerror")
@@ -73,6 +76,7 @@ def load_library(path: str = LIB_PATH):
     L.moe_expert_down.argtypes = [cfg, P, P, P, P, P, S, P]
     L.moe_combine.argtypes = [cfg, P, P, P, P, P, P]
     L.moe_forward.argtypes = [cfg, P, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
+    L.moe_forward_noalloc.argtypes = [cfg, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
     L.moe_quantize_fp8_rows.argtypes = [I, I, I, P, P, P, P]
     L.moe_quantize_fp8_blocks.argtypes = [I, I, I, P, P, P, P]
     L.moe_expert_up_fp8.argtypes = [cfg, P, P, P, P, P, P, P, P, P, S, P]
@@ -249,6 +253,31 @@ def moe_forward(cfg, hidden, w_router, logit_offset, bias, token_ids, tid2eid, w
             _t("topk_weights_out", topk_weights_out, (T, k), torch.float32, False),
             *_ws(cfg, workspace), _stream(stream)]
     _check("moe_forward", load_library().moe_forward(*args))
+
+
+def moe_forward_noalloc(cfg, hidden, w_router, logit_offset, bias, token_ids, tid2eid, w13, w2,
+                        w13_shared, w2_shared, out, topk_ids_out, topk_weights_out,
+                        stream=None):
+    """moe_forward with the library's static scratch as its workspace (no
+    allocation); configurations needing more than MOE_NOALLOC_SCRATCH_BYTES of
+    workspace raise with MOE_ERR_TOO_LARGE."""
+    dt, T, d, E, k, F = cfg.torch_dtype, cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
+    hsh = cfg.route_mode == MOE_ROUTE_HASH
+    sh = bool(cfg.n_shared)
+    args = [C.byref(cfg),
+            _t("hidden", hidden, (T, d), dt), _t("w_router", w_router, (E, d), dt),
+            _t("logit_offset", logit_offset, (E,), torch.float32, False),
+            _t("bias", bias, (E,), torch.float32, False),
+            _t("token_ids", token_ids, (T,), torch.int32, hsh),
+            _t("tid2eid", tid2eid, (cfg.vocab, k), torch.int32, hsh),
+            _t("w13", w13, (E, 2 * F, d), dt), _t("w2", w2, (E, d, F), dt),
+            _t("w13_shared", w13_shared, (2 * F, d), dt, sh),
+            _t("w2_shared", w2_shared, (d, F), dt, sh),
+            _t("out", out, (T, d), dt),
+            _t("topk_ids_out", topk_ids_out, (T, k), torch.int32, False),
+            _t("topk_weights_out", topk_weights_out, (T, k), torch.float32, False),
+            _stream(stream)]
+    _check("moe_forward_noalloc", load_library().moe_forward_noalloc(*args))
 
 
 _IN_DTYPES = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}

@@ -1,7 +1,9 @@
 // C ABI entry points (include/moe.h): argument checks on the host, workspace
-// carve-up, and the launch sequence on the caller's stream.  The library keeps
-// no state between calls and never allocates or synchronises.
+// carve-up, and the launch sequence on the caller's stream.  The library never
+// allocates or synchronises; the only state it keeps is, per device, the
+// address of moe_forward_noalloc's static scratch array.
 #include <algorithm>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -88,6 +90,29 @@ int check_fp8(const moe_config* c) {
   const int64_t P = T * (c->k + c->n_shared);
   if (T * d >= lim || P * F >= lim || 2 * F * d >= lim || P * (F / 128) * 4 >= lim)
     return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// The workspace of moe_forward_noalloc: a static device array (one copy on
+// every GPU the library runs on, held until the process ends).  Host code
+// never passes the array's name to a kernel: its address on a device comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+int noalloc_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
   return MOE_OK;
 }
 
@@ -305,6 +330,23 @@ int moe_forward(const moe_config* cfg, const void* hidden, const void* w_router,
   const int64_t es = c.dtype == MOE_F32 ? 4 : 2;
   const char* shared_rows = c.n_shared ? at<char>(workspace, w.Y) + (int64_t)R * c.d * es : nullptr;
   return hip_status(launch_combine(c, a.Y, dispatch, gates, shared_rows, out, s));
+}
+
+int moe_forward_noalloc(const moe_config* cfg, const void* hidden, const void* w_router,
+                        const float* logit_offset, const float* bias, const int32_t* token_ids,
+                        const int32_t* tid2eid, const void* w13, const void* w2,
+                        const void* w13_shared, const void* w2_shared, void* out,
+                        int32_t* topk_ids_out, float* topk_weights_out, void* stream) {
+  const int st = check_cfg(cfg);
+  if (st) return st;
+  if (workspace_layout(*cfg).total > (int64_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_TOO_LARGE;
+  if (cfg->T == 0) return MOE_OK;
+  void* ws = nullptr;
+  const int sst = noalloc_scratch(&ws);
+  if (sst) return sst;
+  return moe_forward(cfg, hidden, w_router, logit_offset, bias, token_ids, tid2eid, w13, w2,
+                     w13_shared, w2_shared, out, topk_ids_out, topk_weights_out, ws,
+                     MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int moe_quantize_fp8_rows(int n, int K, int in_dtype, const void* x, uint8_t* q, float* scales,
@@ -549,6 +591,7 @@ const char* moe_strerror(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_HIP: return "HIP launch or runtime error";
+    case MOE_ERR_TOO_LARGE: return "workspace larger than the no-alloc entry point's scratch";
     default: return "unknown status";
   }
 }

@@ -196,3 +196,19 @@ def test_peaks_reject_bad_arguments_on_the_host():
     assert L.moe_peaks_mfma(0, None, 1, 4, p, None) == -1
     assert L.moe_peaks_read(p, 4095, 1, p, None) == -1      # not a multiple of 4096
     assert L.moe_peaks_read(p, 4096, 0, p, None) == -1
+
+
+def test_noalloc_rejects_on_the_host():
+    """moe_forward_noalloc: argument errors and a workspace beyond its static
+    scratch are reported before any launch (no GPU is touched here)."""
+    L = moe.load_library()
+    p = C.c_void_p(16)  # never dereferenced
+    args = [p] * 13 + [None]
+    big = cfg(T=4096, d=4096, E=8, k=2, d_ff=14336, dtype="bf16")
+    assert L.moe_forward_noalloc(C.byref(big), *args) == B.MOE_ERR_TOO_LARGE
+    n = C.c_size_t(0)
+    assert L.moe_workspace_size(C.byref(big), C.byref(n)) == 0 and n.value > B.MOE_NOALLOC_SCRATCH_BYTES
+    assert L.moe_forward_noalloc(C.byref(cfg(k=9)), *args) == -1
+    assert L.moe_forward_noalloc(C.byref(cfg(d=96)), *args) == -2
+    assert L.moe_forward_noalloc(C.byref(cfg(T=0)), *args) == 0  # nothing to do, nothing queued
+    assert "scratch" in moe.moe_strerror(B.MOE_ERR_TOO_LARGE)
