@@ -198,6 +198,25 @@ hipError_t launch_fp8(const Fp8Args& q, int m_tiles_bound, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The two tile lists of a skewed prefill-shaped batch in one launch
+// (grouped_gemm_fp8_split): Small's 32-row streaming tiles of `small` on the
+// first kSmallGroupBlocks blocks, one Big tile of `big` on each later block.
+template <class Big, class Small, int EPI, int WF>
+hipError_t launch_fp8_split(const Fp8Args& big, int big_m_tiles, const Fp8Args& small,
+                            hipStream_t s) {
+  constexpr int LDS_B = Big::ST * fp8_stage_bytes<Big::BM, Big::BN, WF>();
+  constexpr int LDS_S = Small::ST * fp8_stage_bytes<32, Small::BN, WF>();
+  constexpr int LDS = LDS_B > LDS_S ? LDS_B : LDS_S;
+  const int grid = kSmallGroupBlocks + xcd_grid((int64_t)big_m_tiles * big.g.n_tiles);
+  auto kern = grouped_gemm_fp8_split<Big, Small, EPI, WF>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * Big::WAVES), LDS, s, big, small,
+                     kSmallGroupBlocks);
+  return hipGetLastError();
+}
+
 int tile_bound8(int64_t rows, int groups, int bm) {
   const int64_t ne = rows < groups ? rows : groups;
   return (int)((rows + ne * (bm - 1)) / bm);
@@ -306,13 +325,26 @@ hipError_t launch_expert_up_fp8(const moe_config& c, const Fp8FfnArgs& a, hipStr
     // V4-Pro 4.42 -> 3.97 ms, Mixtral 0.97 -> 0.92 ms, DeepSeek-V3 2.23 ->
     // 2.07 ms against one block of 256x256 per CU.  (An E4M3 tile of the same
     // shape needs 100 KB: one block per CU.)
+    // (these tiles keep the groups of a few rows: splitting those off onto
+    // streaming tiles in the same launch, as for E4M3 below, measured neutral
+    // on V4-Pro's up GEMM and 3% slower on its down GEMM)
     g.tile_prefix = a.tile_prefix + tile_height_index(128) * (a.n_groups + 1);
     return launch_fp8<128, 256, 2, 4, EPI_SWIGLU8, 2, WF_MXFP4>(
         q, tile_bound8(a.rows_bound, a.n_groups, 128), s);
   }
-  g.tile_prefix = a.tile_prefix + tile_height_index(256) * (a.n_groups + 1);
   const int mt = tile_bound8(a.rows_bound, a.n_groups, 256);
-  // scheduled main loop (0-2% faster)
+  // groups of a few rows on a skewed load: one 32-row streaming tile each,
+  // walked by a few blocks of the same launch as the 256-row tiles (V4-Pro's
+  // up GEMM 5.03-5.05 -> 4.91-4.92 ms; DeepSeek-V3, without such groups,
+  // unchanged).  Scheduled main loop (0-2% faster).
+  if (split_small_groups(a.rows_bound, a.n_groups)) {
+    Fp8Args qs = q;
+    qs.g.tile_prefix = a.tile_prefix + kListSmall32 * (a.n_groups + 1);
+    g.tile_prefix = a.tile_prefix + kListLarge256 * (a.n_groups + 1);
+    return launch_fp8_split<Fp8Tile<256, 256, 4, 2, 2, 1>, Fp8Tile<32, 256, 1, 4, 2>, EPI_SWIGLU8,
+                            WF_E4M3>(q, mt, qs, s);
+  }
+  g.tile_prefix = a.tile_prefix + tile_height_index(256) * (a.n_groups + 1);
   return launch_fp8<256, 256, 4, 2, EPI_SWIGLU8, 2, WF_E4M3, 1>(q, mt, s);
 }
 
@@ -366,11 +398,21 @@ hipError_t launch_expert_down_fp8(const moe_config& c, const Fp8FfnArgs& a, hipS
     return launch_fp8<128, 256, 2, 4, EPI_STORE, 2, WF_MXFP4>(
         q, tile_bound8(a.rows_bound, a.n_groups, 128), s);
   }
-  g.tile_prefix = a.tile_prefix + tile_height_index(256) * (a.n_groups + 1);
   const int mt = tile_bound8(a.rows_bound, a.n_groups, 256);
   // scheduled main loop (within 1%; the 288-row tiles above keep the
   // compiler's order: their double-buffered fragments would not fit in the
-  // registers of three waves per SIMD)
+  // registers of three waves per SIMD).  Groups of a few rows on a skewed
+  // load: 32 x 128 streaming tiles in the same launch, as for the up GEMM
+  // (V4-Pro's down GEMM 2.67 -> 2.60-2.63 ms).
+  if (split_small_groups(a.rows_bound, a.n_groups)) {
+    Fp8Args qs = q;
+    qs.g.n_tiles = ceil_div(c.d, 128);
+    qs.g.tile_prefix = a.tile_prefix + kListSmall32 * (a.n_groups + 1);
+    g.tile_prefix = a.tile_prefix + kListLarge256 * (a.n_groups + 1);
+    return launch_fp8_split<Fp8Tile<256, 256, 4, 4, 2, 1>, Fp8Tile<32, 128, 1, 4, 3>, EPI_STORE,
+                            WF_E4M3>(q, mt, qs, s);
+  }
+  g.tile_prefix = a.tile_prefix + tile_height_index(256) * (a.n_groups + 1);
   return launch_fp8<256, 256, 4, 4, EPI_STORE, 2, WF_E4M3, 1>(q, mt, s);
 }
 

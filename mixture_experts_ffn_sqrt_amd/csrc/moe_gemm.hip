@@ -66,35 +66,19 @@ int tile_bound(int64_t rows, int groups, int bm) {
   return (int)((rows + ne * (bm - 1)) / bm);
 }
 
-// Row tiles of list kListSmall32: one per group of at most kSmallGroupRows rows.
-int small_group_bound(const ExpertFfnArgs& a) {
-  return (int)(a.rows_bound < a.n_groups ? a.rows_bound : a.n_groups);
-}
-
-// Whether a prefill-shaped launch splits off the groups of a few rows.  Not
-// when the groups average 512 rows or more (Mixtral's 8 experts): few groups
-// can be that small then, and the launch of the streaming tiles would mostly
-// be empty blocks (about 4.5 us each for GEMM 1 and GEMM 2); the 288-row
-// tiles then take every group.
 bool split_small_groups(const ExpertFfnArgs& a) {
-  return a.rows_bound < (int64_t)512 * a.n_groups;
+  return moe::split_small_groups(a.rows_bound, a.n_groups);
 }
 
-// Blocks that walk the small groups' streaming tiles when they share the up
-// GEMM's launch with the 288-row tiles (a multiple of 8; one block per CU).
-// V4-Pro's up GEMM (127 groups of at most 32 rows): 9.11 ms with the two
-// kinds of tile in two launches in sequence, 8.61 ms with the streaming tiles
-// on 64 CUs beside the 288-row tiles (8.77 on 32, 8.69 on 128).
-constexpr int kSmallGroupBlocks = 64;
-
-// The up GEMM's two tile lists in one launch (grouped_gemm_dma_split): the
-// streaming tiles of `small` on the first kSmallGroupBlocks blocks, one
-// 288-row tile of `big` on each later block.
-hipError_t launch_up_split(const GemmArgs& big, int big_m_tiles, const GemmArgs& small,
-                           hipStream_t s) {
+// A grouped GEMM's two tile lists in one launch (grouped_gemm_dma_split): the
+// 32 x 256 streaming tiles of `small` on the first kSmallGroupBlocks blocks,
+// one 288 x 256 tile of `big` on each later block.
+template <int EPI>
+hipError_t launch_split(const GemmArgs& big, int big_m_tiles, const GemmArgs& small,
+                        hipStream_t s) {
   const int big_grid = xcd_grid((int64_t)big_m_tiles * big.n_tiles);
   const int grid = kSmallGroupBlocks + big_grid;
-  auto kern = grouped_gemm_dma_split<EPI_SWIGLU>;
+  auto kern = grouped_gemm_dma_split<EPI>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, kSplitLds);
   if (e != hipSuccess) return e;
@@ -239,7 +223,7 @@ hipError_t launch_expert_up(const moe_config& c, const ExpertFfnArgs& a, hipStre
       GemmArgs gs = g;
       gs.tile_prefix = a.tile_prefix + kListSmall32 * (a.n_groups + 1);
       g.tile_prefix = a.tile_prefix + kListLarge288 * (a.n_groups + 1);
-      return launch_up_split(g, mb, gs, s);
+      return launch_split<EPI_SWIGLU>(g, mb, gs, s);
     }
     default:
       g.n_tiles = c.d_ff / 64;
@@ -284,22 +268,17 @@ hipError_t launch_expert_down(const moe_config& c, const ExpertFfnArgs& a, hipSt
     case FfnTiles::BF16_PREFILL: {
       g.a_bytes = (uint32_t)((int64_t)a.rows_bound * F * es);
       g.b_bytes = (uint32_t)(d * F * es);
-      // groups of a few rows: one 32-row streaming tile each (in sequence
-      // with the 288-row tiles: running them beside those, as the up GEMM
-      // does, measured no faster here)
-      if (split_small_groups(a)) {
-        GemmArgs gs = g;
-        gs.n_tiles = ceil_div(c.d, 128);
-        gs.tile_prefix = a.tile_prefix + kListSmall32 * (a.n_groups + 1);
-        const hipError_t e =
-            launch_gemm_dma<32, 128, 1, 2, EPI_STORE, 4, 128, 3>(gs, small_group_bound(a), s);
-        if (e != hipSuccess) return e;
-        g.tile_prefix = a.tile_prefix + kListLarge288 * (a.n_groups + 1);
-      }
-      // the others: 288-row tiles with the scheduled main loop (Mixtral's down
-      // GEMM 0.88 -> 0.83 ms against the compiler's order)
       g.n_tiles = ceil_div(c.d, 256);
-      return launch_gemm_dma<288, 256, 3, 4, EPI_STORE, 2, 128, 3, 1>(g, mb, s);
+      // 288-row tiles with the scheduled main loop (Mixtral's down GEMM 0.88 ->
+      // 0.83 ms against the compiler's order)
+      if (!split_small_groups(a))
+        return launch_gemm_dma<288, 256, 3, 4, EPI_STORE, 2, 128, 3, 1>(g, mb, s);
+      // groups of a few rows: one 32-row streaming tile each, walked by a few
+      // blocks of the same launch
+      GemmArgs gs = g;
+      gs.tile_prefix = a.tile_prefix + kListSmall32 * (a.n_groups + 1);
+      g.tile_prefix = a.tile_prefix + kListLarge288 * (a.n_groups + 1);
+      return launch_split<EPI_STORE>(g, mb, gs, s);
     }
     default:
       g.n_tiles = ceil_div(c.d, 128);

@@ -103,10 +103,11 @@ __host__ __device__ constexpr int fp8_stage_bytes() {
          (WF == WF_MXFP4 ? BN * 4 : 256);
 }
 
+// One tile of grouped_gemm_fp8 (below).
 // SCHED = 1: fragments double-buffered in registers across the two k-steps of
 // a stage, in the order sched_stage fixes (full tiles only).
 template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int WF = WF_E4M3, int SCHED = 0>
-__global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
+__device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& q, const TileCoord& tc) {
   const GemmArgs& p = q.g;
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -141,8 +142,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
   static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024, "LDS budget");
   extern __shared__ __align__(16) char smem[];
 
-  TileCoord tc;
-  if (!decode_tile<BM>(p, tc)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
@@ -441,6 +440,45 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
       }
     }
   }
+}
+
+// FP8 / MXFP4 grouped GEMM: one tile per block.
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int WF = WF_E4M3, int SCHED = 0>
+__global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_fp8(Fp8Args q) {
+  TileCoord tc;
+  if (!decode_tile<BM>(q.g, tc)) return;
+  gemm_fp8_tile<BM, BN, WM, WN, EPI, STAGES, WF, SCHED>(q, tc);
+}
+
+// A tile shape of grouped_gemm_fp8_split: gemm_fp8_tile's parameters.
+template <int BM_, int BN_, int WM_, int WN_, int ST_, int SCHED_ = 0>
+struct Fp8Tile {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, ST = ST_, SCHED = SCHED_;
+  static constexpr int WAVES = WM_ * WN_;
+};
+
+// Both kinds of tile of a prefill-shaped batch with a skewed load in one
+// launch, as grouped_gemm_dma_split does for bf16: blocks [0, n_small) walk the
+// 32-row streaming tiles of `small` (Small's waves; the others end at once,
+// and a barrier then waits only for the waves still running), every later
+// block takes one Big tile of `big`.  The two roles write disjoint rows.
+template <class Big, class Small, int EPI, int WF>
+__global__ __launch_bounds__(64 * Big::WAVES, 1) void grouped_gemm_fp8_split(Fp8Args big,
+                                                                            Fp8Args small,
+                                                                            int n_small) {
+  static_assert(Small::WAVES <= Big::WAVES && Small::BM == 32, "streaming role");
+  TileCoord tc;
+  const int bid = blockIdx.x;
+  if (bid < n_small) {
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= Small::WAVES) return;
+    for (int vb = bid; decode_tile<32>(small.g, tc, vb); vb += n_small) {
+      if (vb != bid) __syncthreads();
+      gemm_fp8_tile<32, Small::BN, Small::WM, Small::WN, EPI, Small::ST, WF, Small::SCHED>(small, tc);
+    }
+    return;
+  }
+  if (!decode_tile<Big::BM>(big.g, tc, bid - n_small)) return;
+  gemm_fp8_tile<Big::BM, Big::BN, Big::WM, Big::WN, EPI, Big::ST, WF, Big::SCHED>(big, tc);
 }
 
 }  // namespace gemm

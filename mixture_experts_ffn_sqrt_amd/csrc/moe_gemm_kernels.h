@@ -678,9 +678,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) 
   gemm_dma_tile<BM, BN, WM, WN, EPI, STAGES, ROWB, SWZ, SCHED>(p, tc);
 }
 
-// Tile shapes of the two roles of grouped_gemm_dma_split (the up GEMM of a
-// prefill-shaped batch with a skewed load): 288 x 256 tiles on 12 waves with
-// the scheduled main loop for the groups of more than 32 rows, and 32-row
+// Tile shapes of the two roles of grouped_gemm_dma_split (the grouped GEMMs of
+// a prefill-shaped batch with a skewed load): 288 x 256 tiles on 12 waves with
+// the scheduled main loop for the groups of more than 32 rows, and 32 x 256
 // streaming tiles (4 waves, a four-stage ring of weight loads) for the others.
 constexpr int kSplitBigWaves = 12, kSplitSmallWaves = 4;
 constexpr int kSplitLds = 4 * (32 + 256) * 128;  // the larger of the two rings

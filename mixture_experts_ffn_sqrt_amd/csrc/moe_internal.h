@@ -50,18 +50,23 @@ __host__ __device__ constexpr int group_tiles(int M, int bm) {
   return M <= 0 ? 0 : ceil_div(M, group_tile_rows(M, bm));
 }
 
-// Two more lists split the groups by size, for prefill-shaped batches whose
+// More lists split the groups by size, for prefill-shaped batches whose
 // routing leaves some experts a few rows (a skewed load): the groups with at
 // most kSmallGroupRows rows get one 32-row tile each (list kListSmall32), run
 // on the streaming tiles that keep a deep ring of weight loads in flight; the
-// others get 288-row tiles (list kListLarge288).
+// others get tiles of the GEMM's prefill height (bf16: 288 rows, list
+// kListLarge288; E4M3: 256, kListLarge256).
 constexpr int kSmallGroupRows = 32;
 constexpr int kListLarge288 = kNumTileHeights, kListSmall32 = kNumTileHeights + 1;
-constexpr int kNumTileLists = kNumTileHeights + 2;
+constexpr int kListLarge256 = kNumTileHeights + 2;
+constexpr int kNumTileLists = kNumTileHeights + 3;
+__host__ __device__ constexpr int large_list_height(int list) {
+  return list == kListLarge288 ? 288 : 256;
+}
 __host__ __device__ constexpr int list_tiles(int list, int M) {
   return list < kNumTileHeights ? group_tiles(M, tile_height(list))
-         : list == kListLarge288 ? (M > kSmallGroupRows ? group_tiles(M, 288) : 0)
-                                 : (M > kSmallGroupRows ? 0 : group_tiles(M, 32));
+         : list == kListSmall32 ? (M > kSmallGroupRows ? 0 : group_tiles(M, 32))
+                                : (M > kSmallGroupRows ? group_tiles(M, large_list_height(list)) : 0);
 }
 
 // Consecutive tiles of a grouped GEMM's tile order that run on one XCD (see
@@ -81,6 +86,22 @@ inline int xcd_grid(int64_t tiles) {
 inline bool tall_down_tiles(int64_t rows_bound, int n_groups) {
   return n_groups > 0 && rows_bound >= (int64_t)512 * n_groups;
 }
+
+// Whether a prefill-shaped batch's grouped GEMMs split off the groups of a few
+// rows onto streaming tiles.  Not when the groups average 512 rows or more
+// (Mixtral's 8 experts): few groups can be that small then, and the streaming
+// blocks would mostly be empty; the large tiles then take every group.
+inline bool split_small_groups(int64_t rows_bound, int n_groups) {
+  return rows_bound < (int64_t)512 * n_groups;
+}
+
+// Blocks that walk the small groups' streaming tiles when they share a launch
+// with the large tiles (a multiple of 8; one block per CU).  V4-Pro's bf16 up
+// GEMM (127 groups of at most 32 rows): 9.11 ms with the two kinds of tile in
+// two launches in sequence, 8.61 ms with the streaming tiles on 64 CUs beside
+// the 288-row tiles (8.77 on 32, 8.69 on 128); its down GEMM 4.66-4.71 ->
+// 4.57-4.63 ms (three rounds; 96 blocks: 4.63-4.64).
+constexpr int kSmallGroupBlocks = 64;
 
 // pairs handled by one histogram / scatter block of the permutation
 constexpr int kPermuteChunk = 256;   // pairs per histogram / scatter chunk

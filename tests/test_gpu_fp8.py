@@ -23,6 +23,8 @@ import parity_helpers as H
 
 pytestmark = pytest.mark.gpu
 
+MIXED_SIZES = [0, 1, 31, 32, 33, 64, 300, 1100]
+
 TOL = 2e-2
 # The layer: a row's output sums d_ff terms of H; where one of its H codes is one
 # E4M3 step (12.5% of that element) away from the oracle's, the row can move by
@@ -81,12 +83,18 @@ def _dev(a):
     (300, 384, 3, 3, 128),      # k = E, d not a multiple of 256 (partial column tile)
     (2100, 384, 4, 2, 128),     # ~1050 rows per expert: 288x256 down tiles, partial column tile
     (1300, 256, 2, 1, 128),     # ~650 rows per expert: 288-row down tiles, ragged last row tile
+    # groups of 0, 1, 31, 32, 33, 64, 300 and 1100 rows (195 on average): the
+    # groups of at most 32 rows on 32-row streaming tiles, in the same launch as
+    # the large tiles of the others (E4M3)
+    (1561, 256, 8, 1, 256),
 ])
 def test_expert_up_down_fp8(T, d, E, k, d_ff):
     lc = CONFIGS["mixtral_prefill"].with_(T=T, d=d, E=E, k=k, d_ff=d_ff, seed=31)
     inp = make_inputs(lc, "cuda")
     rng = np.random.default_rng(T)
     ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    if T == 1561:  # explicit group sizes (see the case list)
+        ids = rng.permutation(np.repeat(np.arange(E), MIXED_SIZES)).astype(np.int32)[:, None]
     perm = O.permute(ids, np.ones((T, k), np.float32), E)
     c = H.cfg_of(lc)
     ws = torch.empty(moe.moe_workspace_size(c), dtype=torch.uint8, device="cuda")
@@ -162,6 +170,10 @@ FP8_LAYERS = {
     "decode_T1": CONFIGS["v4flash_decode"].with_(T=1, d=256, d_ff=128),
     "single_expert": CONFIGS["mixtral_prefill"].with_(T=100, d=256, E=1, k=1, d_ff=128),
     "mixtral_tall_tiles": CONFIGS["mixtral_prefill"].with_(T=2048, d=256, d_ff=256),
+    # about 70 experts of at most 32 rows beside larger ones: the E4M3 GEMMs run
+    # them on streaming tiles in the same launches as the 256-row tiles
+    "v4pro_skew_many_small": CONFIGS["v4pro_skew_prefill"].with_(T=4096, d=256, E=128, k=6,
+                                                                 d_ff=1024),
 }
 
 
@@ -216,9 +228,11 @@ def test_forward_fp8_full_size(name, n_rows):
     H.check_quantized_tiles(inp, fp8, "fp8", seed=lc.seed)
 
 
-@pytest.mark.parametrize("name", ["mixtral_small", "mixtral_tall_tiles"])
+@pytest.mark.parametrize("name", ["mixtral_small", "mixtral_tall_tiles", "v4pro_skew_many_small"])
 def test_forward_fp8_batch_invariant(name):
-    # mixtral_tall_tiles: the full batch's down GEMM runs 288-row tiles
+    # mixtral_tall_tiles: the full batch's down GEMM runs 288-row tiles;
+    # v4pro_skew_many_small: the full batch runs its small groups on streaming
+    # tiles beside the 256-row tiles, the slices 32-row tiles throughout
     lc = FP8_LAYERS[name]
     inp = make_inputs(lc, "cuda")
     fp8 = moe.quantize_fp8_weights(inp)

@@ -23,6 +23,8 @@ import parity_helpers as H
 
 pytestmark = pytest.mark.gpu
 
+MIXED_SIZES = [0, 1, 31, 32, 33, 64, 300, 1100]
+
 TOL = 2e-2
 LAYER_TOL, LAYER_MEDIAN_TOL = 5e-2, 1e-2
 
@@ -97,12 +99,18 @@ def _dev(a):
     (1, 512, 8, 2, 256),        # one token
     (2100, 384, 4, 2, 128),     # ~1050 rows per expert: 288x256 down tiles, partial column tile
     (1300, 256, 2, 1, 128),     # ~650 rows per expert: 288-row down tiles, ragged last row tile
+    # groups of 0, 1, 31, 32, 33, 64, 300 and 1100 rows (195 on average): the
+    # groups of at most 32 rows on 32-row streaming tiles, in the same launch as
+    # the large tiles of the others (E4M3)
+    (1561, 256, 8, 1, 256),
 ])
 def test_expert_up_down_mxfp4(T, d, E, k, d_ff):
     lc = CONFIGS["mixtral_prefill"].with_(T=T, d=d, E=E, k=k, d_ff=d_ff, seed=37)
     inp = make_inputs(lc, "cuda")
     rng = np.random.default_rng(T + 1)
     ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    if T == 1561:  # explicit group sizes (see the case list)
+        ids = rng.permutation(np.repeat(np.arange(E), MIXED_SIZES)).astype(np.int32)[:, None]
     perm = O.permute(ids, np.ones((T, k), np.float32), E)
     c = H.cfg_of(lc)
     ws = torch.empty(moe.moe_workspace_size(c), dtype=torch.uint8, device="cuda")
@@ -171,6 +179,8 @@ MX_LAYERS = {
     "decode_T1": CONFIGS["v4flash_decode"].with_(T=1, d=256, d_ff=128),
     "single_expert": CONFIGS["mixtral_prefill"].with_(T=100, d=256, E=1, k=1, d_ff=128),
     "mixtral_tall_tiles": CONFIGS["mixtral_prefill"].with_(T=2048, d=256, d_ff=256),
+    "v4pro_skew_many_small": CONFIGS["v4pro_skew_prefill"].with_(T=4096, d=256, E=128, k=6,
+                                                                 d_ff=1024),
 }
 
 
