@@ -25,8 +25,11 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        path = _build.LIB
-        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+        # MOE_ORACLE_LIB: a library built from a modified copy of moe_oracle.c,
+        # so that a test can plant a mistake in the oracle and see the pins fail
+        path = os.environ.get("MOE_ORACLE_LIB") or _build.LIB
+        if path == _build.LIB and (not os.path.exists(path) or
+                                   os.path.getmtime(path) < os.path.getmtime(_build.SRC)):
             _build.build()
         L = C.CDLL(path)
         P, I, F = C.c_void_p, C.c_int, C.c_float

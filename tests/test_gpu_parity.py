@@ -109,6 +109,22 @@ def test_route_from_given_logits(case):
         assert max(len(np.unique(r // G)) for r in ids) <= grp["topk_group"]
 
 
+@pytest.mark.parametrize("scoring", [O.SOFTMAX, O.SIGMOID])
+def test_group_limited_routing_worked_example(golden, scoring):
+    """The hand-built node-limited routing example of [P3] 五.3 (1 + 3 + 2 + 2
+    experts over the 4 kept groups), from given logits (see the oracle pin)."""
+    g = golden("group_limited_routing_example.json")
+    keys = np.array([g["keys"]], np.float32)
+    grp = dict(n_group=g["n_group"], topk_group=g["topk_group"], group_topk=g["group_topk"])
+    if scoring == O.SOFTMAX:
+        ids, _ = gpu_route_given(keys, g["k"], scoring, **grp)
+    else:
+        ids, gates = gpu_route_given(np.full_like(keys, -200.0), g["k"], scoring, bias=keys[0],
+                                     **grp)
+        assert np.all(gates == np.float32(1.0 / g["k"]))
+    assert ids[0].tolist() == g["expected_ids"]
+
+
 def test_zero_denominator_gates():
     lg = np.full((3, 8), -200.0, np.float32)
     ids, gates = gpu_route_given(lg, 2, O.SQRTSOFTPLUS)

@@ -218,6 +218,39 @@ def test_group_routing_matches_array_formulation():
     assert (np.sort(flat, 1) != np.sort(ids, 1)).any(axis=1).sum() > 10
 
 
+@pytest.mark.parametrize("scoring", [O.SOFTMAX, O.SIGMOID])
+def test_group_limited_routing_worked_example(golden, scoring):
+    """[P3] 五.3's node-limited rule on hand-built keys realising its figure's
+    1 + 3 + 2 + 2 split (tests/golden/group_limited_routing_example.json).
+    Softmax: the keys are the logits.  Sigmoid: logits of -200 give affinity 0
+    (float underflow), so the keys are the bias, which therefore enters the
+    group scores (selection keys, reading R6); the gates fall back to 1/k."""
+    g = golden("group_limited_routing_example.json")
+    keys = np.array([g["keys"]], np.float32)
+    grp = dict(n_group=g["n_group"], topk_group=g["topk_group"], group_topk=g["group_topk"])
+    if scoring == O.SOFTMAX:
+        ids, gates, margin = O.route(keys, g["k"], scoring, **grp)
+    else:
+        ids, gates, margin = O.route(np.full_like(keys, -200.0), g["k"], scoring, bias=keys[0],
+                                     **grp)
+        assert np.all(gates == np.float32(1.0 / g["k"]))
+    assert ids[0].tolist() == g["expected_ids"]
+    G = keys.shape[1] // g["n_group"]
+    assert sorted(set((ids[0] // G).tolist())) == g["expected_kept_groups"]
+    split = [int((ids[0] // G == grp_).sum()) for grp_ in g["expected_kept_groups"]]
+    assert split == g["expected_split"]
+    assert margin[0] > 0.01  # no decision is near a tie
+    # the misreadings named in the fixture really do differ from the rule
+    assert g["misreadings"]["global_top8"] != g["expected_ids"]
+    top8 = np.argsort(-keys[0], kind="stable")[:g["k"]].tolist()
+    assert top8 == g["misreadings"]["global_top8"]
+    kg = keys[0].reshape(g["n_group"], G)
+    by_max = sorted(np.argsort(-kg.max(1), kind="stable")[:g["topk_group"]].tolist())
+    by_sum = sorted(np.argsort(-kg.sum(1), kind="stable")[:g["topk_group"]].tolist())
+    assert by_max == g["misreadings"]["group_score_max_key_kept_groups"] != g["expected_kept_groups"]
+    assert by_sum == g["misreadings"]["group_score_sum_all_kept_groups"] != g["expected_kept_groups"]
+
+
 def test_group_routing_reductions():
     rng = np.random.default_rng(6)
     lg = rng.standard_normal((200, 64)).astype(np.float32)
