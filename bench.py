@@ -12,10 +12,12 @@ ceilings, and the CPU oracle timed on a bounded sample of the same workload.
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--side NAMES|none]
 
 Beside the headline the line carries the other prefill workloads (DeepSeek-V3
-and Mixtral shapes: grouped GEMMs against the bf16 matrix-core peak) and the
-decode workload (V4-Flash shapes, learned and hash-routed passes: GEMM 1
-against HBM bandwidth), each with its own roofline, and the FP8 / MXFP4 expert
-variants of every workload.
+and Mixtral shapes) and the decode workload (V4-Flash shapes, learned and
+hash-routed passes), and the FP8 / MXFP4 expert variants of every workload,
+each with the roofline of its GEMM 1.  A roofline's bound is the one that the
+kernel's algorithmic FLOPs and bytes make binding at the published peaks
+(matrix cores for large groups, HBM where the weights outweigh the rows that
+use them); the other bound's fraction rides along.
 """
 import argparse
 import json
@@ -193,27 +195,42 @@ def lowp_accounting(lc, counts, kind):
     return flops, nbytes
 
 
-def up_roofline(acct, ms_up, decode, dtype, measured, name):
-    """Roofline of the dominant kernel (grouped GEMM 1 + SwiGLU, routed rows):
-    algorithmic bytes (decode-shaped batches) or FLOPs (prefill-shaped) of one
-    launch over its measured duration, against the published peak and the
-    chip's measured ceiling."""
-    if decode:
-        ach = acct["up_routed_bytes"] / (ms_up * 1e-3) / 1e9
-        roof = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(ach / PEAK_HBM_GBS, 4))
-        ceil = measured.get("hbm_read_stream_gbs") if measured else None
+def roofline_of(flops, nbytes, ms, mfma_peak, mfma_ceiling, hbm_ceiling):
+    """Roofline of one kernel launch: its algorithmic FLOPs and bytes over its
+    measured duration.  The bound is the one whose ideal time at the published
+    peaks is longer (FLOPs / MFMA peak against bytes / HBM peak: the ridge
+    point), so a batch whose experts see few rows is priced against the HBM
+    it streams the weights from, and a batch of large groups against the
+    matrix cores; the other bound's fraction is reported beside it."""
+    s = ms * 1e-3
+    tflops, gbs = flops / s / 1e12, nbytes / s / 1e9
+    mfma = dict(achieved=round(tflops, 1), peak=mfma_peak, unit="TFLOP/s",
+                frac=round(tflops / mfma_peak, 4))
+    hbm = dict(achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+               frac=round(gbs / PEAK_HBM_GBS, 4))
+    if nbytes / PEAK_HBM_GBS / 1e9 > flops / mfma_peak / 1e12:
+        roof, other, ceil = dict(bound="hbm", **hbm), dict(bound="mfma", **mfma), hbm_ceiling
+        ach = gbs
     else:
-        ach = acct["up_routed_flops"] / (ms_up * 1e-3) / 1e12
-        peak = PEAK_TFLOPS[dtype]
-        roof = dict(bound="mfma", achieved=round(ach, 1), peak=peak, unit="TFLOP/s",
-                    frac=round(ach / peak, 4))
-        ceil = measured.get("mfma_bf16_random_tflops") if measured and dtype == "bf16" else None
-    roof["traffic"] = measured_traffic(name)
+        roof, other, ceil = dict(bound="mfma", **mfma), dict(bound="hbm", **hbm), mfma_ceiling
+        ach = tflops
+    roof["other_bound"] = other
     roof["measured_peak"] = ceil
     roof["frac_of_measured_peak"] = round(ach / ceil, 4) if ceil else None
+    roof["kernel_ms"] = round(ms, 4)
+    return roof
+
+
+def up_roofline(acct, ms_up, dtype, measured, name):
+    """Roofline of the dominant kernel (grouped GEMM 1 + SwiGLU, routed rows),
+    against the published peaks and the chip's measured ceilings."""
+    m = measured or {}
+    roof = roofline_of(acct["up_routed_flops"], acct["up_routed_bytes"], ms_up,
+                       PEAK_TFLOPS[dtype],
+                       m.get("mfma_bf16_random_tflops") if dtype == "bf16" else None,
+                       m.get("hbm_read_stream_gbs"))
+    roof["traffic"] = measured_traffic(name)
     roof["kernel"] = "grouped GEMM 1 + SwiGLU (moe_expert_up, routed rows)"
-    roof["kernel_ms"] = round(ms_up, 4)
     return roof
 
 
@@ -271,8 +288,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True, with
     ms_down, _ = time_gpu(down, steps, warmup, stream)
     ms_combine, _ = time_gpu(combine, steps, warmup, stream)
 
-    decode = acct["rows"] / max(acct["active_experts"], 1) < 48
-    roof = up_roofline(acct, ms_up, decode, lc.dtype, measured, name)
+    roof = up_roofline(acct, ms_up, lc.dtype, measured, name)
     gemm_tflops = 6 * lc.d * lc.d_ff * T * k / ((ms_up + ms_down) * 1e-3) / 1e12
     res = dict(
         workload=name, ms_per_step=ms_step, tokens_per_s=T / (ms_step * 1e-3), wall_s=wall,
@@ -312,7 +328,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True, with
     lowp_ok = lc.dtype == "bf16" and lc.d % 128 == 0 and lc.d_ff % 128 == 0
     for kind, on in (("fp8", with_fp8), ("mxfp4", with_mx)):
         if on and lowp_ok:
-            res[kind] = run_lowp(kind, lc, c, layer, inp, perm, ws, Y, counts, decode, steps,
+            res[kind] = run_lowp(kind, lc, c, layer, inp, perm, ws, Y, counts, steps,
                                  warmup, stream, measured)
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(lc, inp, cpu_seconds)
@@ -322,7 +338,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True, with
     return res
 
 
-def run_lowp(kind, lc, c, layer, inp, perm, ws, Y, counts, decode, steps, warmup, stream,
+def run_lowp(kind, lc, c, layer, inp, perm, ws, Y, counts, steps, warmup, stream,
              measured=None):
     """The same step with FP8 activations and FP8 (E4M3, kind "fp8") or MXFP4
     (kind "mxfp4") expert weights (moe_forward_fp8 / moe_forward_mxfp4), and its
@@ -355,24 +371,12 @@ def run_lowp(kind, lc, c, layer, inp, perm, ws, Y, counts, decode, steps, warmup
     ms_up, _ = time_gpu(up, steps, warmup, stream)
     ms_down, _ = time_gpu(down, steps, warmup, stream)
     flops, nbytes = lowp_accounting(lc, counts, kind)
-    if decode:
-        ach = nbytes / (ms_up * 1e-3) / 1e9
-        roof = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(ach / PEAK_HBM_GBS, 4), traffic=measured_traffic(lc.name, kind))
-    else:
-        ach = flops / (ms_up * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=round(ach, 1), peak=PEAK_TFLOPS["fp8"],
-                    unit="TFLOP/s", frac=round(ach / PEAK_TFLOPS["fp8"], 4),
-                    traffic=measured_traffic(lc.name, kind))
-    ceil = None
-    if measured:
-        ceil = measured.get("hbm_read_stream_gbs") if decode else measured.get(
-            "mfma_fp8_random_tflops")
-    roof["measured_peak"] = ceil
-    roof["frac_of_measured_peak"] = round(ach / ceil, 4) if ceil else None
+    m = measured or {}
+    roof = roofline_of(flops, nbytes, ms_up, PEAK_TFLOPS["fp8"], m.get("mfma_fp8_random_tflops"),
+                       m.get("hbm_read_stream_gbs"))
+    roof["traffic"] = measured_traffic(lc.name, kind)
     roof["kernel"] = "%s grouped GEMM 1 + SwiGLU + FP8 cast (%s, routed rows)" % (
         "MXFP4-weight" if mx else "FP8", up_fn.__name__)
-    roof["kernel_ms"] = round(ms_up, 4)
     gemm_tflops = 6 * d * F * T * k / ((ms_up + ms_down) * 1e-3) / 1e12
     del wq, xq, xs, hq, hs
     return dict(ms_per_step=round(ms_step, 4), tokens_per_s=round(T / (ms_step * 1e-3), 1),
