@@ -443,14 +443,22 @@ def calibrate_copy():
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family and model numbers
+    (a virtualised host may report only the brand) and the logical CPUs seen."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                key, _, val = line.partition(":")
+                key = key.strip()
+                if key in ("model name", "cpu family", "model") and key not in info:
+                    info[key] = val.strip()
     except OSError:
-        pass
-    return None
+        return None
+    if "model name" not in info:
+        return None
+    return "%s (family %s, model %s; %d logical CPUs)" % (
+        info["model name"], info.get("cpu family", "?"), info.get("model", "?"), os.cpu_count() or 0)
 
 
 def cpu_baseline(lc, inp, seconds):

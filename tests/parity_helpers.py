@@ -404,3 +404,13 @@ def check_quantized_tiles(inp, wq, fmt, seed):
                 gs = s[e, c0 // 128, r0:r0 + 128, :].cpu().numpy()
             assert np.array_equal(gs, rs), (name, e, r0, c0)
             assert np.array_equal(gq, rq), (name, e, r0, c0)
+
+
+def dequantized(fmt, q, s):
+    """A weight matrix as the oracle's quantizer left it, in float64: E4M3 codes
+    times their 128x128 tile scales ("fp8"), or E2M1 codes times their 1x32
+    block scales ("mxfp4")."""
+    if fmt == "mxfp4":
+        return np.asarray(O.mxfp4_dequantize(q, s), np.float64)
+    w = O.e4m3_decode(q).astype(np.float64)
+    return w * np.kron(np.asarray(s, np.float64), np.ones((128, 128)))

@@ -110,3 +110,20 @@ def test_stratified_rows_cover_every_fragment():
             assert tok[b - 1] in rows
     for f0 in range(0, T, H.FRAG):  # shared expert: identity rows
         assert rows & set(range(f0, min(T, f0 + H.FRAG)))
+
+
+def test_dequantized_weights_within_one_rounding_step():
+    """The helper the low-precision stage tests use to bound a row's move from
+    its H differences: codes times scales, each element within half a step of
+    the bf16 master (E4M3: 3 mantissa bits; E2M1: 1 bit; plus the subnormal
+    step near zero)."""
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal((256, 384)) * np.exp(rng.standard_normal((256, 1)))).astype(np.float32)
+    q, s = O.quantize_blocks(w)
+    tile_s = np.kron(s, np.ones((128, 128)))
+    deq = H.dequantized("fp8", q, s)
+    assert np.all(np.abs(deq - w) <= np.abs(w) / 16 + 2.0 ** -10 * tile_s)
+    q, s = O.quantize_mxfp4(w)
+    blk_s = np.repeat(np.ldexp(1.0, s.astype(np.int32) - 127), 32, axis=1)
+    deq = H.dequantized("mxfp4", q, s)
+    assert np.all(np.abs(deq - w) <= np.abs(w) / 4 + 0.25 * blk_s)
