@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s + grouped-GEMM % bf16 MFMA peak (prefill), % HBM BW (decode)"
 DEFAULT_WORKLOAD = "v4pro_skew_prefill"  # T=16384, d=7168, E=384+1, top-6, d_ff=3072, bf16
 SIDE_WORKLOADS = ("dsv3_prefill", "mixtral_prefill", "v4flash_decode")
+SIDE_CPU_SECONDS = 3.0  # oracle on one host thread per side workload
 
 # MI355X published peaks
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8": 5000.0}  # dense MFMA
@@ -235,7 +236,7 @@ def up_roofline(acct, ms_up, dtype, measured, name):
 
 
 def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True, with_mx=True,
-                 measured=None):
+                 measured=None, cpu_single=0.0):
     import numpy as np
     import torch
 
@@ -333,6 +334,8 @@ def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True, with
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(lc, inp, cpu_seconds)
         res["input_digests"] = input_digests(inp)
+    elif cpu_single > 0:
+        res["cpu_single_core"] = cpu_single_core(lc, inp, cpu_single)
     del layer, inp, H, Y, out, perm
     torch.cuda.empty_cache()
     return res
@@ -461,18 +464,16 @@ def cpu_model():
         info["model name"], info.get("cpu family", "?"), info.get("model", "?"), os.cpu_count() or 0)
 
 
-def cpu_baseline(lc, inp, seconds):
-    """The oracle as it stands, on a bounded sample of this workload's tokens (the
-    first n rows, n sized from a probe to about `seconds` of work), on all the
-    host threads OpenMP gives it, and on one thread for a smaller sample.
-    Reported in tokens/s.  Only the experts the sampled tokens select are copied
-    to the host (the oracle's own routing of those rows decides which)."""
+def oracle_runner(lc, inp):
+    """run(rows) -> seconds: the oracle's whole layer (float64 FFN) on the listed
+    token rows of this workload's inputs, on the threads OpenMP currently gives
+    it.  Only the experts the listed rows select are copied to the host (the
+    oracle's own routing of those rows decides which)."""
     import numpy as np
 
     import oracle as O
     from mixture_experts_ffn_sqrt_amd.synth import to_host_bits
 
-    threads = O.num_threads()
     h = to_host_bits(inp["hidden"])
     wr = to_host_bits(inp["w_router"])
     bias = to_host_bits(inp.get("bias"))
@@ -498,6 +499,20 @@ def cpu_baseline(lc, inp, seconds):
                 logit_offset=off, w13_shared=s13, w2_shared=s2, **grp)
         return time.perf_counter() - t0
 
+    return run
+
+
+def cpu_baseline(lc, inp, seconds):
+    """The oracle as it stands, on a bounded sample of this workload's tokens (the
+    first n rows, n sized from a probe to about `seconds` of work), on all the
+    host threads OpenMP gives it, and on one thread for a smaller sample.
+    Reported in tokens/s."""
+    import numpy as np
+
+    import oracle as O
+
+    threads = O.num_threads()
+    run = oracle_runner(lc, inp)
     probe = np.arange(min(threads, lc.T), dtype=np.int32)
     tp = run(probe)
     n = int(min(lc.T, max(len(probe), seconds / max(tp, 1e-4) * len(probe))))
@@ -505,20 +520,39 @@ def cpu_baseline(lc, inp, seconds):
     rows = np.arange(n, dtype=np.int32)
     t = run(rows)
     # one thread: a sample of about a quarter of the time budget
-    O.set_num_threads(1)
-    try:
-        per_token_1 = tp * threads / len(probe)
-        n1 = int(min(lc.T, max(1, 0.25 * seconds / max(per_token_1, 1e-4))))
-        rows1 = np.arange(n1, dtype=np.int32)
-        t1 = run(rows1)
-    finally:
-        O.set_num_threads(threads)
+    single = cpu_single_core(lc, inp, 0.25 * seconds, run, tp * threads / len(probe))
     return dict(value=round(len(rows) / t, 3), unit="tokens/s", cores=threads, kind="oracle",
                 sample="first %d of %d tokens of %s, full layer per token (float64 FFN), "
                        "%.1f s on %d threads" % (len(rows), lc.T, lc.name, t, threads),
-                cpu_model=cpu_model(),
-                single_core=dict(value=round(n1 / t1, 3), unit="tokens/s", cores=1,
-                                 sample="first %d tokens, %.1f s" % (n1, t1)))
+                cpu_model=cpu_model(), single_core=single)
+
+
+def cpu_single_core(lc, inp, seconds, run=None, per_token=None):
+    """The oracle on one host thread, on the first n tokens of the workload (n
+    sized to about `seconds` of work from one probe token unless the per-token
+    time is given), in tokens/s."""
+    import numpy as np
+
+    import oracle as O
+
+    threads = O.num_threads()
+    run = run or oracle_runner(lc, inp)
+    O.set_num_threads(1)
+    try:
+        if per_token is None:
+            per_token = run(np.arange(1, dtype=np.int32))
+        n1 = int(min(lc.T, max(1, seconds / max(per_token, 1e-6))))
+        rows1 = np.arange(n1, dtype=np.int32)
+        t1 = run(rows1)
+        reps = 1
+        if n1 == lc.T and t1 < 0.25 * seconds:  # a whole small batch: repeat it
+            reps = int(min(1000, seconds / max(t1, 1e-6)))
+            t1 = sum(run(rows1) for _ in range(reps))
+    finally:
+        O.set_num_threads(threads)
+    return dict(value=round(reps * n1 / t1, 3), unit="tokens/s", cores=1, kind="oracle",
+                sample="first %d of %d tokens of %s%s, %.2f s" % (
+                    n1, lc.T, lc.name, " x %d" % reps if reps > 1 else "", t1))
 
 
 def main():
@@ -570,16 +604,23 @@ def main():
         "measured_peaks": measured,
     }
     keep = ("ms_per_step", "tokens_per_s", "roofline", "grouped_gemm", "combine", "layer",
-            "routing", "step_ms_p10_p50_p90", "hash_pass", "fp8", "mxfp4")
+            "routing", "step_ms_p10_p50_p90", "hash_pass", "fp8", "mxfp4", "cpu_single_core")
     side = [] if args.side in ("", "none") else [w for w in args.side.split(",")
                                                  if w != args.workload]
     others = {}
     for name in side:
         r = run_workload(name, args.steps, args.warmup, False, 0, not args.no_fp8,
-                         not args.no_mxfp4, measured)
+                         not args.no_mxfp4, measured,
+                         cpu_single=0.0 if args.no_cpu else SIDE_CPU_SECONDS)
         others[name] = {kk: r.get(kk) for kk in keep if r.get(kk) is not None}
     if others:
         line["workloads"] = others
+    if not args.no_cpu:
+        # the fp32 toy configuration is a parity case, never timed on the GPU;
+        # its oracle time on one thread is the one figure it contributes
+        from mixture_experts_ffn_sqrt_amd.synth import make_inputs
+        tl = CONFIGS["tiny_fp32"]
+        line["cpu_single_core_tiny_fp32"] = cpu_single_core(tl, make_inputs(tl, "cpu"), 0.5)
     if not args.no_peaks:
         line["context"] = peaks()
     if args.calibrate_copy:

@@ -103,6 +103,37 @@ __host__ __device__ constexpr int fp8_stage_bytes() {
          (WF == WF_MXFP4 ? BN * 4 : 256);
 }
 
+// Maxima of NV values per lane over the 32 lanes of a lane half, by recursive
+// halving: at the step with lane distance D, a lane keeps the half of its N
+// remaining values selected by bit D of its column and sends the other half to
+// the lane D apart, which keeps the opposite half; the shuffles of one step are
+// independent of one another.  After log2(NV) steps lane c holds the maximum
+// of value c * NV / 32 (NV < 32: the remaining steps are plain exchanges, and
+// 32 / NV neighbouring lanes hold the same maximum).  31 shuffles for 32
+// values, where one butterfly per value takes 160.  A maximum is exact and
+// independent of the order of its operands.
+template <int NV, int D, int N = NV>
+struct HalvingMax {
+  template <int M>
+  __device__ __forceinline__ static void run(float (&v)[M], int ccol) {
+    if constexpr (D >= 1) {
+      if constexpr (N > 1) {
+        const bool b = (ccol & D) != 0;
+#pragma unroll
+        for (int j = 0; j < N / 2; ++j) {
+          const float send = b ? v[j] : v[j + N / 2];
+          const float keep = b ? v[j + N / 2] : v[j];
+          v[j] = fmaxf(keep, __shfl_xor(send, D, 32));
+        }
+        HalvingMax<NV, D / 2, N / 2>::run(v, ccol);
+      } else {
+        v[0] = fmaxf(v[0], __shfl_xor(v[0], D, 32));
+        HalvingMax<NV, D / 2, 1>::run(v, ccol);
+      }
+    }
+  }
+};
+
 // One tile of grouped_gemm_fp8 (below).
 // SCHED = 1: fragments double-buffered in registers across the two k-steps of
 // a stage, in the order sched_stage fixes (full tiles only).
@@ -371,8 +402,11 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& q, const TileCoord&
     // the WN waves through LDS; scale 2^e = the smallest power of two with
     // max <= 448 * 2^e; codes E4M3(h * 2^-e)
     constexpr int HF = FN / 2;
+    constexpr int NV = FM * 16;       // rows per lane half (lanes 0-31 / 32-63)
+    constexpr int SPAN = 32 / NV;     // lanes that end up holding one row's maximum
+    static_assert(NV == 16 || NV == 32, "one or two fragments of rows per wave");
     float h[FM][HF][16];
-    float pmax[FM][16];
+    float pmax[NV];                   // value q = 16 i + r: row 32 i + 8 (r / 4) + crow + r % 4
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -384,21 +418,19 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& q, const TileCoord&
           h[i][f][r] = silu_mul(g, u);
           m = fmaxf(m, fabsf(h[i][f][r]));
         }
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 32));
-        pmax[i][r] = m;
+        pmax[16 * i + r] = m;
       }
+    // the maxima over the 32 columns of each lane half: lane c ends with row
+    // q = c / SPAN's maximum
+    HalvingMax<NV, 16>::run(pmax, ccol);
     // all waves are past the main loop (their last LDS reads returned) before
     // the stage buffers are reused for the partial maxima
     __builtin_amdgcn_s_waitcnt(0xC07F);
     lds_barrier();
     float* part = reinterpret_cast<float*>(smem);  // [WN][BM]
-    if (ccol == 0) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          part[wn * BM + wm * WTM + 32 * i + 8 * (r >> 2) + crow + (r & 3)] = pmax[i][r];
+    if (ccol % SPAN == 0) {
+      const int q = ccol / SPAN;
+      part[wn * BM + wm * WTM + 32 * (q >> 4) + 8 * ((q & 15) >> 2) + crow + (q & 3)] = pmax[0];
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);
     lds_barrier();
