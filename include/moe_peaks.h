@@ -37,10 +37,14 @@ double moe_peaks_mfma_flops(int kind, int blocks, int iters);
 int moe_peaks_mfma(int kind, const void *operands, int blocks, int iters, float *out,
                    void *stream);
 
-/* HBM read stream: every byte of `src` (device, `bytes` a multiple of 4096)
- * read once with 16-byte loads by `blocks` workgroups of 256 threads walking
- * it in a grid stride; `out` (device, blocks uint32) receives each block's XOR
- * of what it read.  Pick `bytes` well above the 256 MB Infinity Cache. */
+/* HBM read stream: every byte of `src` (device) read once by `blocks`
+ * workgroups of 256 threads, block b streaming the contiguous b-th of `blocks`
+ * equal chunks with 16-byte non-temporal loads, eight in flight per lane (the
+ * fastest of the read patterns measured on the chip: grid-stride loops and
+ * cached loads stream 10-20% slower).  `bytes` must be a multiple of
+ * blocks * 4096 with chunks under 2 GiB, else MOE_PEAKS_EINVAL before any
+ * launch.  `out` (device, blocks uint32) receives each block's XOR of what it
+ * read.  Pick `bytes` well above the 256 MB Infinity Cache. */
 int moe_peaks_read(const void *src, size_t bytes, int blocks, uint32_t *out, void *stream);
 
 #ifdef __cplusplus

@@ -163,6 +163,7 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& q, const TileCoord&
   constexpr int NA = BM / RPL, NB = BN / RPLB;
   constexpr int LA = NA / NW, LB = (NB + NW - 1) / NW;
   constexpr bool B_EVEN = NB % NW == 0;
+  constexpr int B_POL = BM <= 32 && !MX ? kStreamWeightPolicy : 0;  // E4M3 streaming tiles
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "whole 32x32 fragments");
   static_assert(NA * RPL == BM && NB * RPLB == BN && LA * NW == NA, "A loads must split evenly");
   static_assert(NSBL <= NW, "one weight-scale load per wave at most");
@@ -252,7 +253,7 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& q, const TileCoord&
         load_lds16(a_rs, buf_ + (RPL * (wave + NW * j)) * ROWB, a_off[j] + kc_ * ROWB);     \
     _Pragma("unroll") for (int j = 0; j < LB; ++j) {                                        \
       if (j == LB - 1 && !b_last) break;                                                   \
-      load_lds16(b_rs, buf_ + OFF_B + (RPLB * (wave + NW * j)) * BROWB,                    \
+      load_lds16<B_POL>(b_rs, buf_ + OFF_B + (RPLB * (wave + NW * j)) * BROWB,             \
                  b_off[j] + kc_ * BROWB);                                                  \
     }                                                                                      \
     if (has_sa)                                                                            \

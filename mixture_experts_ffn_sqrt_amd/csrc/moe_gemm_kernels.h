@@ -398,10 +398,23 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
-// one 16-byte-per-lane buffer load straight into LDS at `dst` (+16 * lane)
+// one 16-byte-per-lane buffer load straight into LDS at `dst` (+16 * lane),
+// with cache policy POL (the buffer instruction's cache-policy bits)
+template <int POL = 0>
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, char* dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)dst, 16, voff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)dst, 16, voff, 0, 0, POL);
 }
+
+// Cache policy of the weight loads of the 32-row streaming tiles (decode, and
+// the groups of a few rows on a skewed prefill batch): they read every weight
+// once, and the non-temporal bit (NT) lets the L2 let go of those lines first.
+// A block-contiguous read stream runs at 6.9-7.0 TB/s with it against 6.2
+// without; the decode GEMMs of V4-Flash shapes 6-7% faster (bf16 and E4M3),
+// V4-Pro's bf16 up GEMM 1%.  Not for the larger tiles, whose co-running tiles
+// share weight panels through the L2 (Mixtral and V4-Pro 3-5% slower with it),
+// nor for E2M1 weights, whose 64-byte rows leave the other half of each
+// 128-byte line to the next K stage (MXFP4 decode 36% slower with it).
+constexpr int kStreamWeightPolicy = 2;  // NT
 
 // one 4-byte-per-lane buffer load straight into LDS at `dst` (+4 * lane)
 __device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t rs, char* dst, uint32_t voff) {
@@ -470,6 +483,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& p, const TileCoord
   constexpr int NA = BM / RPL, NB = BN / RPL;
   constexpr int LA = NA / NW, LB = (NB + NW - 1) / NW;
   constexpr bool B_EVEN = NB % NW == 0;
+  constexpr int B_POL = BM <= 32 && ROWB == 128 ? kStreamWeightPolicy : 0;  // whole 128-byte lines
   static_assert(ROWB == 64 || ROWB == 128, "64- or 128-byte LDS rows");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "whole 32x32 fragments");
   static_assert(!SW || FN % 2 == 0, "SwiGLU waves hold gate and up fragments in pairs");
@@ -541,7 +555,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& p, const TileCoord
     const uint32_t ko_ = (uint32_t)kc_ * ROWB;                                           \
     _Pragma("unroll") for (int j = 0; j < LB; ++j) {                                      \
       if (j == LB - 1 && !b_last) break;                                                 \
-      load_lds16(b_rs, buf_ + (RPL * (wave + NW * j)) * ROWB, b_off[j] + ko_);           \
+      load_lds16<B_POL>(b_rs, buf_ + (RPL * (wave + NW * j)) * ROWB, b_off[j] + ko_);    \
     }                                                                                    \
   } while (0)
 

@@ -80,7 +80,7 @@ def mfma_tflops(kind, cus=256, iters=32768, reps=3):
     return L.moe_peaks_mfma_flops(kind, blocks, iters) / (ms * 1e-3) / 1e12
 
 
-def read_gbs(gib=4, blocks=256 * 16, reps=5):
+def read_gbs(gib=4, blocks=256 * 4, reps=5):
     """HBM read-stream rate (GB/s) over a `gib` GiB buffer (16 times the
     Infinity Cache)."""
     import torch

@@ -94,22 +94,32 @@ __global__ __launch_bounds__(kThreads) void mfma_fp8_kernel(const void* src, int
   out[blockIdx.x * kThreads + threadIdx.x] = s;
 }
 
-__global__ __launch_bounds__(kThreads) void read_kernel(const uint4* src, size_t n16,
+__global__ __launch_bounds__(kThreads) void read_kernel(const uint4* src, size_t chunk16,
                                                         uint32_t* out) {
-  constexpr int U = 8;  // 16-byte loads in flight per lane per round
+  // block b streams the contiguous elements [b * chunk16, (b + 1) * chunk16)
+  // (chunk16 a multiple of kThreads, under 2 GiB) with 16-byte buffer loads
+  // marked non-temporal, U of them in flight per lane
+  constexpr int U = 8;
+  constexpr int kNonTemporal = 2;  // buffer cache-policy bit NT
+  const char* base = reinterpret_cast<const char*>(src + (size_t)blockIdx.x * chunk16);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(base), 0, (int)(chunk16 * 16), 0x00020000);
   uint32_t x = 0;
-  const size_t stride = (size_t)gridDim.x * kThreads;
-  size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + (U - 1) * stride < n16; i += U * stride) {
-    uint4 v[U];
+  size_t j = threadIdx.x;
+  for (; j + (U - 1) * kThreads < chunk16; j += U * kThreads) {
+    uint32_t w[U][4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = src[i + u * stride];
+    for (int u = 0; u < U; ++u) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)((j + u * kThreads) * 16), 0,
+                                                           kNonTemporal);
+      w[u][0] = v[0]; w[u][1] = v[1]; w[u][2] = v[2]; w[u][3] = v[3];
+    }
 #pragma unroll
-    for (int u = 0; u < U; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    for (int u = 0; u < U; ++u) x ^= w[u][0] ^ w[u][1] ^ w[u][2] ^ w[u][3];
   }
-  for (; i < n16; i += stride) {
-    const uint4 v = src[i];
-    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  for (; j < chunk16; j += kThreads) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(j * 16), 0, kNonTemporal);
+    x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }
   // block XOR through LDS
   __shared__ uint32_t part[kThreads];
@@ -148,9 +158,11 @@ int moe_peaks_mfma(int kind, const void* operands, int blocks, int iters, float*
 
 int moe_peaks_read(const void* src, size_t bytes, int blocks, uint32_t* out, void* stream) {
   if (!src || !out || blocks < 1 || bytes == 0 || bytes % 4096) return MOE_PEAKS_EINVAL;
+  const size_t chunk = bytes / (size_t)blocks;  // bytes per block
+  if (bytes % ((size_t)blocks * 4096) || chunk >= ((size_t)1 << 31)) return MOE_PEAKS_EINVAL;
   hipLaunchKernelGGL(read_kernel, dim3(blocks), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<const uint4*>(src),
-                     bytes / 16, out);
+                     chunk / 16, out);
   return hipGetLastError() == hipSuccess ? MOE_PEAKS_OK : MOE_PEAKS_EHIP;
 }
 

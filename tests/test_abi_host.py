@@ -196,6 +196,7 @@ def test_peaks_reject_bad_arguments_on_the_host():
     assert L.moe_peaks_mfma(0, None, 1, 4, p, None) == -1
     assert L.moe_peaks_read(p, 4095, 1, p, None) == -1      # not a multiple of 4096
     assert L.moe_peaks_read(p, 4096, 0, p, None) == -1
+    assert L.moe_peaks_read(p, 3 * 4096, 2, p, None) == -1  # chunks not whole 4 KB blocks
 
 
 def test_noalloc_rejects_on_the_host():
