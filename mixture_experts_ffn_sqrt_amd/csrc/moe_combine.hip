@@ -7,6 +7,12 @@
 // token and a chunk of kThreads * 16 bytes of its row (so that a small batch
 // still spreads over the chip); each thread issues all of its row loads before
 // it sums them.
+//
+// The expert rows are read once.  When they are more than the 256 MB Infinity
+// Cache holds, the loads carry the non-temporal hint: V4-Pro's combine (1.6 GB
+// of rows) 0.338 -> 0.293 ms, DeepSeek-V3's 0.220 -> 0.193 ms; batches whose
+// rows the Infinity Cache still holds from GEMM 2 read them faster without it
+// (Mixtral 18.4 vs 20.8 us).
 #include "moe_internal.h"
 
 namespace moe {
@@ -16,12 +22,27 @@ constexpr int kThreads = 128;
 constexpr int kMaxK = 16;
 
 // 16 bytes of TE: raw load, and its float lanes
+constexpr int64_t kInfinityCacheBytes = (int64_t)256 << 20;
+
+// 16 bytes at p, non-temporal when NT
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const void* p) {
+  if constexpr (NT) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  } else {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+}
+
 template <typename TE>
 struct Vec;
 template <>
 struct Vec<uint16_t> {
   static constexpr int N = 8;
-  __device__ static uint4 load(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+  template <bool NT>
+  __device__ static uint4 load(const void* p) { return load16<NT>(p); }
   __device__ static void unpack(const uint4& v, float* x) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -42,7 +63,8 @@ struct Vec<uint16_t> {
 template <>
 struct Vec<float> {
   static constexpr int N = 4;
-  __device__ static uint4 load(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+  template <bool NT>
+  __device__ static uint4 load(const void* p) { return load16<NT>(p); }
   __device__ static void unpack(const uint4& v, float* x) {
     x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
     x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
@@ -52,7 +74,7 @@ struct Vec<float> {
   }
 };
 
-template <typename TE>
+template <typename TE, bool NT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const TE* Y, const int32_t* dispatch,
                                                            const float* w, const TE* shared,
                                                            TE* out, int k, int d) {
@@ -70,8 +92,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const TE* Y, const in
   uint4 raw[kMaxK + 1];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j)
-    if (rows[j] >= 0) raw[j] = Vec<TE>::load(Y + static_cast<int64_t>(rows[j]) * d + c);
-  if (shared) raw[kMaxK] = Vec<TE>::load(shared + static_cast<int64_t>(t) * d + c);
+    if (rows[j] >= 0) raw[j] = Vec<TE>::template load<NT>(Y + static_cast<int64_t>(rows[j]) * d + c);
+  if (shared) raw[kMaxK] = Vec<TE>::template load<NT>(shared + static_cast<int64_t>(t) * d + c);
   float acc[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.0f;
@@ -97,12 +119,18 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const TE* Y, const in
 hipError_t launch_combine(const moe_config& c, const void* expert_out, const int32_t* dispatch,
                           const float* weights, const void* shared_out, void* out,
                           hipStream_t s) {
+  const int es = c.dtype == MOE_F32 ? 4 : 2;
+  const int64_t row_bytes =
+      (int64_t)c.T * (c.k + (shared_out ? 1 : 0)) * c.d * es;  // expert rows read
+  const bool nt = row_bytes > kInfinityCacheBytes;
   if (c.dtype == MOE_F32) {
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(c.T, ceil_div(c.d, kThreads * 4)), dim3(kThreads), 0, s,
+    auto kern = nt ? combine_kernel<float, true> : combine_kernel<float, false>;
+    hipLaunchKernelGGL(kern, dim3(c.T, ceil_div(c.d, kThreads * 4)), dim3(kThreads), 0, s,
                        static_cast<const float*>(expert_out), dispatch, weights,
                        static_cast<const float*>(shared_out), static_cast<float*>(out), c.k, c.d);
   } else {
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(c.T, ceil_div(c.d, kThreads * 8)), dim3(kThreads), 0, s,
+    auto kern = nt ? combine_kernel<uint16_t, true> : combine_kernel<uint16_t, false>;
+    hipLaunchKernelGGL(kern, dim3(c.T, ceil_div(c.d, kThreads * 8)), dim3(kThreads), 0, s,
                        static_cast<const uint16_t*>(expert_out), dispatch, weights,
                        static_cast<const uint16_t*>(shared_out), static_cast<uint16_t*>(out),
                        c.k, c.d);
