@@ -127,12 +127,14 @@ hipError_t launch_router_gemm(const moe_config& c, const void* hidden, const voi
     p.c_split = (int64_t)c.T * p.ldc;
   }
   // Large batches with many experts: 128x128 tiles read the hidden rows half as
-  // often (DeepSeek-V3 prefill 92 -> 72 us); small batches keep 64x64 tiles so
-  // that enough blocks run.  Both shapes use the same MFMA and walk K in the
-  // same order for every output, so the logits are bitwise the same either way.
+  // often (DeepSeek-V3 prefill 92 -> 72 us), on 8 waves of 32x64 (routing of
+  // DeepSeek-V3 120 -> 110 us, V4-Pro 187 -> 181 us against 4 waves; 256-row
+  // tiles and 16 waves no better); small batches keep 64x64 tiles so that
+  // enough blocks run.  Every shape uses the same MFMA and walks K in the same
+  // order for every output, so the logits are bitwise the same either way.
   if (c.T >= 1024 && c.E >= 128) {
     p.n_tiles = ceil_div(c.E, 128);
-    return launch_gemm<uint16_t, 128, 128, 2, 2, EPI_LOGITS>(p, ceil_div(c.T, 128), s, splits);
+    return launch_gemm<uint16_t, 128, 128, 4, 2, EPI_LOGITS>(p, ceil_div(c.T, 128), s, splits);
   }
   p.n_tiles = ceil_div(c.E, 64);
   return launch_gemm<uint16_t, 64, 64, 2, 2, EPI_LOGITS>(p, ceil_div(c.T, 64), s, splits);
