@@ -281,29 +281,37 @@ int moe_forward_fp8(const moe_config *cfg, const void *hidden, const void *w_rou
  *   K-block-major, [C/128, R, 4]: for each 128-column block j, each row r's four
  *   bytes (its blocks 4j .. 4j+3).  The matrix cores' loads then read one K
  *   block's scales of consecutive rows as contiguous words.
- *   Weights: w13q [E, 2*d_ff, d/2] uint8 with w13s [E, d/128, 2*d_ff, 4] uint8,
- *            w2q [E, d, d_ff/2] with w2s [E, d_ff/128, d, 4].  Shared expert: one
+ *   Code layout: rows are paired.  For a weight matrix [R, C] (R even) the
+ *   codes are stored [R/2, C/128, 2, 64]: for row pair i and 128-column block
+ *   j, 64 bytes of row 2i then 64 bytes of row 2i+1, so the element (r, c)
+ *   sits at byte (r/2)*C + (c/128)*128 + (r%2)*64 + (c%128)/2.  One K block of
+ *   two rows fills one whole 128-byte line.  Total size R*C/2 bytes, the size
+ *   of the row-major [R, C/2] array it replaces.
+ *   Weights: w13q [E, d_ff, d] uint8 (2*d_ff rows in pairs) with w13s
+ *            [E, d/128, 2*d_ff, 4] uint8, w2q [E, d/2, d_ff] (d rows in pairs)
+ *            with w2s [E, d_ff/128, d, 4].  Shared expert: one
  *            expert's worth.
  * A dot product sums each 32-element block, scales the block sum by the
  * weight block's scale and the activation's 1x128 scale, and accumulates in
  * float32.  Requirements, workspace and errors as for the FP8 entry points. */
 
 /* Quantize n_mat matrices w [n_mat, R, C] (in_dtype MOE_F32 or MOE_BF16) in 1x32
- * blocks: q [n_mat, R, C/2] packed codes, scales [n_mat, C/128, R, 4] E8M0 bytes
- * (the layout above).  C a multiple of 128 (else MOE_ERR_UNSUPPORTED).  Needs no
- * workspace; n_mat, R or C == 0 queues nothing. */
+ * blocks: q [n_mat, R/2, C] packed codes in the paired-row code layout above,
+ * scales [n_mat, C/128, R, 4] E8M0 bytes.  C a multiple of 128 and R even (else
+ * MOE_ERR_UNSUPPORTED).  Needs no workspace; n_mat, R or C == 0 queues nothing. */
 int moe_quantize_mxfp4(int n_mat, int R, int C, int in_dtype, const void *w, uint8_t *q,
                        uint8_t *scales, void *stream);
 
 /* Linear-1 + SwiGLU + FP8 cast of h with MXFP4 weights; arguments as for
- * moe_expert_up_fp8 except w13q [E, 2*d_ff, d/2] and w13s [E, d/128, 2*d_ff, 4]. */
+ * moe_expert_up_fp8 except w13q [E, d_ff, d] (paired rows) and w13s
+ * [E, d/128, 2*d_ff, 4]. */
 int moe_expert_up_mxfp4(const moe_config *cfg, const uint8_t *xq, const float *xs,
                         const int32_t *sorted_token_ids, const int32_t *expert_offsets,
                         const uint8_t *w13q, const uint8_t *w13s, uint8_t *hq, float *hs,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /* Linear-2 with MXFP4 weights; arguments as for moe_expert_down_fp8 except w2q
- * [E, d, d_ff/2] and w2s [E, d_ff/128, d, 4]. */
+ * [E, d/2, d_ff] (paired rows) and w2s [E, d_ff/128, d, 4]. */
 int moe_expert_down_mxfp4(const moe_config *cfg, const uint8_t *hq, const float *hs,
                           const int32_t *expert_offsets, const uint8_t *w2q, const uint8_t *w2s,
                           void *expert_out, void *workspace, size_t workspace_bytes,

@@ -383,8 +383,10 @@ def quantize_fp8_weights(inp, stream=None):
 
 
 def moe_quantize_mxfp4(w, q, scales, stream=None):
-    """w [R, C] or [n, R, C] float32/bfloat16 (C a multiple of 128) -> q [..., R,
-    C/2] uint8 packed E2M1, scales [..., C/128, R, 4] uint8 E8M0 (K-block-major)."""
+    """w [R, C] or [n, R, C] float32/bfloat16 (C a multiple of 128, R even) ->
+    q [..., R/2, C] uint8 packed E2M1 in row pairs (row pair i, 128-column block j:
+    64 bytes of row 2i, then 64 of row 2i+1), scales [..., C/128, R, 4] uint8 E8M0
+    (K-block-major)."""
     if w.dtype not in _IN_DTYPES:
         raise ValueError("w must be float32 or bfloat16, got %s" % w.dtype)
     if w.dim() not in (2, 3):
@@ -393,7 +395,7 @@ def moe_quantize_mxfp4(w, q, scales, stream=None):
     n = w.shape[0] if w.dim() == 3 else 1
     lead = tuple(w.shape[:-2])
     args = [n, R, C_, _IN_DTYPES[w.dtype], _t("w", w, tuple(w.shape), w.dtype),
-            _t("q", q, lead + (R, C_ // 2), torch.uint8),
+            _t("q", q, lead + (R // 2, C_), torch.uint8),
             _t("scales", scales, lead + (C_ // 128, R, 4), torch.uint8), _stream(stream)]
     _check("moe_quantize_mxfp4", load_library().moe_quantize_mxfp4(*args))
 
@@ -406,7 +408,7 @@ def moe_expert_up_mxfp4(cfg, xq, xs, sorted_token_ids, expert_offsets, w13q, w13
             _t("xq", xq, (T, d), u8), _t("xs", xs, (d // 128, T), f32),
             _t("sorted_token_ids", sorted_token_ids, (T * k,), torch.int32),
             _t("expert_offsets", expert_offsets, (E + 1,), torch.int32),
-            _t("w13q", w13q, (E, 2 * F, d // 2), u8),
+            _t("w13q", w13q, (E, F, d), u8),
             _t("w13s", w13s, (E, d // 128, 2 * F, 4), u8),
             _t("hq", hq, (T * k, F), u8), _t("hs", hs, (F // 128, T * k), f32),
             *_ws(cfg, workspace), _stream(stream)]
@@ -420,7 +422,7 @@ def moe_expert_down_mxfp4(cfg, hq, hs, expert_offsets, w2q, w2s, expert_out, wor
     args = [C.byref(cfg),
             _t("hq", hq, (T * k, F), u8), _t("hs", hs, (F // 128, T * k), f32),
             _t("expert_offsets", expert_offsets, (E + 1,), torch.int32),
-            _t("w2q", w2q, (E, d, F // 2), u8), _t("w2s", w2s, (E, F // 128, d, 4), u8),
+            _t("w2q", w2q, (E, d // 2, F), u8), _t("w2s", w2s, (E, F // 128, d, 4), u8),
             _t("expert_out", expert_out, (T * k, d), torch.bfloat16),
             *_ws(cfg, workspace), _stream(stream)]
     _check("moe_expert_down_mxfp4", load_library().moe_expert_down_mxfp4(*args))
@@ -439,12 +441,12 @@ def moe_forward_mxfp4(cfg, hidden, w_router, logit_offset, bias, token_ids, tid2
             _t("bias", bias, (E,), f32, False),
             _t("token_ids", token_ids, (T,), torch.int32, hsh),
             _t("tid2eid", tid2eid, (cfg.vocab, k), torch.int32, hsh),
-            _t("w13q", w13q, (E, 2 * F, d // 2), u8),
+            _t("w13q", w13q, (E, F, d), u8),
             _t("w13s", w13s, (E, d // 128, 2 * F, 4), u8),
-            _t("w2q", w2q, (E, d, F // 2), u8), _t("w2s", w2s, (E, F // 128, d, 4), u8),
-            _t("w13q_shared", w13q_shared, (2 * F, d // 2), u8, sh),
+            _t("w2q", w2q, (E, d // 2, F), u8), _t("w2s", w2s, (E, F // 128, d, 4), u8),
+            _t("w13q_shared", w13q_shared, (F, d), u8, sh),
             _t("w13s_shared", w13s_shared, (d // 128, 2 * F, 4), u8, sh),
-            _t("w2q_shared", w2q_shared, (d, F // 2), u8, sh),
+            _t("w2q_shared", w2q_shared, (d // 2, F), u8, sh),
             _t("w2s_shared", w2s_shared, (F // 128, d, 4), u8, sh),
             _t("out", out, (T, d), bf),
             _t("topk_ids_out", topk_ids_out, (T, k), torch.int32, False),
@@ -463,7 +465,7 @@ def quantize_mxfp4_weights(inp, stream=None):
         if w is None:
             continue
         lead, R, C_ = tuple(w.shape[:-2]), w.shape[-2], w.shape[-1]
-        q = torch.empty(lead + (R, C_ // 2), dtype=torch.uint8, device=w.device)
+        q = torch.empty(lead + (R // 2, C_), dtype=torch.uint8, device=w.device)
         s = torch.empty(lead + (C_ // 128, R, 4), dtype=torch.uint8, device=w.device)
         moe_quantize_mxfp4(w, q, s, stream)
         base = name.replace("_shared", "")

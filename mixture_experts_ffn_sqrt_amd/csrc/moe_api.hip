@@ -547,7 +547,7 @@ int moe_forward_fp8(const moe_config* cfg, const void* hidden, const void* w_rou
 int moe_quantize_mxfp4(int n_mat, int R, int C, int in_dtype, const void* w, uint8_t* q,
                        uint8_t* scales, void* stream) {
   if (n_mat < 0 || R < 0 || C < 0) return MOE_ERR_INVALID_ARG;
-  if (C % 128) return MOE_ERR_UNSUPPORTED;
+  if (C % 128 || R % 2) return MOE_ERR_UNSUPPORTED;
   if (in_dtype != MOE_F32 && in_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (n_mat == 0 || R == 0 || C == 0) return MOE_OK;
   if (!w || !q || !scales) return MOE_ERR_INVALID_ARG;

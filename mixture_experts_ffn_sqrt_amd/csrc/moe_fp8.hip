@@ -148,13 +148,14 @@ __global__ __launch_bounds__(256) void quantize_mxfp4_kernel(int64_t nblocks, in
     if (!ok) continue;
     const int e = mx_scale_exp(m);
     const float inv = ldexpf(1.0f, -e);
-    q[base / 2] = (uint8_t)(e2m1_code(v0 * inv) | (e2m1_code(v1 * inv) << 4));
-    if (sub == 0) {
-      const int64_t row = blk / GB;  // over all matrices
-      const int b = (int)(blk - row * GB);
-      const int64_t mat = row / R, r = row - mat * R;
-      scales[((mat * (C / 128) + b / 4) * R + r) * 4 + (b & 3)] = (uint8_t)(e + 127);
-    }
+    const int64_t row = blk / GB;  // over all matrices
+    const int b = (int)(blk - row * GB);
+    const int64_t mat = row / R, r = row - mat * R;
+    // codes of rows 2i and 2i+1 share 128-byte lines per 128-element K block
+    const int c = b * 32 + 2 * sub;  // element column of v0
+    q[mat * ((int64_t)R * C / 2) + (r >> 1) * C + (c >> 7) * 128 + (r & 1) * 64 + ((c & 127) >> 1)] =
+        (uint8_t)(e2m1_code(v0 * inv) | (e2m1_code(v1 * inv) << 4));
+    if (sub == 0) scales[((mat * (C / 128) + b / 4) * R + r) * 4 + (b & 3)] = (uint8_t)(e + 127);
   }
 }
 

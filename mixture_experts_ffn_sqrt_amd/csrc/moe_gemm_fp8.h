@@ -163,7 +163,8 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& q, const TileCoord&
   constexpr int NA = BM / RPL, NB = BN / RPLB;
   constexpr int LA = NA / NW, LB = (NB + NW - 1) / NW;
   constexpr bool B_EVEN = NB % NW == 0;
-  constexpr int B_POL = BM <= 32 && !MX ? kStreamWeightPolicy : 0;  // E4M3 streaming tiles
+  constexpr int B_POL = BM <= 32 ? kStreamWeightPolicy : 0;  // streaming tiles: whole lines
+  constexpr int BKS = MX ? 128 : BROWB;  // bytes between consecutive K blocks of a weight row
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "whole 32x32 fragments");
   static_assert(NA * RPL == BM && NB * RPLB == BN && LA * NW == NA, "A loads must split evenly");
   static_assert(NSBL <= NW, "one weight-scale load per wave at most");
@@ -217,7 +218,10 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& q, const TileCoord&
     const int row = RPLB * (wave + NW * j) + lane / BCH;
     const int ch = MX ? (lane % BCH) ^ ((row >> 2) & 3) : (lane % BCH) ^ ((row >> 1) & 7);
     const int brow = weight_row(row);
-    b_off[j] = brow >= 0 ? (uint32_t)brow * (uint32_t)p.ldb + ch * 16 : kOut;
+    // E2M1 codes: rows 2i, 2i+1 share each 128-byte line of a 128-element K block
+    const uint32_t rowb = MX ? (uint32_t)(brow >> 1) * (uint32_t)(2 * p.ldb) + (uint32_t)(brow & 1) * 64u
+                             : (uint32_t)brow * (uint32_t)p.ldb;
+    b_off[j] = brow >= 0 ? rowb + ch * 16 : kOut;
   }
   // the last B slot exists on waves whose block wave + NW*(LB-1) is < NB
   const bool b_last = B_EVEN || wave + NW * (LB - 1) < NB;
@@ -254,7 +258,7 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& q, const TileCoord&
     _Pragma("unroll") for (int j = 0; j < LB; ++j) {                                        \
       if (j == LB - 1 && !b_last) break;                                                   \
       load_lds16<B_POL>(b_rs, buf_ + OFF_B + (RPLB * (wave + NW * j)) * BROWB,             \
-                 b_off[j] + kc_ * BROWB);                                                  \
+                 b_off[j] + kc_ * BKS);                                                    \
     }                                                                                      \
     if (has_sa)                                                                            \
       load_lds4(s_rs, buf_ + OFF_SA + 256 * wave, s_off + (uint32_t)kc_ * q.as_kstride);   \

@@ -411,9 +411,10 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, char* dst,
 // A block-contiguous read stream runs at 6.9-7.0 TB/s with it against 6.2
 // without; the decode GEMMs of V4-Flash shapes 6-7% faster (bf16 and E4M3),
 // V4-Pro's bf16 up GEMM 1%.  Not for the larger tiles, whose co-running tiles
-// share weight panels through the L2 (Mixtral and V4-Pro 3-5% slower with it),
-// nor for E2M1 weights, whose 64-byte rows leave the other half of each
-// 128-byte line to the next K stage (MXFP4 decode 36% slower with it).
+// share weight panels through the L2 (Mixtral and V4-Pro 3-5% slower with it).
+// E2M1 weights take it only because their rows are stored in pairs: with
+// row-major codes one K stage reads 64 bytes of each 128-byte line and leaves
+// the rest to the next stage, which NT made 36% slower.
 constexpr int kStreamWeightPolicy = 2;  // NT
 
 // one 4-byte-per-lane buffer load straight into LDS at `dst` (+4 * lane)

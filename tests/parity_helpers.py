@@ -400,10 +400,20 @@ def check_quantized_tiles(inp, wq, fmt, seed):
                 gs = s[e, r0 // 128, c0 // 128].reshape(1, 1).cpu().numpy()
             else:
                 rq, rs = O.quantize_mxfp4(region)  # [128, 64] codes, [128, 4] E8M0
-                gq = q[e, r0:r0 + 128, c0 // 2:c0 // 2 + 64].cpu().numpy()
+                gq = mxfp4_rows(q[e, r0 // 2:r0 // 2 + 64, c0:c0 + 128].cpu().numpy())
                 gs = s[e, c0 // 128, r0:r0 + 128, :].cpu().numpy()
             assert np.array_equal(gs, rs), (name, e, r0, c0)
             assert np.array_equal(gq, rq), (name, e, r0, c0)
+
+
+def mxfp4_rows(q):
+    """E2M1 codes in the library's paired-row layout, [..., R/2, C] bytes (row
+    pair i, 128-column block j: 64 bytes of row 2i, then 64 of row 2i+1) ->
+    the row-major [..., R, C/2] that the oracle's quantizer returns."""
+    q = np.asarray(q)
+    *lead, P, C_ = q.shape
+    t = q.reshape(*lead, P, C_ // 128, 2, 64)
+    return np.ascontiguousarray(np.moveaxis(t, -2, -3)).reshape(*lead, 2 * P, C_ // 2)
 
 
 def dequantized(fmt, q, s):

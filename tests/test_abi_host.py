@@ -143,6 +143,7 @@ def test_mxfp4_entry_points_check_on_host():
     z = None
     bogus = C.c_void_p(0x1000)
     assert L.moe_quantize_mxfp4(1, 4, 96, 1, bogus, bogus, bogus, z) == -2    # C % 128
+    assert L.moe_quantize_mxfp4(1, 5, 128, 1, bogus, bogus, bogus, z) == -2   # odd R
     assert L.moe_quantize_mxfp4(1, -1, 128, 1, bogus, bogus, bogus, z) == -1
     assert L.moe_quantize_mxfp4(-1, 4, 128, 1, bogus, bogus, bogus, z) == -1
     assert L.moe_quantize_mxfp4(1, 4, 128, 5, bogus, bogus, bogus, z) == -1   # dtype

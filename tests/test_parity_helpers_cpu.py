@@ -127,3 +127,21 @@ def test_dequantized_weights_within_one_rounding_step():
     blk_s = np.repeat(np.ldexp(1.0, s.astype(np.int32) - 127), 32, axis=1)
     deq = H.dequantized("mxfp4", q, s)
     assert np.all(np.abs(deq - w) <= np.abs(w) / 4 + 0.25 * blk_s)
+
+
+def test_mxfp4_rows_inverts_the_paired_row_layout():
+    """The paired-row code layout, built byte by byte from its definition
+    (element (r, c) at byte (r/2)*C + (c/128)*128 + (r%2)*64 + (c%128)/2),
+    maps back to the row-major codes."""
+    rng = np.random.default_rng(5)
+    R, C_ = 6, 384
+    rowmajor = rng.integers(0, 256, (R, C_ // 2), dtype=np.uint8)
+    flat = np.zeros(R * C_ // 2, np.uint8)
+    for r in range(R):
+        for c in range(0, C_, 2):
+            flat[(r // 2) * C_ + (c // 128) * 128 + (r % 2) * 64 + (c % 128) // 2] = \
+                rowmajor[r, c // 2]
+    paired = flat.reshape(R // 2, C_)
+    assert np.array_equal(H.mxfp4_rows(paired), rowmajor)
+    stacked = np.stack([paired, paired[::-1]])
+    assert np.array_equal(H.mxfp4_rows(stacked)[0], rowmajor)
