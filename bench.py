@@ -177,6 +177,16 @@ def input_digests(inp):
     return dict(sha256=sha, xxh3_128=xxh)
 
 
+def output_digest(t):
+    """XXH3-128 of a layer output's bytes (after the timed region, from one more
+    step on the same inputs): two runs computed the same output bitwise exactly
+    when their digests agree."""
+    import torch
+    import xxhash
+    torch.cuda.synchronize()
+    return xxhash.xxh3_128(t.detach().contiguous().view(torch.uint8).cpu().numpy().tobytes()).hexdigest()
+
+
 def lowp_accounting(lc, counts, kind):
     """Algorithmic work of the low-precision expert GEMM 1 (routed rows): the same
     FLOPs as bf16; bytes = every active expert's w13 codes and scales (FP8: 1
@@ -310,6 +320,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True, with
         routing=dict(active_experts=acct["active_experts"], max_rows=int(counts.max()),
                      mean_rows=float(counts.mean()), empty_experts=int((counts == 0).sum())),
     )
+    res["output_xxh3_128"] = output_digest(layer.forward())
     if with_hash:
         # the hash-routed pass: ids from tid2eid[token_ids], same experts and shapes
         hc = moe.make_config(T=lc.T, d=lc.d, E=lc.E, k=lc.k, d_ff=lc.d_ff,
@@ -381,9 +392,10 @@ def run_lowp(kind, lc, c, layer, inp, perm, ws, Y, counts, steps, warmup, stream
     roof["kernel"] = "%s grouped GEMM 1 + SwiGLU + FP8 cast (%s, routed rows)" % (
         "MXFP4-weight" if mx else "FP8", up_fn.__name__)
     gemm_tflops = 6 * d * F * T * k / ((ms_up + ms_down) * 1e-3) / 1e12
+    digest = output_digest(fwd(wq))
     del wq, xq, xs, hq, hs
     return dict(ms_per_step=round(ms_step, 4), tokens_per_s=round(T / (ms_step * 1e-3), 1),
-                roofline=roof,
+                roofline=roof, output_xxh3_128=digest,
                 grouped_gemm=dict(ms_up=round(ms_up, 4), ms_down=round(ms_down, 4),
                                   tflops=round(gemm_tflops, 1),
                                   frac_fp8_peak=round(gemm_tflops / PEAK_TFLOPS["fp8"], 4)))
@@ -599,12 +611,14 @@ def main():
         "routing": head["routing"],
         "step_ms_p10_p50_p90": head["step_ms_p10_p50_p90"],
         "input_digests": head.get("input_digests"),
+        "output_xxh3_128": head.get("output_xxh3_128"),
         "fp8": head.get("fp8"),
         "mxfp4": head.get("mxfp4"),
         "measured_peaks": measured,
     }
     keep = ("ms_per_step", "tokens_per_s", "roofline", "grouped_gemm", "combine", "layer",
-            "routing", "step_ms_p10_p50_p90", "hash_pass", "fp8", "mxfp4", "cpu_single_core")
+            "routing", "step_ms_p10_p50_p90", "hash_pass", "fp8", "mxfp4", "cpu_single_core",
+            "output_xxh3_128")
     side = [] if args.side in ("", "none") else [w for w in args.side.split(",")
                                                  if w != args.workload]
     others = {}
