@@ -206,6 +206,17 @@ def lowp_accounting(lc, counts, kind):
     return flops, nbytes
 
 
+def layer_roofline(flops, nbytes, ms, dtype):
+    """The whole layer step against its roofline: rates, each as a fraction of
+    its published peak, and roof_frac = t_roof / t_measured with t_roof =
+    max(FLOPs / MFMA peak, bytes / HBM peak) (the larger of the two fractions)."""
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    mfma_frac, hbm_frac = tflops / PEAK_TFLOPS[dtype], gbs / PEAK_HBM_GBS
+    return dict(tflops=round(tflops, 1), gbs=round(gbs, 1), hbm_frac=round(hbm_frac, 4),
+                mfma_frac=round(mfma_frac, 4), roof_frac=round(max(mfma_frac, hbm_frac), 4))
+
+
 def roofline_of(flops, nbytes, ms, mfma_peak, mfma_ceiling, hbm_ceiling):
     """Roofline of one kernel launch: its algorithmic FLOPs and bytes over its
     measured duration.  The bound is the one whose ideal time at the published
@@ -312,11 +323,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_seconds, with_fp8=True, with
         # and the gated sum written): the cost of keeping the weighted sum out
         # of the GEMM 2 epilogue
         combine=dict(ms=round(ms_combine, 4), share_of_step=round(ms_combine / ms_step, 4)),
-        layer=dict(tflops=round(acct["layer_flops"] / (ms_step * 1e-3) / 1e12, 1),
-                   gbs=round(acct["layer_bytes"] / (ms_step * 1e-3) / 1e9, 1),
-                   hbm_frac=round(acct["layer_bytes"] / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                   mfma_frac=round(acct["layer_flops"] / (ms_step * 1e-3) / 1e12
-                                   / PEAK_TFLOPS[lc.dtype], 4)),
+        layer=layer_roofline(acct["layer_flops"], acct["layer_bytes"], ms_step, lc.dtype),
         routing=dict(active_experts=acct["active_experts"], max_rows=int(counts.max()),
                      mean_rows=float(counts.mean()), empty_experts=int((counts == 0).sum())),
     )

@@ -56,3 +56,12 @@ def test_accounting_counts():
     assert f == a["up_routed_flops"]
     w = 2 * F * d + (2 * F // 128) * (d // 128) * 4
     assert nb == 3 * w + rows * (d + d // 128 * 4) + rows * (F + F // 128 * 4)
+
+
+def test_layer_roofline_fraction_is_t_roof_over_t():
+    # 1 TFLOP and 2 GB in 1 ms: t_roof = max(0.4, 0.25) ms -> 0.4 of the roof
+    r = bench.layer_roofline(1e12, 2e9, 1.0, "bf16")
+    assert r["mfma_frac"] == pytest.approx(0.4) and r["hbm_frac"] == pytest.approx(0.25)
+    assert r["roof_frac"] == pytest.approx(0.4)
+    r = bench.layer_roofline(1e11, 4e9, 1.0, "bf16")
+    assert r["roof_frac"] == pytest.approx(0.5)
