@@ -88,7 +88,8 @@ int check_fp8(const moe_config* c) {
   const int64_t lim = int64_t(1) << 31;
   const int64_t T = c->T, d = c->d, F = c->d_ff;
   const int64_t P = T * (c->k + c->n_shared);
-  if (T * d >= lim || P * F >= lim || 2 * F * d >= lim || P * (F / 128) * 4 >= lim)
+  if (T * d >= lim || P * F >= lim || 2 * F * d >= lim || P * (F / 128) * 4 >= lim ||
+      288 * d * 2 >= lim)  // a tile's rows of Y (bf16) through one buffer range
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }

@@ -158,11 +158,12 @@ enum class FfnTiles { F32_16, BF16_16, BF16_32, BF16_128, BF16_PREFILL };
 FfnTiles pick_tiles(const moe_config& c, const ExpertFfnArgs& a) {
   if (c.dtype == MOE_F32) return FfnTiles::F32_16;
   const int64_t avg_rows = a.rows_bound / (a.n_groups > 0 ? a.n_groups : 1);
-  // the buffer-load kernels address each operand with 32-bit offsets
+  // the buffer-load kernels address each operand, and a tile's rows of the
+  // output (at most 288), with 32-bit offsets
   const int64_t lim = int64_t(1) << 31;
   const bool fits = c.d_ff % 128 == 0 && (int64_t)c.T * c.d * 2 < lim &&
                     (int64_t)a.rows_bound * c.d_ff * 2 < lim &&
-                    (int64_t)2 * c.d_ff * c.d * 2 < lim;
+                    (int64_t)2 * c.d_ff * c.d * 2 < lim && (int64_t)288 * c.d * 2 < lim;
   // a few rows per expert: the GEMMs stream each expert's weights once
   // (HBM-bound); 32-row tiles with a deep direct-to-LDS pipeline
   if (avg_rows < 48) return fits ? FfnTiles::BF16_32 : FfnTiles::BF16_16;

@@ -401,7 +401,13 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& q, const TileCoord&
 #undef MOE_FP8_ISSUE
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no LDS load may still be in flight
 
+  // Stores go through buffer resources whose range is exactly the tile's valid
+  // rows (consecutive rows of C and of the H scales), so a store to a row past
+  // them, or given an offset outside the range, is dropped by the hardware: no
+  // lane branches on its row, and addresses are 32-bit offsets from one base.
   const int ccol = lane & 31, crow = (lane >> 5) * 4;
+  const __amdgpu_buffer_rsrc_t c_rs = __builtin_amdgcn_make_buffer_rsrc(
+      p.C + (int64_t)tc.row0 * p.ldc, 0, tc.nrows * (int)p.ldc, 0x00020000);
   if constexpr (SW) {
     // h = SiLU(g) * u; the row maximum of |h| over this wave's columns, then over
     // the WN waves through LDS; scale 2^e = the smallest power of two with
@@ -439,6 +445,11 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& q, const TileCoord&
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);
     lds_barrier();
+    // the tile's H scales: rows row0 .. row0 + nrows - 1 of column block nt;
+    // one lane per row (wave column 0, lane column 0) writes each
+    const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc(
+        q.c_scale + (int64_t)tc.nt * q.ldcs + tc.row0, 0, tc.nrows * 4, 0x00020000);
+    const bool s_lane = wn == 0 && ccol == 0;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -447,17 +458,17 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& q, const TileCoord&
         float m = 0.0f;
 #pragma unroll
         for (int w = 0; w < WN; ++w) m = fmaxf(m, part[w * BM + lrw]);
-        if (lrw >= tc.nrows) continue;
         const int e = fp8_scale_exp(m);
         const float inv = ldexpf(1.0f, -e);  // exact: codes = E4M3(h * 2^-e)
-        const int64_t row = tc.row0 + lrw;
-        uint8_t* crow_ptr = reinterpret_cast<uint8_t*>(p.C) + row * p.ldc;
+        const uint32_t roff = (uint32_t)lrw * (uint32_t)p.ldc;
 #pragma unroll
         for (int f = 0; f < HF; ++f) {
           const int col = tc.nt * (BN / 2) + wn * (WTN / 2) + 32 * f + ccol;
-          crow_ptr[col] = (uint8_t)e4m3_code(h[i][f][r] * inv);
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)e4m3_code(h[i][f][r] * inv), c_rs,
+                                               roff + col, 0, 0);
         }
-        if (wn == 0 && ccol == 0) q.c_scale[(int64_t)tc.nt * q.ldcs + row] = ldexpf(1.0f, e);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ldexpf(1.0f, e)), s_rs,
+                                              s_lane ? (uint32_t)lrw * 4u : kOut, 0, 0);
       }
     }
   } else {
@@ -466,13 +477,12 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& q, const TileCoord&
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int lrw = wm * WTM + 32 * i + 8 * (r >> 2) + crow + (r & 3);
-        if (lrw >= tc.nrows) continue;
-        char* crow_ptr = p.C + (int64_t)(tc.row0 + lrw) * p.ldc;
+        const uint32_t roff = (uint32_t)lrw * (uint32_t)p.ldc;
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
           const int col = tc.nt * BN + wn * WTN + 32 * f + ccol;
-          if (col >= p.N) continue;
-          *reinterpret_cast<uint16_t*>(crow_ptr + (int64_t)col * 2) = f32_to_bf16(acc[i][f][r]);
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[i][f][r]), c_rs,
+                                                col < p.N ? roff + col * 2 : kOut, 0, 0);
         }
       }
     }

@@ -651,33 +651,40 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& p, const TileCoord
 #undef MOE_DMA_ISSUE_B
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no LDS load may still be in flight at exit
 
-  // epilogue: lane holds C[8*(r/4) + 4*(lane/32) + r%4][lane % 32] of each fragment
+  // epilogue: lane holds C[8*(r/4) + 4*(lane/32) + r%4][lane % 32] of each
+  // fragment.  The stores go through a buffer resource whose range is exactly
+  // the tile's valid rows (they are consecutive rows of C), so a store to a row
+  // past them, or to a column past N (given an offset outside the range), is
+  // dropped by the hardware: no lane branches on its row or column, and every
+  // address is a 32-bit offset from one base.
   const int ccol = lane & 31, crow = (lane >> 5) * 4;
+  const __amdgpu_buffer_rsrc_t c_rs = __builtin_amdgcn_make_buffer_rsrc(
+      p.C + (int64_t)tc.row0 * p.ldc, 0, tc.nrows * (int)p.ldc, 0x00020000);
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int lrw = wm * WTM + 32 * i + 8 * (r >> 2) + crow + (r & 3);
-      if (lrw >= tc.nrows) continue;
-      char* crow_ptr = p.C + (int64_t)(tc.row0 + lrw) * p.ldc;
+      const uint32_t roff = (uint32_t)lrw * (uint32_t)p.ldc;
       if (SW) {
 #pragma unroll
         for (int f = 0; f < FN / 2; ++f) {
           const float g = acc[i][f][r], u = acc[i][f + FN / 2][r];
           const float h = silu_mul(g, u);
           const int col = tc.nt * (BN / 2) + wn * (WTN / 2) + 32 * f + ccol;
-          *reinterpret_cast<uint16_t*>(crow_ptr + (int64_t)col * 2) = f32_to_bf16(h);
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(h), c_rs, roff + col * 2, 0, 0);
         }
       } else {
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
           const int col = tc.nt * BN + wn * WTN + 32 * f + ccol;
-          if (col >= p.N) continue;
           if (EPI == EPI_LOGITS) {
-            reinterpret_cast<float*>(crow_ptr)[col] =
-                acc[i][f][r] + (p.col_add ? p.col_add[col] : 0.0f);
+            const float v = acc[i][f][r] + (p.col_add && col < p.N ? p.col_add[col] : 0.0f);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), c_rs,
+                                                  col < p.N ? roff + col * 4 : kOut, 0, 0);
           } else {
-            *reinterpret_cast<uint16_t*>(crow_ptr + (int64_t)col * 2) = f32_to_bf16(acc[i][f][r]);
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[i][f][r]), c_rs,
+                                                  col < p.N ? roff + col * 2 : kOut, 0, 0);
           }
         }
       }
