@@ -124,8 +124,10 @@ __device__ __forceinline__ int mx_scale_exp(float amax) {
 
 // 16 lanes per 32-element block (two elements each, one output byte), four
 // blocks per wavefront, blocks numbered over the row-major [n_mat * R, C]
-// input (a row's C/32 blocks are consecutive).  Scale of block b of row r of
-// matrix m goes to scales[m][b / 4][r][b % 4].  A workgroup takes 16 blocks
+// input (a row's C/32 blocks are consecutive).  Codes go to the paired-row
+// layout: element (r, c) of matrix m at byte m*R*C/2 + (r/2)*C + (c/128)*128 +
+// (r%2)*64 + (c%128)/2.  Scale of block b of row r of matrix m goes to
+// scales[m][b / 4][r][b % 4].  A workgroup takes 16 blocks
 // per pass and strides over the grid: a dispatch's work-item count is 32-bit,
 // and all the experts' weights of a large layer (384 x 6144 x 7168 elements)
 // would need more work-items than that at one thread per two elements.

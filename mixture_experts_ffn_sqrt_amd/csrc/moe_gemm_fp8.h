@@ -15,8 +15,9 @@
 //
 // MXFP4 weights (WF_MXFP4; the same page's FP4 QAT section: E2M1 with one
 // scale per 1x32 sub-block, native FP4 weights at inference, FP4 x FP8
-// products): B is packed E2M1 (two codes per byte) with an E8M0 scale byte per
-// weight row and 32-element K block, so
+// products): B is packed E2M1 (two codes per byte; rows stored in pairs, so
+// that one 128-element K block of rows 2i and 2i+1 fills one 128-byte line)
+// with an E8M0 scale byte per weight row and 32-element K block, so
 //   acc = sum_b  sa[r, b/4] * sb[o, b] * sum_{k in block b} A[r, k] * B[o, k]
 // over 32-element blocks b.  The scaled MFMA takes FP8 A and FP4 B in one
 // instruction, and its per-lane B scale is exactly one such block (a lane's
