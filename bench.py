@@ -69,12 +69,23 @@ KERNEL_SOURCES = {
 KERNEL_SOURCES["mxfp4"] = KERNEL_SOURCES["fp8"]
 
 
+def code_text(src):
+    """C/HIP source with its comments removed and its whitespace collapsed, so
+    that an edit of the comments alone leaves the code's hash unchanged."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_source_sha(kind="bf16"):
+    """SHA-256 of the code (comments aside) of the sources a GEMM kind is built
+    from: the key under which its counter-derived traffic is stored."""
     import hashlib
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()
 
 

@@ -65,3 +65,11 @@ def test_layer_roofline_fraction_is_t_roof_over_t():
     assert r["roof_frac"] == pytest.approx(0.4)
     r = bench.layer_roofline(1e11, 4e9, 1.0, "bf16")
     assert r["roof_frac"] == pytest.approx(0.5)
+
+
+def test_kernel_hash_ignores_comments_only():
+    a = "int f(int x) {  // twice\n  return 2 * x; /* doubled */\n}\n"
+    b = "/* header */\nint f(int x) {\n  // two times x\n  return 2 * x;\n}"
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) != bench.code_text(a.replace("2 * x", "3 * x"))
+    assert len(bench.kernel_source_sha("fp8")) == 64
