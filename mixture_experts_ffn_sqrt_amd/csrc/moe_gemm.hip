@@ -46,7 +46,7 @@ hipError_t launch_gemm(GemmArgs p, int m_tiles_bound, hipStream_t s, int splits 
 
 // Direct-to-LDS bf16 kernel (ST LDS buffers of ROWB/2 K-elements).
 template <int BM, int BN, int WM, int WN, int EPI, int ST, int ROWB, int SWZ, int SCHED = 0>
-hipError_t launch_gemm_dma(GemmArgs p, int m_tiles_bound, hipStream_t s) {
+hipError_t launch_gemm_dma(GemmArgs p, int m_tiles_bound, hipStream_t s, int splits = 1) {
   constexpr int NT = 64 * WM * WN;
   constexpr int LDS = ST * (BM + BN) * ROWB;
   const int grid = xcd_grid((int64_t)m_tiles_bound * p.n_tiles);
@@ -55,7 +55,7 @@ hipError_t launch_gemm_dma(GemmArgs p, int m_tiles_bound, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), LDS, s, p);
+  hipLaunchKernelGGL(kern, dim3(grid, splits), dim3(NT), LDS, s, p);
   return hipGetLastError();
 }
 
@@ -126,12 +126,28 @@ hipError_t launch_router_gemm(const moe_config& c, const void* hidden, const voi
     p.ldc = (int64_t)router_part_ld(c) * 4;
     p.c_split = (int64_t)c.T * p.ldc;
   }
-  // Large batches with many experts: 128x128 tiles read the hidden rows half as
-  // often (DeepSeek-V3 prefill 92 -> 72 us), on 8 waves of 32x64 (routing of
-  // DeepSeek-V3 120 -> 110 us, V4-Pro 187 -> 181 us against 4 waves; 256-row
-  // tiles and 16 waves no better); small batches keep 64x64 tiles so that
-  // enough blocks run.  Every shape uses the same MFMA and walks K in the same
-  // order for every output, so the logits are bitwise the same either way.
+  // The direct-to-LDS kernel (K slices of whole 64-element stages; hidden rows
+  // and router weights addressed with 31-bit offsets): 128x128 tiles on 8
+  // waves of 64x32 for large batches with many experts, 64x64 tiles on 4
+  // waves otherwise, so that enough blocks run.  Both walk K in the same
+  // order with the same MFMA for every output, so a token's logits are
+  // bitwise the same whichever shape its batch takes.
+  const int64_t lim = int64_t(1) << 31;
+  if ((int64_t)c.T * c.d * 2 < lim && (int64_t)c.E * c.d * 2 < lim) {
+    p.a_bytes = (uint32_t)((int64_t)c.T * c.d * 2);
+    p.b_bytes = (uint32_t)((int64_t)c.E * c.d * 2);
+    if (c.T >= 1024 && c.E >= 128) {
+      p.n_tiles = ceil_div(c.E, 128);
+      return launch_gemm_dma<128, 128, 2, 4, EPI_LOGITS, 2, 128, 3, 1>(p, ceil_div(c.T, 128),
+                                                                       s, splits);
+    }
+    p.n_tiles = ceil_div(c.E, 64);
+    return launch_gemm_dma<64, 64, 2, 2, EPI_LOGITS, 2, 128, 3, 1>(p, ceil_div(c.T, 64), s,
+                                                                   splits);
+  }
+  // batches too large for 31-bit offsets: the register-staged kernel.  Large
+  // batches with many experts: 128x128 tiles read the hidden rows half as
+  // often, on 8 waves of 32x64; small batches 64x64 tiles.
   if (c.T >= 1024 && c.E >= 128) {
     p.n_tiles = ceil_div(c.E, 128);
     return launch_gemm<uint16_t, 128, 128, 4, 2, EPI_LOGITS>(p, ceil_div(c.T, 128), s, splits);

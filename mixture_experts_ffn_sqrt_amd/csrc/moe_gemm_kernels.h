@@ -697,6 +697,15 @@ template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int ROWB, int SWZ
 __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_dma(GemmArgs p) {
   TileCoord tc;
   if (!decode_tile<BM>(p, tc)) return;
+  if (p.k_chunk) {  // split-K over grid rows (dense bf16): K slice y, partial output y
+    const uint32_t ko = (uint32_t)blockIdx.y * (uint32_t)p.k_chunk * 2u;
+    p.A += ko;
+    p.B += ko;
+    p.a_bytes -= ko;  // the buffer ranges still end where the operands end
+    p.b_bytes -= ko;
+    p.C += (int64_t)blockIdx.y * p.c_split;
+    p.K = p.k_chunk;
+  }
   gemm_dma_tile<BM, BN, WM, WN, EPI, STAGES, ROWB, SWZ, SCHED>(p, tc);
 }
 
